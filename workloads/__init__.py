@@ -1,0 +1,372 @@
+"""Seeded synthetic inputs for block verification, shared by the tests and the bench.
+
+This module only draws random inputs and lays them out; it performs none of the
+verification arithmetic (no attention, no argmax of target rows, no softmax, no
+acceptance test).  Both the float64 oracle and the GPU library consume what it
+produces, and neither imports the other.
+
+Workloads (shapes taken from the pages' measurement setups):
+
+* ``tiny_fp32``      -- 1 layer, 2 query heads on 1 KV head, head_dim 64, context
+  512, block 4 (anchor + 3 drafts), fp32 Q/K/V ~ N(0,1), vocabulary 1000,
+  fp32 logits ~ N(0,3), greedy acceptance.
+* ``qwen7b_25k``     -- 7B-shaped verify layer (28 q heads, 4 KV heads, d 128),
+  bf16 KV cache of 25,119 context tokens plus the 16 block tokens, block 16 with
+  the in-block causal mask, bf16 logits [16 x 152,064] ~ N(0,3), greedy.  The
+  context length is the one of the VFlash-FM demo cycle (VFlash-FM page, "How
+  VFlash-FM works", cycle figure), block 16 from its demo setup.
+* ``batched_paged``  -- 8 sequences, contexts log-uniform in [4096, 32768),
+  paged bf16 KV with 16-token pages and one globally shuffled page pool.
+* ``compressor_sar`` -- SpecFLASH latent compressor (SpecFLASH README,
+  "components", compressor equation): 32 images, D = 4096, (C, N) = (64, 576)
+  and (36, 324), fp16 queries ~ N(0, 0.02), features ~ N(0, 1); followed by
+  the semi-autoregressive block of 5 slot queries, 64 heads x 64.
+* ``qwen72b_sampling`` -- 72B-shaped sampling verify (64 q heads, 8 KV heads,
+  d 128), bf16 KV of 25,000 context tokens, block 32, target logits ~ N(0,3),
+  draft logits = bf16(target + N(0,1)), temperature 1.
+
+Conventions (fixed here, used by both sides):
+
+* "N(mu, s)" takes s as the standard deviation.
+* bf16 tensors are carried as ``uint16`` bit patterns, rounded from float32
+  draws with round-to-nearest-even.
+* KV caches are paged.  K pages are ``[num_pages][Hkv][P][d]`` (token-major);
+  V pages are ``[num_pages][Hkv][d][P]`` (dim-major).  ``page_table[b][j]``
+  is the physical page holding tokens ``[j*P, (j+1)*P)`` of sequence b.  The
+  cache of sequence b holds ``ctx_lens[b] + K`` tokens: the context followed
+  by the block's own K/V rows.
+* Planted greedy prefix: every target row gets one planted maximum (value 20,
+  all other entries are clipped to +-19.5 = 6.5 sigma), so the lowest-index
+  argmax of each row is known by construction.  A quarter of the rows repeat
+  the maximum at a later index, which exercises the lowest-index tie rule.
+  Drafts copy the planted maxima for a Geometric(0.25) prefix length L
+  (P(L = k) = 0.75^k * 0.25, truncated to K-1); the next draft is drawn
+  uniformly from the other tokens and later drafts uniformly from all tokens,
+  so the accepted length equals L by construction.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "WORKLOADS", "bf16_bits", "bf16_bits_to_f32", "VerifyInputs", "GreedyInputs",
+    "SampleInputs", "CompressInputs", "SarInputs", "make_verify", "make_greedy",
+    "make_sample", "make_compress", "make_sar", "build_page_table", "causal_mask",
+    "all_ones_mask", "rng_for",
+]
+
+BASE_SEED = 1000
+PLANT_VALUE = 20.0       # planted row maximum (exact in bf16 and fp32)
+PLANT_CLIP = 19.5        # every other logit is clipped to [-19.5, 19.5]
+TIE_FRACTION = 0.25      # rows that repeat the planted maximum at a later index
+
+
+# --------------------------------------------------------------------------- dtypes
+
+def bf16_bits(x) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns -> float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_bits(x)
+    if dtype == "f16":
+        return np.ascontiguousarray(x, dtype=np.float16)
+    raise ValueError(dtype)
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return _round_to(x, dtype)
+
+
+def rng_for(workload: str, cycle: int = 0) -> np.random.Generator:
+    """The generator for a workload's cycle: SeedSequence([1000 + index, cycle])."""
+    idx = list(WORKLOADS).index(workload) + 1
+    return np.random.default_rng(np.random.SeedSequence([BASE_SEED + idx, cycle]))
+
+
+# --------------------------------------------------------------------------- masks
+
+def causal_mask(K: int) -> np.ndarray:
+    """Row i sees block keys 0..i (bit t of row i set iff t <= i)."""
+    return np.array([(1 << (i + 1)) - 1 for i in range(K)], dtype=np.uint64)
+
+
+def all_ones_mask(K: int) -> np.ndarray:
+    """Every row sees every block key (one bidirectional block)."""
+    full = (1 << K) - 1
+    return np.array([full] * K, dtype=np.uint64)
+
+
+# --------------------------------------------------------------------------- paging
+
+def build_page_table(rng: Optional[np.random.Generator], n_tokens: np.ndarray, P: int,
+                     shuffle: bool):
+    """Assign physical pages to sequences.
+
+    Returns (page_table int32 [B][max_pages], num_pages).  Pages are drawn from
+    one pool; with ``shuffle`` a random permutation scatters them across all
+    sequences, otherwise sequence b owns a contiguous run (identity table for
+    B = 1).  Unused table entries are -1.
+    """
+    n_tokens = np.asarray(n_tokens, dtype=np.int64)
+    pages_per = (n_tokens + P - 1) // P
+    num_pages = int(pages_per.sum())
+    pool = np.arange(num_pages, dtype=np.int32)
+    if shuffle:
+        pool = rng.permutation(num_pages).astype(np.int32)
+    max_pages = int(pages_per.max())
+    table = np.full((len(n_tokens), max_pages), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pages_per):
+        table[b, :n] = pool[off:off + n]
+        off += n
+    return table, num_pages
+
+
+# --------------------------------------------------------------------------- verify
+
+@dataclass
+class VerifyInputs:
+    """Inputs of one verify-attention call (one layer)."""
+    B: int
+    K: int
+    Hq: int
+    Hkv: int
+    D: int
+    P: int
+    dtype: str                      # "f32" | "bf16" | "f16"
+    q: np.ndarray                   # [B][K][Hq][D]
+    k_cache: np.ndarray             # [num_pages][Hkv][P][D]
+    v_cache: np.ndarray             # [num_pages][Hkv][D][P]
+    page_table: np.ndarray          # int32 [B][max_pages]
+    ctx_lens: np.ndarray            # int32 [B] (tokens before the block)
+    mask: np.ndarray                # uint64 [K] row bitmasks over block keys
+    scale: float = 0.0              # 0 -> 1/sqrt(D)
+
+    @property
+    def num_pages(self) -> int:
+        return self.k_cache.shape[0]
+
+    @property
+    def n_keys(self) -> np.ndarray:
+        return self.ctx_lens.astype(np.int64) + self.K
+
+    def kv_bytes(self) -> int:
+        """Algorithmic KV bytes: every visible (context + block) key and value, once."""
+        esz = 4 if self.dtype == "f32" else 2
+        return int(self.n_keys.sum()) * self.Hkv * self.D * 2 * esz
+
+
+def make_verify(rng: np.random.Generator, *, B: int, K: int, Hq: int, Hkv: int, D: int,
+                ctx_lens, P: int = 16, dtype: str = "bf16", shuffle: bool = False,
+                mask: Optional[np.ndarray] = None, qk_std: float = 1.0) -> VerifyInputs:
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int32).reshape(B)
+    n_tokens = ctx_lens.astype(np.int64) + K
+    page_table, num_pages = build_page_table(rng, n_tokens, P, shuffle)
+    q = _normal(rng, (B, K, Hq, D), qk_std, dtype)
+    k_cache = _normal(rng, (num_pages, Hkv, P, D), qk_std, dtype)
+    v_cache = _normal(rng, (num_pages, Hkv, D, P), 1.0, dtype)
+    if mask is None:
+        mask = causal_mask(K)
+    return VerifyInputs(B, K, Hq, Hkv, D, P, dtype, q, k_cache, v_cache, page_table,
+                        ctx_lens, np.asarray(mask, dtype=np.uint64))
+
+
+def log_uniform_contexts(rng: np.random.Generator, B: int, lo: int = 4096,
+                         hi: int = 32768) -> np.ndarray:
+    """ctx = floor(exp(U(ln lo, ln hi)))."""
+    u = rng.uniform(np.log(lo), np.log(hi), size=B)
+    return np.floor(np.exp(u)).astype(np.int32)
+
+
+# --------------------------------------------------------------------------- greedy
+
+@dataclass
+class GreedyInputs:
+    B: int
+    K: int
+    V: int
+    dtype: str                 # "f32" | "bf16"
+    logits: np.ndarray         # [B][K][V]
+    drafts: np.ndarray         # int32 [B][K-1]; drafts[b][k-1] is draft d_k
+    planted_len: np.ndarray    # int32 [B]: accepted length by construction
+    planted_tok: np.ndarray    # int32 [B][K]: lowest-index maximum of each row
+
+
+def make_greedy(rng: np.random.Generator, *, B: int, K: int, V: int, dtype: str = "bf16",
+                std: float = 3.0) -> GreedyInputs:
+    x = rng.standard_normal(size=(B, K, V), dtype=np.float32)
+    x *= np.float32(std)
+    np.clip(x, -PLANT_CLIP, PLANT_CLIP, out=x)
+    tok = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    tie = rng.random(size=(B, K)) < TIE_FRACTION
+    tie_u = rng.random(size=(B, K))
+    bb, kk = np.meshgrid(np.arange(B), np.arange(K), indexing="ij")
+    x[bb, kk, tok] = PLANT_VALUE
+    for b in range(B):
+        for k in range(K):
+            t = int(tok[b, k])
+            if tie[b, k] and t < V - 1:
+                j = t + 1 + int(tie_u[b, k] * (V - 1 - t))
+                x[b, k, min(j, V - 1)] = PLANT_VALUE
+    logits = _round_to(x, dtype)
+    L = np.minimum(rng.geometric(0.25, size=B) - 1, K - 1).astype(np.int32)
+    drafts = rng.integers(0, V, size=(B, K - 1)).astype(np.int32)
+    other = rng.integers(0, V - 1, size=B).astype(np.int32)
+    for b in range(B):
+        n = int(L[b])
+        drafts[b, :n] = tok[b, :n]
+        if n < K - 1:
+            t = int(tok[b, n])
+            o = int(other[b])
+            drafts[b, n] = o if o < t else o + 1
+    return GreedyInputs(B, K, V, dtype, logits, drafts, L, tok)
+
+
+# --------------------------------------------------------------------------- sampling
+
+@dataclass
+class SampleInputs:
+    B: int
+    K: int
+    V: int
+    dtype: str                 # "f32" | "bf16"
+    target_logits: np.ndarray  # [B][K][V]
+    draft_logits: np.ndarray   # [B][K-1][V]; row k-1 is the draft distribution of d_k
+    drafts: np.ndarray         # int32 [B][K-1]
+    temperature: float
+    seed: int
+    offset: int
+
+
+def _to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def make_sample(rng: np.random.Generator, *, B: int, K: int, V: int, dtype: str = "bf16",
+                temperature: float = 1.0, std: float = 3.0, noise: float = 1.0,
+                seed: int = 0x5EED, offset: int = 0) -> SampleInputs:
+    """Target logits ~ N(0, std); draft logits = round(target + N(0, noise)).
+
+    The drafts are drawn from the draft distribution softmax(draft/T) with the
+    Gumbel-max trick; this plays the drafter's part and is not verification.
+    """
+    tl = rng.standard_normal(size=(B, K, V), dtype=np.float32)
+    tl *= np.float32(std)
+    target = _round_to(tl, dtype)
+    t32 = _to_f64(target, dtype).astype(np.float32)
+    dn = rng.standard_normal(size=(B, K - 1, V), dtype=np.float32)
+    dn *= np.float32(noise)
+    draft = _round_to(t32[:, :K - 1, :] + dn, dtype)
+    g = -np.log(-np.log(rng.random(size=(B, K - 1, V))))
+    drafts = np.argmax(_to_f64(draft, dtype) / temperature + g, axis=-1).astype(np.int32)
+    return SampleInputs(B, K, V, dtype, target, draft, drafts, float(temperature),
+                        int(seed), int(offset))
+
+
+# --------------------------------------------------------------------------- compressor
+
+@dataclass
+class CompressInputs:
+    B: int
+    C: int
+    N: int
+    D: int
+    queries: np.ndarray   # float16 [C][D]
+    feats: np.ndarray     # float16 [B][N][D]
+
+
+def make_compress(rng: np.random.Generator, *, B: int, C: int, N: int, D: int,
+                  q_std: float = 0.02, f_std: float = 1.0) -> CompressInputs:
+    queries = _normal(rng, (C, D), q_std, "f16")
+    feats = _normal(rng, (B, N, D), f_std, "f16")
+    return CompressInputs(B, C, N, D, queries, feats)
+
+
+@dataclass
+class SarInputs:
+    """Semi-autoregressive block: S slot queries over C context rows + S slot rows."""
+    B: int
+    S: int
+    H: int
+    D: int
+    q: np.ndarray         # float16 [B][S][H][D]
+    slot_k: np.ndarray    # float16 [B][S][H][D]
+    slot_v: np.ndarray    # float16 [B][S][H][D]
+
+
+def make_sar(rng: np.random.Generator, *, B: int, S: int = 5, H: int = 64,
+             D: int = 64) -> SarInputs:
+    return SarInputs(B, S, H, D, _normal(rng, (B, S, H, D), 1.0, "f16"),
+                     _normal(rng, (B, S, H, D), 1.0, "f16"),
+                     _normal(rng, (B, S, H, D), 1.0, "f16"))
+
+
+# --------------------------------------------------------------------------- registry
+
+@dataclass
+class Workload:
+    name: str
+    desc: str
+    params: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", "1 layer, 2q/1kv, d64, ctx 512, block 4, fp32, V 1000",
+                          dict(B=1, K=4, Hq=2, Hkv=1, D=64, ctx=512, V=1000, dtype="f32")),
+    "qwen7b_25k": Workload("qwen7b_25k", "28q/4kv d128 bf16, ctx 25119 + block 16, V 152064",
+                           dict(B=1, K=16, Hq=28, Hkv=4, D=128, ctx=25119, V=152064,
+                                dtype="bf16")),
+    "batched_paged": Workload("batched_paged", "8 seqs, ctx log-uniform 4k-32k, shuffled pages",
+                              dict(B=8, K=16, Hq=28, Hkv=4, D=128, V=152064, dtype="bf16")),
+    "compressor_sar": Workload("compressor_sar", "B 32, D 4096, (64,576) and (36,324); SAR 5 slots",
+                               dict(B=32, D=4096, shapes=((64, 576), (36, 324)), S=5, H=64,
+                                    HD=64)),
+    "qwen72b_sampling": Workload("qwen72b_sampling", "64q/8kv d128 bf16, ctx 25000 + block 32",
+                                 dict(B=1, K=32, Hq=64, Hkv=8, D=128, ctx=25000, V=152064,
+                                      dtype="bf16", T=1.0)),
+}
+
+
+def make_workload_verify(name: str, cycle: int = 0) -> VerifyInputs:
+    """Verify-attention inputs of a named workload (draw order: contexts, pages, Q, K, V)."""
+    p = WORKLOADS[name].params
+    rng = rng_for(name, cycle)
+    if name == "batched_paged":
+        ctx = log_uniform_contexts(rng, p["B"])
+        return make_verify(rng, B=p["B"], K=p["K"], Hq=p["Hq"], Hkv=p["Hkv"], D=p["D"],
+                           ctx_lens=ctx, P=16, dtype=p["dtype"], shuffle=True)
+    return make_verify(rng, B=p["B"], K=p["K"], Hq=p["Hq"], Hkv=p["Hkv"], D=p["D"],
+                       ctx_lens=[p["ctx"]] * p["B"], P=16, dtype=p["dtype"])
+
+
+def make_workload_greedy(name: str, cycle: int = 0) -> GreedyInputs:
+    p = WORKLOADS[name].params
+    rng = rng_for(name, 10_000 + cycle)
+    return make_greedy(rng, B=p["B"], K=p["K"], V=p["V"], dtype=p["dtype"])
+
+
+def make_workload_sample(name: str, cycle: int = 0) -> SampleInputs:
+    p = WORKLOADS[name].params
+    rng = rng_for(name, 10_000 + cycle)
+    return make_sample(rng, B=p["B"], K=p["K"], V=p["V"], dtype=p["dtype"],
+                       temperature=p["T"], seed=0x5EED, offset=cycle)

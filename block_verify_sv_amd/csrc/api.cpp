@@ -1,0 +1,407 @@
+// libspecverify C ABI: argument validation, work planning and launches.
+// Every check runs on the host before anything touches the GPU, so invalid calls fail
+// with a status code (and a message in sv_last_error) and launch nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "internal.hpp"
+#include "specverify.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sv_status fail(sv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sv_status fail(sv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sv_status ok() {
+  g_last_error.clear();
+  return SV_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+sv_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- attention checks
+sv_status check_attn_desc(const sv_attn_desc* d) {
+  if (!d) return fail(SV_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 1 || d->batch > 65535)
+    return fail(SV_ERR_INVALID_ARG, "batch must be in [1, 65535] (got %d)", d->batch);
+  if (d->block < 1 || d->block > sv::kMaxBlock)
+    return fail(SV_ERR_INVALID_ARG, "block must be in [1, 64] (got %d)", d->block);
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads > 65535)
+    return fail(SV_ERR_INVALID_ARG, "head counts must be in [1, 65535]");
+  if (d->num_q_heads % d->num_kv_heads != 0)
+    return fail(SV_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                d->num_q_heads, d->num_kv_heads);
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (d->block * G > sv::kMaxRows)
+    return fail(SV_ERR_INVALID_ARG, "block * (num_q_heads / num_kv_heads) = %d exceeds 256",
+                d->block * G);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  if (d->dtype != SV_F32 && d->dtype != SV_BF16 && d->dtype != SV_F16)
+    return fail(SV_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(d->dtype));
+  if (!pow2(d->page_size) || d->page_size < 16 || d->page_size > 256)
+    return fail(SV_ERR_INVALID_ARG, "page_size must be a power of two in [16, 256] (got %d)",
+                d->page_size);
+  if (d->max_pages_per_seq < 1 || d->num_pages < 1)
+    return fail(SV_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+  if (d->max_ctx < 0) return fail(SV_ERR_INVALID_ARG, "max_ctx must be >= 0");
+  if (static_cast<int64_t>(d->max_ctx) + d->block >
+      static_cast<int64_t>(d->max_pages_per_seq) * d->page_size)
+    return fail(SV_ERR_INVALID_ARG,
+                "max_ctx + block (%lld) exceeds max_pages_per_seq * page_size (%lld)",
+                static_cast<long long>(d->max_ctx) + d->block,
+                static_cast<long long>(d->max_pages_per_seq) * d->page_size);
+  if (static_cast<int64_t>(d->max_ctx) + d->block > (1ll << 30))
+    return fail(SV_ERR_INVALID_ARG, "max_ctx too large");
+  if (d->split_keys < 0 || (d->split_keys % 16) != 0)
+    return fail(SV_ERR_INVALID_ARG, "split_keys must be 0 or a positive multiple of 16 (got %d)",
+                d->split_keys);
+  if (!(d->scale >= 0.0f) || !isfinite(d->scale))
+    return fail(SV_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (d->sum_ctx_hint < 0) return fail(SV_ERR_INVALID_ARG, "sum_ctx_hint must be >= 0");
+  return SV_OK;
+}
+
+}  // namespace
+
+namespace sv {
+
+AttnPlan plan_attention(const sv_attn_desc& d) {
+  AttnPlan pl;
+  const int64_t n_max = static_cast<int64_t>(d.max_ctx) + d.block;
+  pl.rows = d.block * (d.num_q_heads / d.num_kv_heads);
+  int64_t chunk = d.split_keys;
+  if (chunk == 0) {
+    // one key split per compute unit: total (context + block) keys over all KV heads,
+    // spread over the 256 CUs, in multiples of 16 keys
+    const int64_t ctx_sum =
+        d.sum_ctx_hint > 0 ? d.sum_ctx_hint : static_cast<int64_t>(d.batch) * d.max_ctx;
+    const int64_t work = (ctx_sum + static_cast<int64_t>(d.batch) * d.block) * d.num_kv_heads;
+    chunk = (work + kNumCUs - 1) / kNumCUs;
+    chunk = (chunk + 15) / 16 * 16;
+    if (chunk < 64) chunk = 64;
+    const int64_t cap = (n_max + 15) / 16 * 16;
+    if (chunk > cap) chunk = cap;
+  }
+  pl.chunk = static_cast<int>(chunk);
+  pl.nsplit = static_cast<int>((n_max + chunk - 1) / chunk);
+  pl.ws_bytes = static_cast<size_t>(d.batch) * d.num_kv_heads * pl.nsplit * pl.rows *
+                (static_cast<size_t>(d.head_dim) * sizeof(float) + sizeof(float2));
+  return pl;
+}
+
+}  // namespace sv
+
+extern "C" {
+
+int sv_version(void) { return SV_API_VERSION; }
+
+const char* sv_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported";
+    case SV_ERR_WORKSPACE: return "workspace too small";
+    case SV_ERR_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* sv_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------- attention
+sv_status sv_verify_attention_workspace(const sv_attn_desc* desc, size_t* bytes) {
+  sv_status st = check_attn_desc(desc);
+  if (st != SV_OK) return st;
+  if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = sv::plan_attention(*desc).ws_bytes;
+  return ok();
+}
+
+sv_status sv_verify_attention(const sv_attn_desc* desc, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* page_table,
+                              const int32_t* ctx_lens, const uint64_t* block_mask, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  sv_status st = check_attn_desc(desc);
+  if (st != SV_OK) return st;
+  if (!q || !k_cache || !v_cache || !page_table || !ctx_lens || !out)
+    return fail(SV_ERR_INVALID_ARG, "q, k_cache, v_cache, page_table, ctx_lens and out are required");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(SV_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+  const int K = desc->block;
+  sv::AttnParams p;
+  memset(&p, 0, sizeof p);
+  for (int i = 0; i < K; ++i) {
+    const uint64_t m = block_mask ? block_mask[i] : ((i == 63) ? ~0ull : ((1ull << (i + 1)) - 1));
+    if (!((m >> i) & 1ull))
+      return fail(SV_ERR_INVALID_ARG, "block_mask row %d must contain its own bit", i);
+    if (K < 64 && (m >> K) != 0)
+      return fail(SV_ERR_INVALID_ARG, "block_mask row %d has bits at or beyond block %d", i, K);
+    p.mask[i] = m;
+  }
+  const sv::AttnPlan pl = sv::plan_attention(*desc);
+  if (!workspace || workspace_bytes < pl.ws_bytes)
+    return fail(SV_ERR_WORKSPACE, "attention needs %zu workspace bytes (got %zu)", pl.ws_bytes,
+                workspace ? workspace_bytes : 0);
+  if (!aligned16(workspace)) return fail(SV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.page_table = page_table;
+  p.ctx_lens = ctx_lens;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
+                                        static_cast<size_t>(desc->batch) * desc->num_kv_heads *
+                                            pl.nsplit * pl.rows * desc->head_dim * sizeof(float));
+  p.out = out;
+  p.lse = lse;
+  p.B = desc->batch;
+  p.K = K;
+  p.Hq = desc->num_q_heads;
+  p.Hkv = desc->num_kv_heads;
+  p.G = desc->num_q_heads / desc->num_kv_heads;
+  p.R = pl.rows;
+  p.P_log2 = log2i(desc->page_size);
+  p.max_pages = desc->max_pages_per_seq;
+  p.num_pages = desc->num_pages;
+  p.max_ctx = desc->max_ctx;
+  p.chunk = pl.chunk;
+  p.nsplit = pl.nsplit;
+  const float scale = desc->scale > 0.0f ? desc->scale : 1.0f / sqrtf(static_cast<float>(desc->head_dim));
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return device_status(sv::launch_attention(p, desc->head_dim, desc->dtype,
+                                            static_cast<hipStream_t>(stream)),
+                       "sv_verify_attention launch");
+}
+
+// ---------------------------------------------------------------- greedy
+static sv_status check_accept_shape(int32_t B, int32_t K, int32_t V, int min_k) {
+  if (B < 1) return fail(SV_ERR_INVALID_ARG, "B must be >= 1 (got %d)", B);
+  if (K < min_k || K > sv::kMaxBlock)
+    return fail(SV_ERR_INVALID_ARG, "K must be in [%d, 64] (got %d)", min_k, K);
+  if (V < 1) return fail(SV_ERR_INVALID_ARG, "V must be >= 1 (got %d)", V);
+  if (static_cast<int64_t>(B) * K > 65535)
+    return fail(SV_ERR_INVALID_ARG, "B * K must be <= 65535 (got %lld)",
+                static_cast<long long>(B) * K);
+  return SV_OK;
+}
+
+sv_status sv_accept_greedy_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes) {
+  sv_status st = check_accept_shape(B, K, V, 1);
+  if (st != SV_OK) return st;
+  if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = sv::greedy_workspace_bytes(B, K);
+  return ok();
+}
+
+sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                           const void* logits, const int32_t* drafts, int32_t* accept_len,
+                           int32_t* out_tokens, int32_t* argmax, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  sv_status st = check_accept_shape(B, K, V, 1);
+  if (st != SV_OK) return st;
+  if (logit_dtype != SV_F32 && logit_dtype != SV_BF16)
+    return fail(SV_ERR_UNSUPPORTED, "greedy logits must be SV_F32 or SV_BF16");
+  if (!logits || !accept_len || !out_tokens || (K > 1 && !drafts))
+    return fail(SV_ERR_INVALID_ARG, "logits, drafts, accept_len and out_tokens are required");
+  if (!aligned16(logits)) return fail(SV_ERR_INVALID_ARG, "logits must be 16-byte aligned");
+  const size_t need = sv::greedy_workspace_bytes(B, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "greedy accept needs %zu workspace bytes", need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+    return fail(SV_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
+  sv::GreedyParams p;
+  p.logits = logits;
+  p.drafts = drafts;
+  p.accept_len = accept_len;
+  p.out_tokens = out_tokens;
+  p.argmax = argmax;
+  p.keys = static_cast<unsigned long long*>(workspace);
+  p.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) +
+                                               static_cast<size_t>(B) * K * sizeof(unsigned long long));
+  p.B = B;
+  p.K = K;
+  p.V = V;
+  p.chunk = sv::greedy_chunk(V, logit_dtype);
+  p.nchunk = (V + p.chunk - 1) / p.chunk;
+  if (static_cast<int64_t>(p.nchunk) * K >= (1ll << 31))
+    return fail(SV_ERR_INVALID_ARG, "V too large");
+  return device_status(sv::launch_greedy(p, logit_dtype, static_cast<hipStream_t>(stream)),
+                       "sv_accept_greedy launch");
+}
+
+// ---------------------------------------------------------------- sampling
+sv_status sv_accept_sample_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes) {
+  sv_status st = check_accept_shape(B, K, V, 2);
+  if (st != SV_OK) return st;
+  if (static_cast<int64_t>(B) * (2 * K - 1) > 65535)
+    return fail(SV_ERR_INVALID_ARG, "B * (2K - 1) must be <= 65535");
+  if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+  const int chunk = sv::sample_chunk(V);
+  *bytes = sv::sample_workspace_bytes(B, K, V, (V + chunk - 1) / chunk);
+  return ok();
+}
+
+sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                           const void* target_logits, const void* draft_logits,
+                           const int32_t* drafts, float temperature, uint64_t seed,
+                           uint64_t offset, int32_t* accept_len, int32_t* out_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  sv_status st = check_accept_shape(B, K, V, 2);
+  if (st != SV_OK) return st;
+  if (static_cast<int64_t>(B) * (2 * K - 1) > 65535)
+    return fail(SV_ERR_INVALID_ARG, "B * (2K - 1) must be <= 65535");
+  if (logit_dtype != SV_F32 && logit_dtype != SV_BF16)
+    return fail(SV_ERR_UNSUPPORTED, "sampling logits must be SV_F32 or SV_BF16");
+  if (!(temperature > 0.0f) || !isfinite(temperature))
+    return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0 (use sv_accept_greedy for 0)");
+  if (!target_logits || !draft_logits || !drafts || !accept_len || !out_tokens)
+    return fail(SV_ERR_INVALID_ARG, "logits, drafts and outputs are required");
+  const int chunk = sv::sample_chunk(V);
+  const int nchunk = (V + chunk - 1) / chunk;
+  const size_t need = sv::sample_workspace_bytes(B, K, V, nchunk);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "sampling accept needs %zu workspace bytes", need);
+  if (!aligned16(workspace)) return fail(SV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const size_t rows = static_cast<size_t>(B) * (2 * K - 1);
+  char* w = static_cast<char*>(workspace);
+  sv::SampleParams p;
+  p.target = target_logits;
+  p.draft = draft_logits;
+  p.drafts = drafts;
+  p.accept_len = accept_len;
+  p.out_tokens = out_tokens;
+  p.part_s = reinterpret_cast<double*>(w);
+  w += rows * nchunk * sizeof(double);
+  p.race_key = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(B) * nchunk * 2 * sizeof(double);
+  p.part_m = reinterpret_cast<float*>(w);
+  w += rows * nchunk * sizeof(float);
+  p.race_idx = reinterpret_cast<int32_t*>(w);
+  w += static_cast<size_t>(B) * nchunk * 2 * sizeof(int32_t);
+  const size_t used = static_cast<size_t>(w - static_cast<char*>(workspace));
+  p.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + ((used + 15) & ~static_cast<size_t>(15)));
+  p.B = B;
+  p.K = K;
+  p.V = V;
+  p.chunk = chunk;
+  p.nchunk = nchunk;
+  p.inv_t = 1.0 / static_cast<double>(temperature);
+  p.seed = seed;
+  p.offset = offset;
+  return device_status(sv::launch_sample(p, logit_dtype, static_cast<hipStream_t>(stream)),
+                       "sv_accept_sample launch");
+}
+
+// ---------------------------------------------------------------- compressor
+static sv_status check_compress(int32_t B, int32_t C, int32_t N, int32_t D) {
+  if (B < 1 || B > 65535) return fail(SV_ERR_INVALID_ARG, "B must be in [1, 65535] (got %d)", B);
+  if (C < 1 || C > 64) return fail(SV_ERR_INVALID_ARG, "C must be in [1, 64] (got %d)", C);
+  if (N < 1 || N > 1024) return fail(SV_ERR_INVALID_ARG, "N must be in [1, 1024] (got %d)", N);
+  if (D < 128 || D % 128 != 0 || D > (1 << 20))
+    return fail(SV_ERR_INVALID_ARG, "D must be a positive multiple of 128 (got %d)", D);
+  return SV_OK;
+}
+
+sv_status sv_latent_compress_workspace(int32_t B, int32_t C, int32_t N, int32_t D, size_t* bytes) {
+  sv_status st = check_compress(B, C, N, D);
+  if (st != SV_OK) return st;
+  if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = sv::compress_workspace_bytes(B, C, N);
+  return ok();
+}
+
+sv_status sv_latent_compress(int32_t B, int32_t C, int32_t N, int32_t D, sv_dtype dtype,
+                             const void* queries, const void* feats, void* out, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  sv_status st = check_compress(B, C, N, D);
+  if (st != SV_OK) return st;
+  if (dtype != SV_F16) return fail(SV_ERR_UNSUPPORTED, "the compressor takes SV_F16 tensors");
+  if (!queries || !feats || !out) return fail(SV_ERR_INVALID_ARG, "queries, feats and out are required");
+  if (!aligned16(queries) || !aligned16(feats) || !aligned16(out))
+    return fail(SV_ERR_INVALID_ARG, "queries, feats and out must be 16-byte aligned");
+  if (!(scale >= 0.0f) || !isfinite(scale)) return fail(SV_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  const size_t need = sv::compress_workspace_bytes(B, C, N);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "compressor needs %zu workspace bytes", need);
+  sv::CompressParams p;
+  p.queries = queries;
+  p.feats = feats;
+  p.out = out;
+  p.scores = static_cast<float*>(workspace);
+  p.B = B;
+  p.C = C;
+  p.N = N;
+  p.D = D;
+  p.scale = scale > 0.0f ? scale : 1.0f;
+  return device_status(sv::launch_compress(p, static_cast<hipStream_t>(stream)),
+                       "sv_latent_compress launch");
+}
+
+// ---------------------------------------------------------------- KV append
+sv_status sv_kv_append(const sv_attn_desc* desc, int32_t n, const void* k_new, const void* v_new,
+                       const int32_t* start, const int32_t* page_table, void* k_cache,
+                       void* v_cache, void* stream) {
+  if (!desc) return fail(SV_ERR_INVALID_ARG, "desc is NULL");
+  if (desc->batch < 1 || desc->batch > 65535) return fail(SV_ERR_INVALID_ARG, "batch out of range");
+  if (desc->num_kv_heads < 1 || desc->num_kv_heads > 65535)
+    return fail(SV_ERR_INVALID_ARG, "num_kv_heads out of range");
+  if (desc->head_dim != 64 && desc->head_dim != 128)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!pow2(desc->page_size) || desc->page_size < 16 || desc->page_size > 256)
+    return fail(SV_ERR_INVALID_ARG, "page_size must be a power of two in [16, 256]");
+  if (desc->max_pages_per_seq < 1 || desc->num_pages < 1)
+    return fail(SV_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+  if (desc->dtype != SV_F32 && desc->dtype != SV_BF16 && desc->dtype != SV_F16)
+    return fail(SV_ERR_UNSUPPORTED, "unknown dtype");
+  if (n < 1 || n > 65535) return fail(SV_ERR_INVALID_ARG, "n must be in [1, 65535] (got %d)", n);
+  if (!k_new || !v_new || !start || !page_table || !k_cache || !v_cache)
+    return fail(SV_ERR_INVALID_ARG, "all arrays are required");
+  sv::AppendParams p;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.start = start;
+  p.page_table = page_table;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.B = desc->batch;
+  p.n = n;
+  p.Hkv = desc->num_kv_heads;
+  p.D = desc->head_dim;
+  p.P_log2 = log2i(desc->page_size);
+  p.max_pages = desc->max_pages_per_seq;
+  p.num_pages = desc->num_pages;
+  p.elem_bytes = desc->dtype == SV_F32 ? 4 : 2;
+  return device_status(sv::launch_kv_append(p, static_cast<hipStream_t>(stream)),
+                       "sv_kv_append launch");
+}
+
+}  // extern "C"

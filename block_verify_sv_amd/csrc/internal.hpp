@@ -1,0 +1,112 @@
+// Kernel parameter blocks and launchers of libspecverify (internal; not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kNumCUs = 256;      // MI355X compute units (8 XCDs x 32)
+constexpr int kMaxBlock = 64;     // K limit (one uint64 mask row per block row)
+constexpr int kMaxRows = 256;     // K * G limit of one KV-head tile
+
+// ---------------------------------------------------------------- verify attention
+struct AttnParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* page_table;
+  const int32_t* ctx_lens;
+  float* part_o;        // [B][Hkv][nsplit][R][D] unnormalised partial outputs
+  float2* part_ml;      // [B][Hkv][nsplit][R] (running max in log2 units, sum)
+  void* out;
+  float* lse;
+  int32_t B, K, Hq, Hkv, G, R;
+  int32_t P_log2, max_pages, num_pages, max_ctx;
+  int32_t chunk;        // keys per split
+  int32_t nsplit;       // splits allocated per (b, g)
+  float scale_log2;     // scale * log2(e)
+  uint64_t mask[kMaxBlock];
+};
+
+struct AttnPlan {
+  int chunk;
+  int nsplit;
+  int rows;             // R = K * G
+  size_t ws_bytes;
+};
+
+AttnPlan plan_attention(const sv_attn_desc& d);
+hipError_t launch_attention(const AttnParams& p, int head_dim, sv_dtype dtype,
+                            hipStream_t stream);
+
+// ---------------------------------------------------------------- greedy accept
+struct GreedyParams {
+  const void* logits;
+  const int32_t* drafts;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  int32_t* argmax;
+  unsigned long long* keys;   // [B][K] packed argmax keys (zero between calls)
+  unsigned int* counters;     // [B] arrival counters (zero between calls)
+  int32_t B, K, V;
+  int32_t chunk;              // vocabulary entries per workgroup
+  int32_t nchunk;
+};
+
+size_t greedy_workspace_bytes(int B, int K);
+int greedy_chunk(int V, sv_dtype dtype);
+hipError_t launch_greedy(const GreedyParams& p, sv_dtype dtype, hipStream_t stream);
+
+// ---------------------------------------------------------------- sampling accept
+struct SampleParams {
+  const void* target;
+  const void* draft;
+  const int32_t* drafts;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  float* part_m;              // [rows][nchunk] chunk maxima of the raw logits
+  double* part_s;             // [rows][nchunk] chunk sums of exp((x - m) / T)
+  double* race_key;           // [B][nchunk][2] chunk winners' keys (residual, p)
+  int32_t* race_idx;          // [B][nchunk][2]
+  unsigned int* counters;     // [B] (zero between calls)
+  int32_t B, K, V;
+  int32_t chunk, nchunk;
+  float inv_t;
+  uint64_t seed, offset;
+};
+
+size_t sample_workspace_bytes(int B, int K, int V, int nchunk);
+int sample_chunk(int V);
+hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stream);
+
+// ---------------------------------------------------------------- latent compressor
+struct CompressParams {
+  const void* queries;
+  const void* feats;
+  void* out;
+  float* scores;              // [B][C][N] fp32
+  int32_t B, C, N, D;
+  float scale;
+};
+
+size_t compress_workspace_bytes(int B, int C, int N);
+hipError_t launch_compress(const CompressParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------- KV append
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* start;
+  const int32_t* page_table;
+  void* k_cache;
+  void* v_cache;
+  int32_t B, n, Hkv, D, P_log2, max_pages, num_pages, elem_bytes;
+};
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
+
+}  // namespace sv

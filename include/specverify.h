@@ -1,0 +1,196 @@
+/*
+ * libspecverify -- one-pass block verification for lossless speculative decoding.
+ *
+ * A drafter proposes a block of K tokens (the anchor, i.e. the last committed
+ * token, followed by K-1 drafts); the unchanged target scores every block
+ * position in one forward over its whole context plus the block, and an
+ * acceptance rule decides how many drafts to keep (VFlash-FM page, "How VFlash-FM
+ * works", cycle figure and caption).  This library runs the data-parallel part
+ * of that step on one AMD Instinct MI355X (gfx950):
+ *
+ *   sv_verify_attention  block-causal grouped-query attention of the K block rows
+ *                        over a paged KV cache (split-KV pass + merge pass)
+ *   sv_accept_greedy     longest prefix matching the target's argmax + correction
+ *   sv_accept_sample     min(1, p/q) acceptance with a residual resample, driven
+ *                        by counter-based Philox4x64-10 uniforms
+ *   sv_latent_compress   softmax(C . F^T) . F latent visual compressor
+ *   sv_kv_append         write new K/V rows into the paged cache
+ *
+ * Conventions for every call
+ *   - Array arguments are DEVICE pointers unless stated otherwise.  The caller
+ *     owns all memory, including the workspace; the library never allocates,
+ *     frees or synchronises.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Outputs are valid once the stream reaches the call.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     nonzero status launches nothing and leaves outputs untouched.  A short
+ *     message for the last failure on the calling thread is in sv_last_error().
+ *   - Inputs must be finite.  Results are bitwise reproducible for identical
+ *     inputs, shapes and workspace contents.
+ *   - The workspace of sv_accept_greedy / sv_accept_sample holds counters: it
+ *     must be zero-filled once before its first use, and every call leaves it
+ *     zeroed again.  Two calls that share one workspace must not overlap in time.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_API_VERSION 1
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1, SV_F16 = 2 } sv_dtype;
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = -1, /* a shape, pointer or value is out of its documented range */
+  SV_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement (dtype, head_dim) */
+  SV_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than the size query says */
+  SV_ERR_DEVICE = -4       /* the HIP runtime refused a launch */
+} sv_status;
+
+int sv_version(void);
+const char* sv_status_string(int status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* sv_last_error(void);
+
+/* -------------------------------------------------------------------------------------
+ * Block-verification attention.
+ *
+ * Operation (VFlash-FM page, "How VFlash-FM works": the target scores all K block
+ * positions in one forward over the full context; demo setup: native grouped-query
+ * attention, preallocated KV caches).  For sequence b, block row i in [0, K) and
+ * query head h, with G = Hq / Hkv and KV head g = h / G:
+ *     visible keys: context positions 0 .. ctx_lens[b]-1, plus block position
+ *                   ctx_lens[b] + t whenever bit t of block_mask[i] is set;
+ *     s_j = scale * <q[b][i][h], k_j>,  out[b][i][h] = sum_j softmax(s)_j v_j,
+ *     lse[b][i][h] = log sum_j exp(s_j)  (natural log).
+ *
+ * Layouts
+ *   q          [B][K][Hq][d]               dtype
+ *   k_cache    [num_pages][Hkv][P][d]      dtype, token-major pages
+ *   v_cache    [num_pages][Hkv][d][P]      dtype, dim-major pages (each head's page is
+ *                                          d rows of P consecutive tokens)
+ *   page_table [B][max_pages_per_seq]      int32: token j of sequence b lives in page
+ *                                          page_table[b][j / P], slot j % P
+ *   ctx_lens   [B]                         int32: context tokens before the block; the
+ *                                          block's own K/V rows are already written at
+ *                                          positions ctx .. ctx+K-1 (see sv_kv_append)
+ *   block_mask HOST [K] uint64             row masks over the block keys; NULL = causal
+ *                                          (bit t of row i set iff t <= i)
+ *   out        [B][K][Hq][d]               dtype (round to nearest even from fp32)
+ *   lse        [B][K][Hq]                  fp32, optional (NULL = not written)
+ *
+ * Limits: 1 <= K <= 64; Hq % Hkv == 0; K * G <= 256; d in {64, 128}; P a power of two
+ * in [16, 256]; every block_mask row i must contain bit i and no bit >= K.
+ * ctx_lens[b] must lie in [0, max_ctx] and ctx_lens[b] + K <= max_pages_per_seq * P.
+ * Device-side, keys beyond max_ctx + K and table entries outside [0, num_pages) are
+ * never dereferenced (their K/V read as zero), so a violation gives wrong numbers,
+ * never an out-of-bounds access.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t batch;             /* B >= 1 */
+  int32_t block;             /* K */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv */
+  int32_t head_dim;          /* d */
+  int32_t page_size;         /* P */
+  int32_t max_pages_per_seq; /* row stride of page_table */
+  int32_t num_pages;         /* pages in the pool (for device-side bounds) */
+  int32_t max_ctx;           /* host-known upper bound of ctx_lens: sizes the split grid */
+  int32_t split_keys;        /* keys per split-KV work item; 0 = automatic, else a
+                                multiple of 16 */
+  float scale;               /* 0 => 1/sqrt(d) */
+  sv_dtype dtype;            /* q, caches and out */
+  int64_t sum_ctx_hint;      /* host-known sum of ctx_lens, steers the automatic split
+                                size only; 0 = unknown (taken as B * max_ctx) */
+} sv_attn_desc;
+
+/* Bytes of workspace sv_verify_attention needs for this descriptor. */
+sv_status sv_verify_attention_workspace(const sv_attn_desc* desc, size_t* bytes);
+
+sv_status sv_verify_attention(const sv_attn_desc* desc, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* page_table,
+                              const int32_t* ctx_lens, const uint64_t* block_mask, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* -------------------------------------------------------------------------------------
+ * Greedy acceptance (VFlash-FM page, caption of the cycle figure: the prefix matching
+ * the target's greedy choice is accepted, the target supplies the token at the first
+ * disagreement, the rest is discarded).
+ *   t_i = argmax_j logits[b][i][j], ties to the lowest j  (i = 0 .. K-1)
+ *   accept_len[b] = largest a <= K-1 with drafts[b][k-1] == t_{k-1} for all k <= a
+ *   out_tokens[b] = drafts[b][0 .. a-1], t_a, then -1 up to K entries
+ *   argmax[b][i]  = t_i (optional, NULL = not written)
+ * Layouts: logits [B][K][V] (SV_F32 or SV_BF16); drafts [B][K-1] int32 (draft d_k at
+ * index k-1); accept_len [B], out_tokens [B][K], argmax [B][K] int32.
+ * Limits: 1 <= K <= 64, 1 <= V < 2^31.  The workspace must be zeroed before first use.
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_accept_greedy_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes);
+sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                           const void* logits, const int32_t* drafts, int32_t* accept_len,
+                           int32_t* out_tokens, int32_t* argmax, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* -------------------------------------------------------------------------------------
+ * Sampling acceptance: the standard speculative acceptance-rejection rule (SpecFLASH
+ * README, "components": drafts verified in parallel by the target with the standard
+ * rule, so the output follows the target's distribution exactly).
+ *   p_i = softmax(target_logits[b][i] / T), q_k = softmax(draft_logits[b][k-1] / T)
+ *   for k = 1 .. K-1: accept d_k iff u_k < min(1, p_{k-1}(d_k) / q_k(d_k));
+ *   first rejection at k: resample from norm(max(0, p_{k-1} - q_k));
+ *   all accepted: bonus token from p_{K-1}.
+ * Uniforms: Philox4x64-10 with key (seed, 0), counter (offset, b, (purpose << 32) | row,
+ * j >> 2), word j & 3, u = (word >> 11) * 2^-53; purpose 0 (accept test, row = k, j = 0),
+ * purpose 1 (resample, row = target row raced over, j = token).  The resample draws
+ * argmin_j E_j / r_j with E_j = -ln(1 - u_j) over r_j > 0 (an exponential race, exact
+ * in distribution), ties to the lowest j.  The ratio test and the race run in fp64; the
+ * row log-normalisers use fp32 exponentials summed in fp64.
+ * Layouts: target_logits [B][K][V], draft_logits [B][K-1][V] (SV_F32 or SV_BF16),
+ * drafts [B][K-1] int32; outputs as for sv_accept_greedy.  A draft outside [0, V) counts
+ * as rejected (its logits are never read).
+ * Limits: 2 <= K <= 64, 1 <= V < 2^31, temperature > 0 (greedy is its own call).
+ * The workspace must be zeroed before first use.
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_accept_sample_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes);
+sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                           const void* target_logits, const void* draft_logits,
+                           const int32_t* drafts, float temperature, uint64_t seed,
+                           uint64_t offset, int32_t* accept_len, int32_t* out_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* -------------------------------------------------------------------------------------
+ * Latent visual compressor (SpecFLASH README, "components", compressor equation):
+ *   out[b] = softmax(scale * queries . feats[b]^T) . feats[b], softmax over the N rows.
+ * The printed formula has no 1/sqrt(D); pass scale = 1 for it (0 is read as 1).
+ * Layouts: queries [C][D], feats [B][N][D], out [B][C][D], all SV_F16 (fp32 accumulate).
+ * Limits: 1 <= C <= 64, 1 <= N <= 4096, D a multiple of 128.
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_latent_compress_workspace(int32_t B, int32_t C, int32_t N, int32_t D,
+                                       size_t* bytes);
+sv_status sv_latent_compress(int32_t B, int32_t C, int32_t N, int32_t D, sv_dtype dtype,
+                             const void* queries, const void* feats, void* out, float scale,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* -------------------------------------------------------------------------------------
+ * KV append: write n new token rows per sequence into the paged cache at positions
+ * start[b] .. start[b]+n-1 (the preallocated KV cache the VFlash-FM demo setup names;
+ * the block's rows must be in place before sv_verify_attention).
+ *   k_new, v_new [B][n][Hkv][d] (token-major rows, dtype of the cache); start [B] int32.
+ * Uses desc->batch, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
+ * dtype.  Positions must satisfy start[b] + n <= max_pages_per_seq * P; rows whose
+ * page-table entry is outside [0, num_pages) are skipped.  No workspace.
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_kv_append(const sv_attn_desc* desc, int32_t n, const void* k_new,
+                       const void* v_new, const int32_t* start, const int32_t* page_table,
+                       void* k_cache, void* v_cache, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */

@@ -22,6 +22,8 @@ Every function follows a passage of the pages it cites:
   SC'11), the uniform source of the sampling rule.
 * ``compress.latent_compress_ref`` -- softmax(C . F_V^T) . F_V (SpecFLASH
   README, "components", compressor equation).
+* ``kv.kv_append_ref`` -- writing the block's rows into the preallocated paged
+  KV cache (VFlash-FM page, demo setup).
 
 Parity pins: every function is pinned in ``tests/test_oracle_*.py`` against
 something other than itself (worked example, library routine, closed form,
@@ -32,9 +34,11 @@ from .attention import verify_attention_ref, single_query_ref, merge_partials_re
 from .accept import accept_greedy_ref, sample_rule, accept_sample_ref, race_ref
 from .philox import philox4x64_10, uniforms, ACCEPT, RESAMPLE
 from .compress import latent_compress_ref
+from .kv import kv_append_ref
 
 __all__ = [
     "decode", "verify_attention_ref", "single_query_ref", "merge_partials_ref",
     "accept_greedy_ref", "sample_rule", "accept_sample_ref", "race_ref",
     "philox4x64_10", "uniforms", "ACCEPT", "RESAMPLE", "latent_compress_ref",
+    "kv_append_ref",
 ]

@@ -129,6 +129,9 @@ def accept_sample_ref(target_logits, draft_logits, drafts, dtype: str, temperatu
         margin = np.inf
         for k in range(1, K):
             d = int(drafts[b][k - 1])
+            if not 0 <= d < V:                     # a token outside the vocabulary is rejected
+                a = k - 1
+                break
             lam = logp[k - 1, d] - logq[k - 1, d]
             u = float(uniforms(seed, offset, b, ACCEPT, k, np.array([0]))[0])
             thr = np.exp(min(0.0, lam))

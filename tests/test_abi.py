@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the header
+declares, and rejects invalid calls on the host before launching anything.
+
+Every call here fails validation, so nothing reaches the device even where one exists.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_verify_sv_amd as sv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "specverify.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(0x1000)          # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.LIB_PATH):
+        pytest.fail("libspecverify.so is not built (run python -m block_verify_sv_amd.build)")
+    return sv.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:sv_status|int|const char\*)\s+(sv_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 12, names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    assert lib.sv_version() == 1
+
+
+def test_descriptor_layout_matches_header():
+    """ctypes mirror: 12 four-byte fields then one int64 -> 56 bytes, int64 at offset 48."""
+    assert ctypes.sizeof(sv.AttnDesc) == 56
+    assert sv.AttnDesc.sum_ctx_hint.offset == 48
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} sv_attn_desc;", text, re.S).group(1)
+    fields = re.findall(r"^\s*(?:int32_t|int64_t|float|sv_dtype)\s+(\w+);", body, re.M)
+    assert fields == [f[0] for f in sv.AttnDesc._fields_]
+
+
+def _desc(**kw):
+    base = dict(batch=1, block=16, num_q_heads=28, num_kv_heads=4, head_dim=128, page_size=16,
+                max_pages_per_seq=1571, num_pages=1571, max_ctx=25119, split_keys=0, scale=0.0,
+                dtype=sv.SV_BF16, sum_ctx_hint=25119)
+    base.update(kw)
+    return sv.AttnDesc(**base)
+
+
+def _ws(lib, d):
+    n = ctypes.c_size_t()
+    st = lib.sv_verify_attention_workspace(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_attention_workspace_query(lib):
+    st, n = _ws(lib, _desc())
+    assert st == OK
+    # 4 KV heads x splits x 112 rows x (128 fp32 + (m, l))
+    assert n % (4 * 112 * (128 * 4 + 8)) == 0 and n > 0
+    st, n2 = _ws(lib, _desc(split_keys=1024))
+    assert st == OK and n2 == 4 * 25 * 112 * (128 * 4 + 8)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), INVALID), (dict(block=0), INVALID), (dict(block=65), INVALID),
+    (dict(num_q_heads=30), INVALID), (dict(num_q_heads=28 * 20, block=16), INVALID),
+    (dict(head_dim=96), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED), (dict(page_size=24), INVALID),
+    (dict(page_size=8), INVALID), (dict(max_ctx=-1), INVALID), (dict(max_pages_per_seq=10), INVALID),
+    (dict(split_keys=40), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(sum_ctx_hint=-5), INVALID), (dict(num_pages=0), INVALID),
+])
+def test_attention_rejects_bad_descriptors(lib, kw, code):
+    st, _ = _ws(lib, _desc(**kw))
+    assert st == code, lib.sv_last_error()
+    assert lib.sv_last_error().decode() != ""
+    st = lib.sv_verify_attention(ctypes.byref(_desc(**kw)), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                 FAKE, None, FAKE, 1 << 40, None)
+    assert st == code
+
+
+def test_attention_rejects_bad_masks_and_buffers(lib):
+    d = _desc(block=4, num_q_heads=2, num_kv_heads=1, head_dim=64, max_ctx=512,
+              max_pages_per_seq=33, num_pages=33)
+    good = (ctypes.c_uint64 * 4)(1, 3, 7, 15)
+    no_self = (ctypes.c_uint64 * 4)(1, 1, 7, 15)
+    beyond = (ctypes.c_uint64 * 4)(1, 3, 7, 31)
+    call = lambda q, mask, ws, nbytes: lib.sv_verify_attention(
+        ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, mask, FAKE, None, ws, nbytes, None)
+    assert call(FAKE, no_self, FAKE, 1 << 40) == INVALID
+    assert "own bit" in lib.sv_last_error().decode()
+    assert call(FAKE, beyond, FAKE, 1 << 40) == INVALID
+    assert call(None, good, FAKE, 1 << 40) == INVALID                 # missing q
+    assert call(ctypes.c_void_p(0x1008), good, FAKE, 1 << 40) == INVALID   # misaligned q
+    assert call(FAKE, good, None, 1 << 40) == WORKSPACE               # no workspace
+    assert call(FAKE, good, FAKE, 16) == WORKSPACE                    # too small
+    assert "workspace" in lib.sv_last_error().decode()
+
+
+def test_greedy_validation(lib):
+    n = ctypes.c_size_t()
+    assert lib.sv_accept_greedy_workspace(1, 16, 152064, ctypes.byref(n)) == OK
+    assert n.value == 16 * 8 + 4
+    for B, K, V in [(0, 16, 10), (1, 0, 10), (1, 65, 10), (1, 16, 0), (5000, 16, 10)]:
+        assert lib.sv_accept_greedy_workspace(B, K, V, ctypes.byref(n)) == INVALID
+    args = lambda dt, ws: (1, 16, 1000, dt, FAKE, FAKE, FAKE, FAKE, None, ws, 1 << 20, None)
+    assert lib.sv_accept_greedy(*args(sv.SV_F16, FAKE)) == UNSUPPORTED
+    assert lib.sv_accept_greedy(*args(sv.SV_BF16, None)) == WORKSPACE
+    assert lib.sv_accept_greedy(1, 16, 1000, sv.SV_BF16, None, FAKE, FAKE, FAKE, None, FAKE,
+                                1 << 20, None) == INVALID
+
+
+def test_sample_validation(lib):
+    n = ctypes.c_size_t()
+    assert lib.sv_accept_sample_workspace(1, 32, 152064, ctypes.byref(n)) == OK
+    assert lib.sv_accept_sample_workspace(1, 1, 100, ctypes.byref(n)) == INVALID   # K >= 2
+    call = lambda T, ws=FAKE, dt=sv.SV_BF16: lib.sv_accept_sample(
+        1, 4, 100, dt, FAKE, FAKE, FAKE, T, 1, 0, FAKE, FAKE, ws, 1 << 30, None)
+    assert call(0.0) == INVALID
+    assert call(-1.0) == INVALID
+    assert call(float("inf")) == INVALID
+    assert call(1.0, dt=sv.SV_F16) == UNSUPPORTED
+    assert call(1.0, ws=None) == WORKSPACE
+
+
+def test_compress_validation(lib):
+    n = ctypes.c_size_t()
+    assert lib.sv_latent_compress_workspace(32, 64, 576, 4096, ctypes.byref(n)) == OK
+    assert n.value == 32 * 64 * 576 * 4
+    for B, C, N, D in [(0, 64, 576, 4096), (32, 65, 576, 4096), (32, 64, 0, 4096),
+                       (32, 64, 2000, 4096), (32, 64, 576, 100)]:
+        assert lib.sv_latent_compress_workspace(B, C, N, D, ctypes.byref(n)) == INVALID
+    call = lambda dt, ws: lib.sv_latent_compress(2, 4, 8, 128, dt, FAKE, FAKE, FAKE, 1.0, ws,
+                                                 1 << 20, None)
+    assert call(sv.SV_BF16, FAKE) == UNSUPPORTED
+    assert call(sv.SV_F16, None) == WORKSPACE
+
+
+def test_kv_append_validation(lib):
+    d = _desc()
+    assert lib.sv_kv_append(ctypes.byref(d), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.sv_kv_append(ctypes.byref(d), 16, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    d2 = _desc(head_dim=80)
+    assert lib.sv_kv_append(ctypes.byref(d2), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_status_strings(lib):
+    assert lib.sv_status_string(0) == b"ok"
+    assert lib.sv_status_string(-3) == b"workspace too small"

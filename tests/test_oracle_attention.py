@@ -166,3 +166,25 @@ def test_mask_rows_respected():
         sees = any((int(mask[i]) >> t) & 1 for t in (1, 2))
         changed = not np.allclose(out[0, i], o2[0, i], atol=0, rtol=0)
         assert changed == sees, (i, sees, changed)
+
+
+def test_kv_append_round_trip():
+    """Rows appended at positions p are what the attention oracle gathers at p: a block
+    appended after the context gives the same attention as a cache built with it."""
+    inp = _small(21, B=2, K=3, Hq=2, Hkv=2, D=8, ctx=(10, 5), P=4)
+    rng = np.random.default_rng(3)
+    new_k = rng.standard_normal((2, 3, 2, 8)).astype(np.float32)
+    new_v = rng.standard_normal((2, 3, 2, 8)).astype(np.float32)
+    kc, vc = oracle.kv_append_ref(inp.k_cache, inp.v_cache, inp.page_table, inp.ctx_lens,
+                                  new_k, new_v)
+    moved = copy.copy(inp)
+    moved.k_cache, moved.v_cache = kc, vc
+    for b in range(2):
+        for g in range(2):
+            ks, vs = _token_major(moved, b, g)
+            ctx = int(inp.ctx_lens[b])
+            np.testing.assert_array_equal(ks[ctx:ctx + 3], new_k[b, :, g])
+            np.testing.assert_array_equal(vs[ctx:ctx + 3], new_v[b, :, g])
+            k0, v0 = _token_major(inp, b, g)
+            np.testing.assert_array_equal(ks[:ctx], k0[:ctx])     # context untouched
+            np.testing.assert_array_equal(vs[:ctx], v0[:ctx])

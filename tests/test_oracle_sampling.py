@@ -195,3 +195,13 @@ def test_temperature_scales_logits():
         a2, o2 = oracle.accept_sample_ref(tl * 2, dl * 2, d, "f32", 1.0, 9, off)
         np.testing.assert_array_equal(a1, a2)
         np.testing.assert_array_equal(o1, o2)
+
+
+def test_out_of_vocabulary_draft_is_rejected():
+    rng = np.random.default_rng(6)
+    tl = rng.normal(0, 3, (1, 5, 30)).astype(np.float32)
+    dl = tl[:, :4].copy()                       # q == p: in-vocabulary drafts always pass
+    for bad in (-1, 30, 10**6):
+        d = np.array([[3, 4, bad, 5]], dtype=np.int32)
+        acc, out = oracle.accept_sample_ref(tl, dl, d, "f32", 1.0, 2, 0)
+        assert acc[0] == 2 and list(out[0, :2]) == [3, 4] and 0 <= out[0, 2] < 30

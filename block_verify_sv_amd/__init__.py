@@ -235,7 +235,7 @@ def accept_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
     n = c_sz()
     _check(lib.sv_accept_sample_workspace(B, K, V, ctypes.byref(n)), "sv_accept_sample_workspace")
     if workspace is None:
-        workspace = _workspace("sample", n.value, target_logits.device, zero=True)
+        workspace = _workspace("sample", n.value, target_logits.device, zero=False)
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=target_logits.device)
         toks = torch.empty(B, K, dtype=torch.int32, device=target_logits.device)

@@ -14,7 +14,8 @@
 //     key_j = -ln(1 - u_j) / r_j,  r = max(0, p_{k-1} - q_k) (or p_{K-1} for the bonus)
 // in fp64, keeping the smallest key (lowest index on ties).  The last workgroup of a
 // sequence reduces the chunk winners in chunk order and writes the outputs.  A race
-// over p itself is carried along for the (measure-zero) case r == 0 everywhere.
+// over p itself is carried along for the (measure-zero) case r == 0 everywhere.  The
+// arrival counters are cleared by launch 1, so the workspace carries no state.
 #include <math.h>
 
 #include "common.hpp"
@@ -82,6 +83,10 @@ __global__ void __launch_bounds__(kLseThreads) row_lse_kernel(const SampleParams
   const int tid = threadIdx.x;
   const int c = blockIdx.x;
   const int rho = blockIdx.y;
+  // The race launch runs after this one on the same stream: clear its arrival counters
+  // here, so the workspace needs no initial state whatever the previous call's shape.
+  if (c == 0 && rho == 0)
+    for (int i = tid; i < p.B; i += kLseThreads) p.counters[i] = 0u;
   const void* x = row_ptr<kBF16>(p, rho);
   const int j0 = c * p.chunk;
   const int j1 = min(j0 + p.chunk, p.V);

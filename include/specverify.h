@@ -27,9 +27,10 @@
  *     message for the last failure on the calling thread is in sv_last_error().
  *   - Inputs must be finite.  Results are bitwise reproducible for identical
  *     inputs, shapes and workspace contents.
- *   - The workspace of sv_accept_greedy / sv_accept_sample holds counters: it
- *     must be zero-filled once before its first use, and every call leaves it
- *     zeroed again.  Two calls that share one workspace must not overlap in time.
+ *   - The workspace of sv_accept_greedy holds counters: it must be zero-filled
+ *     once before its first use, and every call leaves it zeroed again (so one
+ *     buffer serves calls of any shape).  Two calls that share one workspace
+ *     must not overlap in time.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -154,8 +155,8 @@ sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
  * Layouts: target_logits [B][K][V], draft_logits [B][K-1][V] (SV_F32 or SV_BF16),
  * drafts [B][K-1] int32; outputs as for sv_accept_greedy.  A draft outside [0, V) counts
  * as rejected (its logits are never read).
- * Limits: 2 <= K <= 64, 1 <= V < 2^31, temperature > 0 (greedy is its own call).
- * The workspace must be zeroed before first use.
+ * Limits: 2 <= K <= 64, 1 <= V < 2^31, B * (2K - 1) <= 65535, temperature > 0 (greedy is
+ * its own call).  The workspace needs no initial contents.
  * ------------------------------------------------------------------------------------ */
 sv_status sv_accept_sample_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes);
 sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,

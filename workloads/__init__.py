@@ -229,7 +229,9 @@ def make_greedy(rng: np.random.Generator, *, B: int, K: int, V: int, dtype: str 
     logits = _round_to(x, dtype)
     L = np.minimum(rng.geometric(0.25, size=B) - 1, K - 1).astype(np.int32)
     drafts = rng.integers(0, V, size=(B, K - 1)).astype(np.int32)
-    other = rng.integers(0, V - 1, size=B).astype(np.int32)
+    other = rng.integers(0, max(V - 1, 1), size=B).astype(np.int32)
+    if V == 1:                      # one token: every draft is the argmax
+        L[:] = K - 1
     for b in range(B):
         n = int(L[b])
         drafts[b, :n] = tok[b, :n]

@@ -80,9 +80,11 @@ sv_status check_attn_desc(const sv_attn_desc* d) {
                 static_cast<long long>(d->max_pages_per_seq) * d->page_size);
   if (static_cast<int64_t>(d->max_ctx) + d->block > (1ll << 30))
     return fail(SV_ERR_INVALID_ARG, "max_ctx too large");
-  if (d->split_keys < 0 || (d->split_keys % 16) != 0)
-    return fail(SV_ERR_INVALID_ARG, "split_keys must be 0 or a positive multiple of 16 (got %d)",
-                d->split_keys);
+  const int gran = d->page_size < 64 ? d->page_size : 64;
+  if (d->split_keys < 0 || (d->split_keys % gran) != 0 || d->split_keys > sv::kMaxSplitKeys)
+    return fail(SV_ERR_INVALID_ARG,
+                "split_keys must be 0 or a multiple of min(page_size, 64) = %d, at most 16384 "
+                "(got %d)", gran, d->split_keys);
   if (!(d->scale >= 0.0f) || !isfinite(d->scale))
     return fail(SV_ERR_INVALID_ARG, "scale must be finite and >= 0");
   if (d->sum_ctx_hint < 0) return fail(SV_ERR_INVALID_ARG, "sum_ctx_hint must be >= 0");
@@ -100,20 +102,25 @@ AttnPlan plan_attention(const sv_attn_desc& d) {
   int64_t chunk = d.split_keys;
   if (chunk == 0) {
     // one key split per compute unit: total (context + block) keys over all KV heads,
-    // spread over the 256 CUs, in multiples of 16 keys
+    // spread over the 256 CUs, in multiples of min(P, 64) keys (a split then starts on
+    // a page boundary or a 64-key boundary inside a page)
+    const int64_t gran = d.page_size < 64 ? d.page_size : 64;
     const int64_t ctx_sum =
         d.sum_ctx_hint > 0 ? d.sum_ctx_hint : static_cast<int64_t>(d.batch) * d.max_ctx;
     const int64_t work = (ctx_sum + static_cast<int64_t>(d.batch) * d.block) * d.num_kv_heads;
     chunk = (work + kNumCUs - 1) / kNumCUs;
-    chunk = (chunk + 15) / 16 * 16;
+    chunk = (chunk + gran - 1) / gran * gran;
     if (chunk < 64) chunk = 64;
-    const int64_t cap = (n_max + 15) / 16 * 16;
+    const int64_t cap = (n_max + gran - 1) / gran * gran;
     if (chunk > cap) chunk = cap;
+    if (chunk > kMaxSplitKeys) chunk = kMaxSplitKeys;
   }
   pl.chunk = static_cast<int>(chunk);
   pl.nsplit = static_cast<int>((n_max + chunk - 1) / chunk);
-  pl.ws_bytes = static_cast<size_t>(d.batch) * d.num_kv_heads * pl.nsplit * pl.rows *
-                (static_cast<size_t>(d.head_dim) * sizeof(float) + sizeof(float2));
+  const size_t esz = d.dtype == SV_F32 ? 4 : 2;
+  const size_t rows = static_cast<size_t>(d.batch) * d.num_kv_heads * pl.nsplit * pl.rows;
+  pl.o_bytes = (rows * d.head_dim * esz + 15) / 16 * 16;
+  pl.ws_bytes = pl.o_bytes + rows * sizeof(float2);
   return pl;
 }
 
@@ -177,10 +184,8 @@ sv_status sv_verify_attention(const sv_attn_desc* desc, const void* q, const voi
   p.v_cache = v_cache;
   p.page_table = page_table;
   p.ctx_lens = ctx_lens;
-  p.part_o = static_cast<float*>(workspace);
-  p.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
-                                        static_cast<size_t>(desc->batch) * desc->num_kv_heads *
-                                            pl.nsplit * pl.rows * desc->head_dim * sizeof(float));
+  p.part_o = workspace;
+  p.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + pl.o_bytes);
   p.out = out;
   p.lse = lse;
   p.B = desc->batch;

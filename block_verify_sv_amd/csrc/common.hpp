@@ -20,11 +20,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest even (inputs are finite).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Conversions below use the gfx950 packed converts (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32), which round to nearest even in the default rounding mode.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
@@ -32,16 +34,22 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) {
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // v_cvt_f16_f32: RNE
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
 // Packs two floats into one dword of 16-bit values (lo first).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_f16(lo)) | (static_cast<uint32_t>(f32_to_f16(hi)) << 16);
+  const f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+// 2^x on the hardware exp unit (v_exp_f32): results below the normal range flush to 0,
+// which is what a softmax weight that small should be.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------------ element tags
 // KPL = elements of the contraction dimension one lane holds per MFMA operand

@@ -12,6 +12,7 @@ namespace sv {
 constexpr int kNumCUs = 256;      // MI355X compute units (8 XCDs x 32)
 constexpr int kMaxBlock = 64;     // K limit (one uint64 mask row per block row)
 constexpr int kMaxRows = 256;     // K * G limit of one KV-head tile
+constexpr int kMaxSplitKeys = 16384;  // keys of one split-KV work item
 
 // ---------------------------------------------------------------- verify attention
 struct AttnParams {
@@ -20,7 +21,8 @@ struct AttnParams {
   const void* v_cache;
   const int32_t* page_table;
   const int32_t* ctx_lens;
-  float* part_o;        // [B][Hkv][nsplit][R][D] unnormalised partial outputs
+  void* part_o;         // [B][Hkv][nsplit][R][D] partial outputs divided by their own
+                        // sum, in the input dtype
   float2* part_ml;      // [B][Hkv][nsplit][R] (running max in log2 units, sum)
   void* out;
   float* lse;
@@ -36,6 +38,7 @@ struct AttnPlan {
   int chunk;
   int nsplit;
   int rows;             // R = K * G
+  size_t o_bytes;       // partial outputs (16-byte aligned), then (m, l) pairs
   size_t ws_bytes;
 };
 

@@ -104,7 +104,7 @@ typedef struct {
   int32_t num_pages;         /* pages in the pool (for device-side bounds) */
   int32_t max_ctx;           /* host-known upper bound of ctx_lens: sizes the split grid */
   int32_t split_keys;        /* keys per split-KV work item; 0 = automatic, else a
-                                multiple of 16 */
+                                multiple of min(page_size, 64), at most 16384 */
   float scale;               /* 0 => 1/sqrt(d) */
   sv_dtype dtype;            /* q, caches and out */
   int64_t sum_ctx_hint;      /* host-known sum of ctx_lens, steers the automatic split

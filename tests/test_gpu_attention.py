@@ -38,7 +38,7 @@ CASES = [
     ("bf16", 128, 16, 28, 4, 16, [1000], 0, "causal", False),
     ("bf16", 128, 16, 28, 4, 16, [1000], 64, "causal", True),     # many splits
     ("bf16", 128, 16, 28, 4, 16, [777], 16, "causal", True),      # 16-key splits, ragged tile
-    ("bf16", 128, 32, 8, 8, 5, [333, 70], 48, "ones", True),      # G=1, chunk straddles pages
+    ("bf16", 128, 32, 8, 8, 5, [333, 70], 96, "ones", True),      # G=1, 3 pages per split
     ("bf16", 64, 16, 64, 64, 5, [64], 0, "ones", False),          # SAR-like: d 64, K 5
     ("bf16", 128, 256, 14, 2, 9, [3001], 0, "random", True),      # big pages
     ("bf16", 128, 64, 64, 8, 32, [2500], 0, "causal", False),     # 256 rows: 2 row blocks
@@ -49,7 +49,7 @@ CASES = [
     ("f16", 64, 32, 12, 3, 7, [200, 300], 32, "random", True),
     ("f32", 64, 16, 2, 1, 4, [512], 0, "causal", False),
     ("f32", 128, 16, 8, 2, 6, [250, 999], 0, "random", True),
-    ("f32", 64, 64, 6, 2, 16, [77], 16, "ones", True),
+    ("f32", 64, 64, 6, 2, 16, [77], 64, "ones", True),
 ]
 
 

@@ -32,6 +32,10 @@ constexpr int kTK = 64;           // keys per tile
 constexpr int kThreads = 256;     // merge pass
 constexpr float kNegBig = -1.0e30f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
+#ifndef SV_RING_DEEP
+#define SV_RING_DEEP 4
+#endif
+constexpr int kRingDeep = SV_RING_DEEP;
 constexpr int kMaxSplitPages = kMaxSplitKeys / 16 + 2;
 
 // LDS row of key k within a tile: bits 2 and 3 swapped.  With this order the MFMA
@@ -45,20 +49,19 @@ __device__ __forceinline__ int key_of_reg(int r, int h) { return 16 * (r >> 3) +
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// Zero the 16-bit elements e >= keep of a 16-byte chunk.
+// Zero the 16-bit elements e >= keep of a 16-byte chunk (branch-free).
 __device__ __forceinline__ u32x4 keep16(u32x4 v, int keep) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    if (2 * w >= keep) v[w] = 0u;
-    else if (2 * w + 1 >= keep) v[w] &= 0xFFFFu;
+    const uint32_t m = (2 * w + 1 < keep) ? 0xFFFFFFFFu : ((2 * w < keep) ? 0xFFFFu : 0u);
+    v[w] &= m;
   }
   return v;
 }
-// Zero the fp32 elements e >= keep of a 16-byte chunk.
+// Zero the fp32 elements e >= keep of a 16-byte chunk (branch-free).
 __device__ __forceinline__ u32x4 keep32(u32x4 v, int keep) {
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
-    if (w >= keep) v[w] = 0u;
+  for (int w = 0; w < 4; ++w) v[w] &= (w < keep) ? 0xFFFFFFFFu : 0u;
   return v;
 }
 
@@ -79,9 +82,9 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
   constexpr int KBW = 2 / KW;                    // 32-key blocks per wave per tile
   constexpr int PSW = KBW * 32 / (2 * KPL);      // MFMA steps over one wave's keys
   constexpr int DB = D / 32;                     // 32-wide d blocks of O^T
-  // register tiles in the load ring: 4 (three in flight) for one row block of 16-bit
-  // data, else 2 (one in flight) to stay within the register file
-  constexpr int RING = (NRB == 1 && SZ == 2) ? 4 : 2;
+  // register tiles in the load ring (RING-1 tiles in flight): deep for one row block
+  // of 16-bit data, shallow where the row state already fills the register file
+  constexpr int RING = (NRB == 1 && SZ == 2) ? kRingDeep : 2;
   constexpr int K_LDS = 2 * kTK * KROW * SZ;
   constexpr int V_LDS = 2 * D * VROW * SZ;
   static_assert(KW == 1 || NRB == 1, "key-split waves hold one row block each");
@@ -183,15 +186,21 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
     v_key[u] = run * KR + kp * EPC;              // first key of the chunk in the tile
   }
 
+  // a page holds Hkv heads of P keys x D for K (token-major) and of D x P for V
+  // (dim-major): the same element stride per page for both caches
+  const uint32_t pstride = static_cast<uint32_t>(p.Hkv * D) << p.P_log2;
+  const S* const kc_h = kc + (static_cast<size_t>(g * D) << p.P_log2);
+  const S* const vc_h = vc + (static_cast<size_t>(g * D) << p.P_log2);
   auto load_tile = [&](Tile& r, int kt) {
     const int pos0 = kt + run * KR;
     const bool in = pos0 < k1;
     const int pg = pg_lds[in ? (pos0 >> p.P_log2) - pg0 : 0];
     r.ok = in && pg >= 0;
-    const size_t page = r.ok ? pg : 0;
-    const int slot = r.ok ? (pos0 & Pm1) : 0;
-    const S* kb = kc + (((page * p.Hkv + g) << p.P_log2) + slot) * D;
-    const S* vb = vc + (((page * p.Hkv + g) * D) << p.P_log2) + slot;
+    const uint32_t page = r.ok ? static_cast<uint32_t>(pg) : 0u;
+    const uint32_t slot = r.ok ? static_cast<uint32_t>(pos0 & Pm1) : 0u;
+    const size_t poff = static_cast<size_t>(page) * pstride;   // one 32x32 -> 64-bit multiply
+    const S* kb = kc_h + poff + slot * D;
+    const S* vb = vc_h + poff + slot;
 #pragma unroll
     for (int u = 0; u < K_PER_T; ++u) r.k[u] = *reinterpret_cast<const u32x4*>(kb + k_goff[u]);
 #pragma unroll
@@ -222,9 +231,9 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
     }
   };
 
-  // ---- running state.  m_run is a reference maximum (log2 units) that only moves when
-  // a row's maximum exceeds it by more than 2^kRescale, so the O^T accumulators are
-  // rescaled rarely; weights exp2(s - m_run) then stay below 2^kRescale.
+  // ---- running state.  m_run is a reference maximum (raw score units) that only moves
+  // when a row's maximum exceeds it by more than 2^kRescale in weight, so the O^T
+  // accumulators are rescaled rarely; weights then stay below 2^kRescale.
   float m_run[NRB], l_run[NRB];
   f32x16 oacc[NRB][DB];
 #pragma unroll
@@ -237,6 +246,11 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
       for (int e = 0; e < 16; ++e) oacc[t][db][e] = 0.0f;
   }
 
+  // Scores stay in raw dot-product units until the exponent: m_run and the row maxima
+  // are raw maxima (scale > 0 keeps the order), and 2^(scale_log2 * (s - m)) is one fma
+  // into the exp unit.
+  const float c2 = p.scale_log2;
+  const float resc = kRescale / c2;              // rescale threshold in raw units
   auto compute = [&](int buf, int kt) {
     const bool need_mask = (kt + kTK > ctx) || (kt + kTK > k1);
     const S* kbase = k_lds + buf * kTK * KROW;
@@ -245,38 +259,41 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
     for (int t = 0; t < NRB; ++t) {
       if (!active[t]) continue;
       float sv[16 * KBW];
-      float mt = -INFINITY;
 #pragma unroll
       for (int kbi = 0; kbi < KBW; ++kbi) {
         const int kb = kh * KBW + kbi;
+        const S* krow = kbase + (kb * 32 + l32) * KROW;
+        Op kop[KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          if constexpr (KPL == 8) kop[ks] = *reinterpret_cast<const u32x4*>(krow + ks * 16 + h * 8);
+          else kop[ks] = static_cast<float>(krow[h * (D / 2) + ks]);
+        }
         f32x16 acc;
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-        const S* krow = kbase + (kb * 32 + l32) * KROW;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          Op a;
-          if constexpr (KPL == 8) a = *reinterpret_cast<const u32x4*>(krow + ks * 16 + h * 8);
-          else a = static_cast<float>(krow[h * (D / 2) + ks]);
-          acc = Mfma<Tag>::step(a, qop[t][ks], acc);
-        }
+        for (int ks = 0; ks < KSTEPS; ++ks) acc = Mfma<Tag>::step(kop[ks], qop[t][ks], acc);
+        if (!need_mask) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = acc[r] * p.scale_log2;
-          if (need_mask) {
+          for (int r = 0; r < 16; ++r) sv[kbi * 16 + r] = acc[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
             const int pos = kt + kb * 32 + key_of_reg(r, h);
-            bool vis = pos < k1;
-            if (pos >= ctx) vis = vis && ((rmask[t] >> (pos - ctx)) & 1ull);
-            x = vis ? x : -INFINITY;
+            const int t2 = pos - ctx;
+            const bool vis = pos < k1 && (t2 < 0 || ((rmask[t] >> (t2 & 63)) & 1ull));
+            sv[kbi * 16 + r] = vis ? acc[r] : -INFINITY;
           }
-          sv[kbi * 16 + r] = x;
-          mt = fmaxf(mt, x);
         }
       }
+      float mt = sv[0];
+#pragma unroll
+      for (int e = 1; e < 16 * KBW; ++e) mt = fmaxf(mt, sv[e]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (__any(mt > m_run[t] + kRescale)) {      // wave-uniform: rare after the first tile
+      if (__any(mt > m_run[t] + resc)) {         // wave-uniform: rare after the first tile
         const float m_new = fmaxf(m_run[t], mt);
-        const float alpha = fast_exp2(m_run[t] - m_new);
+        const float alpha = fast_exp2((m_run[t] - m_new) * c2);
         m_run[t] = m_new;
         l_run[t] *= alpha;
 #pragma unroll
@@ -284,11 +301,11 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
 #pragma unroll
           for (int e = 0; e < 16; ++e) oacc[t][db][e] *= alpha;
       }
-      const float mref = m_run[t];
+      const float mneg = -m_run[t] * c2;
       float psum = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16 * KBW; ++e) {
-        sv[e] = fast_exp2(sv[e] - mref);
+        sv[e] = fast_exp2(fmaf(sv[e], c2, mneg));
         psum += sv[e];
       }
       l_run[t] += psum;
@@ -303,17 +320,18 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
         } else {
           bop = sv[psi];
         }
+        Op vop[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const S* vrow = vbase + (db * 32 + l32) * VROW;
-          Op a;
           if constexpr (KPL == 8) {
-            a = *reinterpret_cast<const u32x4*>(vrow + ps * 16 + h * 8);
+            vop[db] = *reinterpret_cast<const u32x4*>(vrow + ps * 16 + h * 8);
           } else {
-            a = static_cast<float>(vrow[32 * (ps >> 4) + key_of_reg(ps & 15, h)]);
+            vop[db] = static_cast<float>(vrow[32 * (ps >> 4) + key_of_reg(ps & 15, h)]);
           }
-          oacc[t][db] = Mfma<Tag>::step(a, bop, oacc[t][db]);
         }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[t][db] = Mfma<Tag>::step(vop[db], bop, oacc[t][db]);
       }
     }
   };
@@ -333,31 +351,18 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
     if (j + 1 < nt) store_tile(rs, buf ^ 1, k0 + (j + 1) * kTK);
     __syncthreads();
   };
-  if constexpr (RING == 4) {
-    Tile r0, r1, r2, r3;
-    load_tile(r0, k0);
-    load_tile(r1, tile_at(1));
-    load_tile(r2, tile_at(2));
-    store_tile(r0, 0, k0);
-    __syncthreads();
-    for (int j = 0; j < nt; j += 4) {
-      step(j, r3, r1, 0);
-      if (j + 1 >= nt) break;
-      step(j + 1, r0, r2, 1);
-      if (j + 2 >= nt) break;
-      step(j + 2, r1, r3, 0);
-      if (j + 3 >= nt) break;
-      step(j + 3, r2, r0, 1);
-    }
-  } else {
-    Tile r0, r1;
-    load_tile(r0, k0);
-    store_tile(r0, 0, k0);
-    __syncthreads();
-    for (int j = 0; j < nt; j += 2) {
-      step(j, r1, r1, 0);
-      if (j + 1 >= nt) break;
-      step(j + 1, r0, r0, 1);
+  Tile r[RING];
+  load_tile(r[0], k0);
+#pragma unroll
+  for (int u = 1; u < RING - 1; ++u) load_tile(r[u], tile_at(u));
+  store_tile(r[0], 0, k0);
+  __syncthreads();
+  for (int j0 = 0; j0 < nt; j0 += RING) {
+#pragma unroll
+    for (int u = 0; u < RING; ++u) {
+      const int j = j0 + u;
+      if (j >= nt) break;
+      step(j, r[(u + RING - 1) % RING], r[(u + 1) % RING], j & 1);
     }
   }
 
@@ -381,7 +386,7 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
     if (active[0]) {
       const float m2 = stage[0], l2 = stage[1];
       const float m = fmaxf(m_run[0], m2);
-      const float a1 = fast_exp2(m_run[0] - m), a2 = fast_exp2(m2 - m);
+      const float a1 = fast_exp2((m_run[0] - m) * c2), a2 = fast_exp2((m2 - m) * c2);
       m_run[0] = m;
       l_run[0] = l_run[0] * a1 + l2 * a2;
 #pragma unroll
@@ -414,7 +419,7 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
             *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
           }
         }
-      if (h == 0) p.part_ml[rowid] = make_float2(m_run[t], l_run[t]);
+      if (h == 0) p.part_ml[rowid] = make_float2(m_run[t] * c2, l_run[t]);   // m in log2 units
     }
   }
 }

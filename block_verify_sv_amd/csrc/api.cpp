@@ -118,9 +118,11 @@ AttnPlan plan_attention(const sv_attn_desc& d) {
   pl.chunk = static_cast<int>(chunk);
   pl.nsplit = static_cast<int>((n_max + chunk - 1) / chunk);
   const size_t esz = d.dtype == SV_F32 ? 4 : 2;
-  const size_t rows = static_cast<size_t>(d.batch) * d.num_kv_heads * pl.nsplit * pl.rows;
-  pl.o_bytes = (rows * d.head_dim * esz + 15) / 16 * 16;
-  pl.ws_bytes = pl.o_bytes + rows * sizeof(float2);
+  const size_t units = static_cast<size_t>(d.batch) * d.num_kv_heads * pl.nsplit;
+  // partial outputs are stored in whole 32-row blocks (the accumulator tile order)
+  const size_t padded_rows = static_cast<size_t>((pl.rows + 31) / 32 * 32);
+  pl.o_bytes = (units * padded_rows * d.head_dim * esz + 15) / 16 * 16;
+  pl.ws_bytes = pl.o_bytes + units * pl.rows * sizeof(float2);
   return pl;
 }
 

@@ -15,11 +15,12 @@
 // query rows on N, so each lane owns one query row), applies the block mask, runs the
 // online softmax in registers, and accumulates O^T = V^T . P^T.
 // Output per row: the partial output divided by its own sum, in the input dtype (half the
-// bytes of fp32 for 16-bit inputs), its reference maximum m (log2 units) and sum l.
+// bytes of fp32 for 16-bit inputs) and in the accumulator's register order, its
+// reference maximum m (log2 units) and sum l.
 //
-// Merge pass: one workgroup per output row; every (split, 32-element slice) pair has its
-// own thread, so all partial loads are in flight at once, and the splits are combined
-// in a fixed order:
+// Merge pass: one workgroup per (32-wide d block, 32-row block, sequence x KV head); its
+// waves read the partial tiles in the same register order (contiguous runs) and combine
+// the splits in a fixed order:
 //   m = max_s m_s, w_s = l_s 2^(m_s - m), out = sum_s w_s O_s / sum_s w_s,
 //   lse = (m + log2 sum_s w_s) * ln 2      (O_s: split s's output, already divided by l_s).
 #include "common.hpp"
@@ -29,7 +30,6 @@ namespace sv {
 namespace {
 
 constexpr int kTK = 64;           // keys per tile
-constexpr int kThreads = 256;     // merge pass
 constexpr float kNegBig = -1.0e30f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
 #ifndef SV_RING_DEEP
@@ -65,11 +65,13 @@ __device__ __forceinline__ u32x4 keep32(u32x4 v, int keep) {
   return v;
 }
 
-template <class Tag, int D, int NRB, int KW>
-__global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParams p) {
+// Split kernel.  RG row-group waves x KW key-part waves; wave (rg, kh) owns row blocks
+// rg, rg + RG, ... (NRB of them) and keys [32 kh*KBW, 32 (kh+1)*KBW) of every tile.
+template <class Tag, int D, int RG, int NRB, int KW, int RING>
+__global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnParams p) {
   using S = typename Tag::store_t;
   using Op = typename Mfma<Tag>::op_t;
-  constexpr int T = 256 * KW;                    // threads: 4 row waves x KW key waves
+  constexpr int T = 64 * RG * KW;                // threads
   constexpr int KPL = Tag::KPL;
   constexpr int SZ = Tag::kBytes;
   constexpr int EPC = 16 / SZ;                   // elements per 16-byte chunk
@@ -82,13 +84,11 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
   constexpr int KBW = 2 / KW;                    // 32-key blocks per wave per tile
   constexpr int PSW = KBW * 32 / (2 * KPL);      // MFMA steps over one wave's keys
   constexpr int DB = D / 32;                     // 32-wide d blocks of O^T
-  // register tiles in the load ring (RING-1 tiles in flight): deep for one row block
-  // of 16-bit data, shallow where the row state already fills the register file
-  constexpr int RING = (NRB == 1 && SZ == 2) ? kRingDeep : 2;
   constexpr int K_LDS = 2 * kTK * KROW * SZ;
   constexpr int V_LDS = 2 * D * VROW * SZ;
-  static_assert(KW == 1 || NRB == 1, "key-split waves hold one row block each");
-  static_assert(KW == 1 || 4 * 64 * (2 + DB * 16) * 4 <= K_LDS + V_LDS, "combine stage");
+  constexpr int NSLOT = NRB * (4 * DB + 1);      // 16-byte combine slots per lane
+  static_assert(KW == 1 || NSLOT * RG * 64 * 16 <= K_LDS + V_LDS, "combine stage");
+  static_assert(K_PER_T >= 1 && V_PER_T >= 1, "tile chunks per thread");
 
   __shared__ __align__(16) char smem[K_LDS + V_LDS];
   __shared__ int32_t pg_lds[kMaxSplitPages];
@@ -100,74 +100,80 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int rbw = wave & 3;                      // first row block of this wave
-  const int kh = wave >> 2;                      // key half of each tile (KW == 2)
+  const int rg = wave % RG;                      // row group: row blocks rg + RG*t
+  const int kh = wave / RG;                      // key part of each tile
   const int s = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
 
-  int ctx = p.ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
-  const int n_keys = ctx + p.K;
+  // ---- start-up.  Nothing below needs the context length until the early-exit test,
+  // so every independent load is issued before the first wait and they share one round
+  // trip: the page ids of the prologue tiles (read directly from the table, so those
+  // tiles' loads follow after a single dependent read), the page ids of the whole split
+  // (staged in LDS for the later tiles), the query rows and the block mask.  All of them
+  // are unconditional loads at clamped, in-bounds indices: a load under a branch would
+  // make the compiler wait for it before the next one.
   const int k0 = s * p.chunk;
-  if (k0 >= n_keys) return;                      // this sequence has fewer splits
-  const int k1 = min(k0 + p.chunk, n_keys);
+  const int pg0 = k0 >> p.P_log2;
   const int Pm1 = (1 << p.P_log2) - 1;
   const int32_t* table = p.page_table + static_cast<size_t>(b) * p.max_pages;
-  const S* kc = static_cast<const S*>(p.k_cache);
-  const S* vc = static_cast<const S*>(p.v_cache);
-
-  // ---- page ids of this split, once (entries outside the pool become -1: read as zero)
-  const int pg0 = k0 >> p.P_log2;
-  const int npg = ((k1 - 1) >> p.P_log2) - pg0 + 1;
-  for (int i = tid; i < npg; i += T) {
-    const int pg = table[pg0 + i];
-    pg_lds[i] = static_cast<unsigned>(pg) < static_cast<unsigned>(p.num_pages) ? pg : -1;
+  const int last_page = p.max_pages - 1;
+  const int KR = min(Pm1 + 1, kTK);              // keys of one run (see tile staging)
+  const int TPR = T * KR / kTK;                  // threads per run
+  const int run = tid / TPR;
+  const int li = tid - run * TPR;
+  const int ntmax = (p.chunk + kTK - 1) / kTK;   // tiles of a full split
+  int pg_pro[RING - 1];
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u) {
+    const int pos0 = k0 + min(u, ntmax - 1) * kTK + run * KR;
+    pg_pro[u] = table[min(pos0 >> p.P_log2, last_page)];
   }
-
-  // ---- query operand (B of S^T = K . Q^T): lane owns query row 32*rb + l32
+  constexpr int NPT = (kMaxSplitPages + T - 1) / T;
+  const int npg = min(((k0 + p.chunk - 1) >> p.P_log2) - pg0 + 1, p.max_pages - pg0);
+  int pg_all[NPT];
+#pragma unroll
+  for (int u = 0; u < NPT; ++u)
+    pg_all[u] = u * T < npg ? table[min(pg0 + tid + u * T, last_page)] : -1;   // uniform test
+  // query operand (B of S^T = K . Q^T): lane owns query row 32*rb + l32 (padding rows
+  // past R read row R-1; their results are never stored)
   Op qop[NRB][KSTEPS];
   uint64_t rmask[NRB];
   bool active[NRB];
 #pragma unroll
   for (int t = 0; t < NRB; ++t) {
-    const int rb = rbw + 4 * t;
-    const int r = rb * 32 + l32;
+    const int rb = rg + RG * t;
+    const int r = min(rb * 32 + l32, p.R - 1);
     active[t] = rb * 32 < p.R;
-    rmask[t] = 0;
-    const S* qp = nullptr;
-    if (r < p.R) {
-      const int i = r / p.G;
-      const int head = g * p.G + (r - i * p.G);
-      qp = static_cast<const S*>(p.q) + ((static_cast<size_t>(b) * p.K + i) * p.Hq + head) * D;
-      rmask[t] = p.mask[i];
-    }
+    const int i = r / p.G;
+    const int head = g * p.G + (r - i * p.G);
+    const S* qp = static_cast<const S*>(p.q) + ((static_cast<size_t>(b) * p.K + i) * p.Hq + head) * D;
+    rmask[t] = p.mask[i];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       if constexpr (KPL == 8) {
-        qop[t][ks] = qp ? *reinterpret_cast<const u32x4*>(qp + ks * 16 + h * 8) : zero4();
+        qop[t][ks] = *reinterpret_cast<const u32x4*>(qp + ks * 16 + h * 8);
       } else {
-        qop[t][ks] = qp ? static_cast<float>(qp[h * (D / 2) + ks]) : 0.0f;
+        qop[t][ks] = static_cast<float>(qp[h * (D / 2) + ks]);
       }
     }
   }
+  const S* kc = static_cast<const S*>(p.k_cache);
+  const S* vc = static_cast<const S*>(p.v_cache);
 
   // ---- tile staging: global -> register ring -> LDS.  A 64-key tile is split into
   // runs of KR = min(P, 64) keys that lie in one page; each thread owns a fixed set of
   // 16-byte chunks (K_PER_T of K, V_PER_T of V) inside one run, so a tile costs one
   // page-id lookup per thread and constant offsets from two base pointers.  Loads are
-  // branch-free: a run past the split end or on an unmapped page reads page 0 and is
-  // zeroed when written to LDS -- never at load time, which would make the load wait
-  // for its data and empty the ring.
+  // branch-free: a run on an unmapped page reads page 0, and a run past the split end
+  // reads whatever its (in-pool) page holds; both are zeroed when written to LDS --
+  // never at load time, which would make the load wait for its data and empty the ring.
   struct Tile {
     u32x4 k[K_PER_T];
     u32x4 v[V_PER_T];
-    int ok;                                      // this thread's run is valid
+    int pos0;                                    // first key of this thread's run
+    bool page_ok;                                // the run's page id is inside the pool
   };
-  const int KR = min(Pm1 + 1, kTK);              // keys of one run
-  const int TPR = T * KR / kTK;                  // threads per run
-  const int run = tid / TPR;
-  const int li = tid - run * TPR;
   const int KGR = KR / EPC;                      // EPC-key groups per run row of V
   int k_goff[K_PER_T], k_loff[K_PER_T], v_goff[V_PER_T], v_loff[V_PER_T], v_key[V_PER_T];
 #pragma unroll
@@ -191,13 +197,11 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
   const uint32_t pstride = static_cast<uint32_t>(p.Hkv * D) << p.P_log2;
   const S* const kc_h = kc + (static_cast<size_t>(g * D) << p.P_log2);
   const S* const vc_h = vc + (static_cast<size_t>(g * D) << p.P_log2);
-  auto load_tile = [&](Tile& r, int kt) {
-    const int pos0 = kt + run * KR;
-    const bool in = pos0 < k1;
-    const int pg = pg_lds[in ? (pos0 >> p.P_log2) - pg0 : 0];
-    r.ok = in && pg >= 0;
-    const uint32_t page = r.ok ? static_cast<uint32_t>(pg) : 0u;
-    const uint32_t slot = r.ok ? static_cast<uint32_t>(pos0 & Pm1) : 0u;
+  auto load_tile = [&](Tile& r, int kt, int pg) {
+    r.pos0 = kt + run * KR;
+    r.page_ok = static_cast<unsigned>(pg) < static_cast<unsigned>(p.num_pages);
+    const uint32_t page = r.page_ok ? static_cast<uint32_t>(pg) : 0u;
+    const uint32_t slot = static_cast<uint32_t>(r.pos0 & Pm1);
     const size_t poff = static_cast<size_t>(page) * pstride;   // one 32x32 -> 64-bit multiply
     const S* kb = kc_h + poff + slot * D;
     const S* vb = vc_h + poff + slot;
@@ -206,25 +210,46 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
 #pragma unroll
     for (int u = 0; u < V_PER_T; ++u) r.v[u] = *reinterpret_cast<const u32x4*>(vb + v_goff[u]);
   };
+  Tile r[RING];
+#pragma unroll
+  for (int u = 0; u < RING - 1; ++u) load_tile(r[u], k0 + min(u, ntmax - 1) * kTK, pg_pro[u]);
+
+  // ---- the context length: the first wait of the kernel
+  int ctx = p.ctx_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  const int n_keys = ctx + p.K;
+  if (k0 >= n_keys) return;                      // this sequence has fewer splits
+  const int k1 = min(k0 + p.chunk, n_keys);
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int i = tid + u * T;
+    if (i < npg)
+      pg_lds[i] = static_cast<unsigned>(pg_all[u]) < static_cast<unsigned>(p.num_pages) ? pg_all[u] : -1;
+  }
+  auto page_of = [&](int kt) {                   // page id of this thread's run of tile kt
+    const int pos0 = kt + run * KR;
+    return pos0 < k1 ? pg_lds[(pos0 >> p.P_log2) - pg0] : -1;
+  };
 
   auto store_tile = [&](const Tile& r, int buf, int kt) {
     S* kl = k_lds + buf * kTK * KROW;
     S* vl = v_lds + buf * D * VROW;
+    const bool ok = r.page_ok && r.pos0 < k1;
     if (kt + kTK <= k1) {                        // interior tile: zero only unmapped runs
 #pragma unroll
       for (int u = 0; u < K_PER_T; ++u)
-        *reinterpret_cast<u32x4*>(kl + k_loff[u]) = r.ok ? r.k[u] : zero4();
+        *reinterpret_cast<u32x4*>(kl + k_loff[u]) = ok ? r.k[u] : zero4();
 #pragma unroll
       for (int u = 0; u < V_PER_T; ++u)
-        *reinterpret_cast<u32x4*>(vl + v_loff[u]) = r.ok ? r.v[u] : zero4();
+        *reinterpret_cast<u32x4*>(vl + v_loff[u]) = ok ? r.v[u] : zero4();
     } else {                                     // tail tile: also zero keys past k1
       const int left = k1 - kt;
 #pragma unroll
       for (int u = 0; u < K_PER_T; ++u)
-        *reinterpret_cast<u32x4*>(kl + k_loff[u]) = r.ok ? r.k[u] : zero4();
+        *reinterpret_cast<u32x4*>(kl + k_loff[u]) = ok ? r.k[u] : zero4();
 #pragma unroll
       for (int u = 0; u < V_PER_T; ++u) {
-        u32x4 v = r.ok ? r.v[u] : zero4();
+        u32x4 v = ok ? r.v[u] : zero4();
         v = (SZ == 2) ? keep16(v, left - v_key[u]) : keep32(v, left - v_key[u]);
         *reinterpret_cast<u32x4*>(vl + v_loff[u]) = v;
       }
@@ -255,10 +280,8 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
     const bool need_mask = (kt + kTK > ctx) || (kt + kTK > k1);
     const S* kbase = k_lds + buf * kTK * KROW;
     const S* vbase = v_lds + buf * D * VROW;
-#pragma unroll
-    for (int t = 0; t < NRB; ++t) {
-      if (!active[t]) continue;
-      float sv[16 * KBW];
+    f32x16 sacc[NRB][KBW];
+    auto scores = [&](int t) {
 #pragma unroll
       for (int kbi = 0; kbi < KBW; ++kbi) {
         const int kb = kh * KBW + kbi;
@@ -269,21 +292,30 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
           if constexpr (KPL == 8) kop[ks] = *reinterpret_cast<const u32x4*>(krow + ks * 16 + h * 8);
           else kop[ks] = static_cast<float>(krow[h * (D / 2) + ks]);
         }
-        f32x16 acc;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+        for (int e = 0; e < 16; ++e) sacc[t][kbi][e] = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) acc = Mfma<Tag>::step(kop[ks], qop[t][ks], acc);
+        for (int ks = 0; ks < KSTEPS; ++ks) sacc[t][kbi] = Mfma<Tag>::step(kop[ks], qop[t][ks], sacc[t][kbi]);
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < NRB; ++t) {
+      if (!active[t]) continue;
+      scores(t);
+      float sv[16 * KBW];
+#pragma unroll
+      for (int kbi = 0; kbi < KBW; ++kbi) {
+        const int kb = kh * KBW + kbi;
         if (!need_mask) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sv[kbi * 16 + r] = acc[r];
+          for (int r = 0; r < 16; ++r) sv[kbi * 16 + r] = sacc[t][kbi][r];
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int pos = kt + kb * 32 + key_of_reg(r, h);
             const int t2 = pos - ctx;
             const bool vis = pos < k1 && (t2 < 0 || ((rmask[t] >> (t2 & 63)) & 1ull));
-            sv[kbi * 16 + r] = vis ? acc[r] : -INFINITY;
+            sv[kbi * 16 + r] = vis ? sacc[t][kbi][r] : -INFINITY;
           }
         }
       }
@@ -311,7 +343,6 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
       l_run[t] += psum;
 #pragma unroll
       for (int psi = 0; psi < PSW; ++psi) {
-        const int ps = kh * PSW + psi;           // MFMA step within the tile
         Op bop;
         if constexpr (KPL == 8) {
           const float* pv = &sv[psi * 8];
@@ -323,6 +354,7 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
         Op vop[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
+          const int ps = kh * PSW + psi;         // MFMA step within the tile
           const S* vrow = vbase + (db * 32 + l32) * VROW;
           if constexpr (KPL == 8) {
             vop[db] = *reinterpret_cast<const u32x4*>(vrow + ps * 16 + h * 8);
@@ -346,15 +378,12 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
   const int nt = (k1 - k0 + kTK - 1) / kTK;
   auto tile_at = [&](int j) { return k0 + min(j, nt - 1) * kTK; };
   auto step = [&](int j, Tile& rl, const Tile& rs, int buf) {
-    load_tile(rl, tile_at(j + RING - 1));
+    const int kt = tile_at(j + RING - 1);
+    load_tile(rl, kt, page_of(kt));
     compute(buf, k0 + j * kTK);
     if (j + 1 < nt) store_tile(rs, buf ^ 1, k0 + (j + 1) * kTK);
     __syncthreads();
   };
-  Tile r[RING];
-  load_tile(r[0], k0);
-#pragma unroll
-  for (int u = 1; u < RING - 1; ++u) load_tile(r[u], tile_at(u));
   store_tile(r[0], 0, k0);
   __syncthreads();
   for (int j0 = 0; j0 < nt; j0 += RING) {
@@ -366,44 +395,63 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
     }
   }
 
-  // ---- the row's sum over both lane halves, then (KW == 2) the two key-half waves of
-  // a row block combine through LDS (the tile buffers are free after the last barrier)
+  // ---- the row's sum over both lane halves, then (KW == 2) the two key-part waves of
+  // a row group combine through LDS (the tile buffers are free after the last barrier)
 #pragma unroll
   for (int t = 0; t < NRB; ++t) l_run[t] += __shfl_xor(l_run[t], 32);
   if constexpr (KW == 2) {
-    constexpr int SW = 2 + DB * 16;              // floats staged per lane
-    float* stage = reinterpret_cast<float*>(smem) + (rbw * 64 + lane) * SW;
-    if (kh == 1 && active[0]) {
-      stage[0] = m_run[0];
-      stage[1] = l_run[0];
+    // staged as [slot][row group][lane] 16-byte slots: every LDS access of a wave is one
+    // contiguous, conflict-free 1 KB run
+    f32x4* stage = reinterpret_cast<f32x4*>(smem);
+    auto slot = [&](int t, int c) { return ((t * (4 * DB + 1) + c) * RG + rg) * 64 + lane; };
+    if (kh == 1) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int t = 0; t < NRB; ++t) {
+        if (!active[t]) continue;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) stage[2 + db * 16 + e] = oacc[0][db][e];
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            stage[slot(t, db * 4 + q4)] = f32x4{oacc[t][db][4 * q4], oacc[t][db][4 * q4 + 1],
+                                                oacc[t][db][4 * q4 + 2], oacc[t][db][4 * q4 + 3]};
+        stage[slot(t, 4 * DB)] = f32x4{m_run[t], l_run[t], 0.0f, 0.0f};
+      }
     }
     __syncthreads();
     if (kh == 1) return;
-    if (active[0]) {
-      const float m2 = stage[0], l2 = stage[1];
-      const float m = fmaxf(m_run[0], m2);
-      const float a1 = fast_exp2((m_run[0] - m) * c2), a2 = fast_exp2((m2 - m) * c2);
-      m_run[0] = m;
-      l_run[0] = l_run[0] * a1 + l2 * a2;
+#pragma unroll
+    for (int t = 0; t < NRB; ++t) {
+      if (!active[t]) continue;
+      const f32x4 ml2 = stage[slot(t, 4 * DB)];
+      const float m = fmaxf(m_run[t], ml2[0]);
+      const float a1 = fast_exp2((m_run[t] - m) * c2), a2 = fast_exp2((ml2[0] - m) * c2);
+      m_run[t] = m;
+      l_run[t] = l_run[t] * a1 + ml2[1] * a2;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[0][db][e] = oacc[0][db][e] * a1 + stage[2 + db * 16 + e] * a2;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 o2 = stage[slot(t, db * 4 + q4)];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            oacc[t][db][4 * q4 + e] = oacc[t][db][4 * q4 + e] * a1 + o2[e] * a2;
+        }
     }
   }
 
-  // ---- partial results: O / l in the input dtype, (m, l) in fp32
+  // ---- partial results: O / l in the input dtype, (m, l) in fp32.  O is kept in the
+  // accumulator's own order, [b, g][row block][d block][register quad][split][lane] x 4
+  // consecutive d values: each store instruction of a wave writes one contiguous run
+  // (512 bytes for 16-bit data), and the merge reads every split of one (row block,
+  // d block, quad) as a single contiguous stretch.
+  const int RBT = (p.R + 31) >> 5;
+  const size_t bg = static_cast<size_t>(b) * p.Hkv + g;
 #pragma unroll
   for (int t = 0; t < NRB; ++t) {
     if (!active[t]) continue;
-    const int r = (rbw + 4 * t) * 32 + l32;
+    const int rb = rg + RG * t;
+    const int r = rb * 32 + l32;
     if (r < p.R) {
-      const size_t rowid = ((static_cast<size_t>(b) * p.Hkv + g) * p.nsplit + s) * p.R + r;
-      S* po = static_cast<S*>(p.part_o) + rowid * D;
       const float inv = l_run[t] > 0.0f ? 1.0f / l_run[t] : 0.0f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -411,7 +459,8 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
         for (int q4 = 0; q4 < 4; ++q4) {
           const float o[4] = {oacc[t][db][4 * q4], oacc[t][db][4 * q4 + 1],
                               oacc[t][db][4 * q4 + 2], oacc[t][db][4 * q4 + 3]};
-          S* dst = po + db * 32 + q4 * 8 + h * 4;
+          S* dst = static_cast<S*>(p.part_o) +
+                   ((((bg * RBT + rb) * DB + db) * 4 + q4) * p.nsplit + s) * 256 + lane * 4;
           if constexpr (SZ == 2) {
             const uint2 v = {Tag::pack2(o[0] * inv, o[1] * inv), Tag::pack2(o[2] * inv, o[3] * inv)};
             *reinterpret_cast<uint2*>(dst) = v;
@@ -419,123 +468,146 @@ __global__ void __launch_bounds__(256 * KW, 1) attn_split_kernel(const AttnParam
             *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
           }
         }
-      if (h == 0) p.part_ml[rowid] = make_float2(m_run[t] * c2, l_run[t]);   // m in log2 units
+      if (h == 0) {
+        const size_t rowid = (bg * p.nsplit + s) * p.R + r;
+        p.part_ml[rowid] = make_float2(m_run[t] * c2, l_run[t]);   // m in log2 units
+      }
     }
   }
 }
 
-// 32 consecutive partial-output elements as floats.
+// Four consecutive partial-output elements as floats.
 template <class Tag>
-__device__ __forceinline__ void load32(const typename Tag::store_t* src, float* x) {
+__device__ __forceinline__ f32x4 load4(const typename Tag::store_t* src) {
   if constexpr (Tag::kBytes == 2) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(src + 8 * q);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        x[8 * q + e] = Tag::to_f32(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))));
-    }
+    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    return f32x4{Tag::to_f32(static_cast<uint16_t>(w.x)), Tag::to_f32(static_cast<uint16_t>(w.x >> 16)),
+                 Tag::to_f32(static_cast<uint16_t>(w.y)), Tag::to_f32(static_cast<uint16_t>(w.y >> 16))};
   } else {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(src + 4 * q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * q + e] = w[e];
-    }
+    return *reinterpret_cast<const f32x4*>(src);
   }
 }
+
+// Merge: one workgroup per (d block of 32 x register quad, row block of 32, sequence b x
+// KV head g).  Lane l owns row 32*rb + l%32 and the 4 d values 8q + 4(l/32) .. +3 of the
+// d block -- the partial layout's own order, so a wave's load of one split is one
+// contiguous 512-byte run.  Wave w folds splits w, w+4, ... in batches of kMergeBatch
+// (all loads of a batch in flight) with a running maximum; the four wave states are
+// combined in wave order through LDS.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 16;
 
 template <class Tag, int D>
-__global__ void __launch_bounds__(kThreads) attn_merge_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(kMergeWaves * 64) attn_merge_kernel(const AttnParams p) {
   using S = typename Tag::store_t;
-  constexpr int TPS = D / 32;                    // threads per split: 32 elements each
-  constexpr int SPP = kThreads / TPS;            // splits per pass
-  __shared__ float red[kThreads / kWave];
-  __shared__ float acc_lds[SPP][D + 4];
-  __shared__ float l_lds[SPP];
+  constexpr int DB = D / 32;
+  __shared__ f32x4 st[2][kMergeWaves][64];       // accumulator quad, (m, l) per lane
 
   const int tid = threadIdx.x;
-  const int row = blockIdx.x;                    // over B * K * Hq
-  const int hq = row % p.Hq;
-  const int i = (row / p.Hq) % p.K;
-  const int b = row / (p.Hq * p.K);
-  const int g = hq / p.G;
-  const int r = i * p.G + (hq - g * p.G);
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int db = blockIdx.x >> 2;
+  const int q = blockIdx.x & 3;
+  const int rb = blockIdx.y;
+  const int bg = blockIdx.z;                     // b * Hkv + g
+  const int b = bg / p.Hkv;
+  const int g = bg - b * p.Hkv;
+  const int r = rb * 32 + (lane & 31);
+  const bool valid = r < p.R;                    // padding rows of the last row block
   int ctx = p.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
   const int ns = (ctx + p.K + p.chunk - 1) / p.chunk;
-  const size_t base = (static_cast<size_t>(b) * p.Hkv + g) * p.nsplit * p.R + r;
-  const S* po = static_cast<const S*>(p.part_o);
-  const int grp = tid / TPS;                     // split slot within a pass
-  const int e0 = (tid % TPS) * 32;               // first element of this thread's slice
+  const int RBT = (p.R + 31) >> 5;
+  const S* const po = static_cast<const S*>(p.part_o) +
+                      ((((static_cast<size_t>(bg) * RBT + rb) * DB + db) * 4 + q) * p.nsplit) * 256 + lane * 4;
+  const float2* const pml = p.part_ml + static_cast<size_t>(bg) * p.nsplit * p.R + min(r, p.R - 1);
 
-  // the first pass's partial slice goes in flight before the maximum is known
-  float o[32];
-  float ms = kNegBig, ls = 0.0f;
-  if (grp < ns) {
-    const size_t id = base + static_cast<size_t>(grp) * p.R;
-    load32<Tag>(po + id * D + e0, o);
-    const float2 ml = p.part_ml[id];
-    ms = ml.x;
-    ls = ml.y;
-  } else {
+  float m_w = kNegBig, l_w = 0.0f;
+  f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // Loads cover every allocated split and are issued together with the context-length
+  // read (no dependent round trip).  They are unconditional, at clamped in-bounds
+  // indices -- a load under a branch would be waited for before the next one -- and
+  // splits past this sequence's end (stale workspace: may hold anything) are replaced
+  // by empty ones afterwards.
+  for (int s0 = wave; s0 < p.nsplit; s0 += kMergeWaves * kMergeBatch) {
+    float2 ml[kMergeBatch];
+    f32x4 o[kMergeBatch];
 #pragma unroll
-    for (int e = 0; e < 32; ++e) o[e] = 0.0f;
-  }
-  float m = ms;
-  for (int s = grp + SPP; s < ns; s += SPP) m = fmaxf(m, p.part_ml[base + static_cast<size_t>(s) * p.R].x);
-  m = wave_max(m);
-  if ((tid & 63) == 0) red[tid >> 6] = m;
-  __syncthreads();
-  m = red[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / kWave; ++w) m = fmaxf(m, red[w]);
-
-  const float w0 = grp < ns ? ls * fast_exp2(ms - m) : 0.0f;
-  float lsum = w0;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) o[e] *= w0;
-  for (int s = grp + SPP; s < ns; s += SPP) {    // more splits than one pass holds
-    const size_t id = base + static_cast<size_t>(s) * p.R;
-    const float2 ml = p.part_ml[id];
-    const float w = ml.y * fast_exp2(ml.x - m);
-    lsum += w;
-    float x[32];
-    load32<Tag>(po + id * D + e0, x);
-#pragma unroll
-    for (int e = 0; e < 32; ++e) o[e] += w * x[e];
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    *reinterpret_cast<f32x4*>(&acc_lds[grp][e0 + 4 * q]) = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-  if (tid % TPS == 0) l_lds[grp] = lsum;
-  __syncthreads();
-
-  const int nsp = ns < SPP ? ns : SPP;
-  if (tid < D) {
-    float a = 0.0f, l = 0.0f;
-    for (int q = 0; q < nsp; ++q) {
-      a += acc_lds[q][tid];
-      l += l_lds[q];
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const size_t sp = static_cast<size_t>(min(s0 + u * kMergeWaves, p.nsplit - 1));
+      ml[u] = pml[sp * p.R];
+      o[u] = load4<Tag>(po + sp * 256);
     }
-    S* out = static_cast<S*>(p.out) + ((static_cast<size_t>(b) * p.K + i) * p.Hq + hq) * D;
-    out[tid] = Tag::from_f32(a / l);
-    if (p.lse && tid == 0)
-      p.lse[(static_cast<size_t>(b) * p.K + i) * p.Hq + hq] = (m + log2f(l)) * 0.69314718055994531f;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      if (!valid || s0 + u * kMergeWaves >= ns) {
+        ml[u] = make_float2(kNegBig, 0.0f);
+        o[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    float bm = m_w;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) bm = fmaxf(bm, ml[u].x);
+    const float a = fast_exp2(m_w - bm);
+    m_w = bm;
+    l_w *= a;
+    acc *= a;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float w = ml[u].y * fast_exp2(ml[u].x - bm);   // 0 for absent / empty splits
+      l_w += w;
+      acc += w * o[u];
+    }
   }
+  st[0][wave][lane] = acc;
+  st[1][wave][lane] = f32x4{m_w, l_w, 0.0f, 0.0f};
+  __syncthreads();
+  if (wave != 0 || !valid) return;
+
+  float M = kNegBig;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) M = fmaxf(M, st[1][w][lane][0]);
+  float L = 0.0f;
+  f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) {
+    const f32x4 ml = st[1][w][lane];
+    const float a = ml[1] > 0.0f ? fast_exp2(ml[0] - M) : 0.0f;
+    L += ml[1] * a;
+    o += a * st[0][w][lane];
+  }
+  const float inv = 1.0f / L;
+  const int i = r / p.G;
+  const int hq = g * p.G + (r - i * p.G);
+  S* out = static_cast<S*>(p.out) + ((static_cast<size_t>(b) * p.K + i) * p.Hq + hq) * D +
+           db * 32 + 8 * q + 4 * h;
+  if constexpr (Tag::kBytes == 2) {
+    *reinterpret_cast<uint2*>(out) = uint2{Tag::pack2(o[0] * inv, o[1] * inv), Tag::pack2(o[2] * inv, o[3] * inv)};
+  } else {
+    *reinterpret_cast<f32x4*>(out) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+  }
+  if (p.lse && blockIdx.x == 0 && h == 0)
+    p.lse[(static_cast<size_t>(b) * p.K + i) * p.Hq + hq] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
 template <class Tag, int D>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const dim3 grid(p.nsplit, p.Hkv, p.B);
-  if ((p.R + 31) / 32 <= 4)
-    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 1, 2>), grid, dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 2, 1>), grid, dim3(256), 0, stream, p);
+  // up to 4 row blocks: 4 row-group waves x 2 key halves, one row block each (512
+  // threads, two waves per SIMD); a deep register ring for 16-bit data.  Up to 8 row
+  // blocks: 4 row-group waves with two row blocks each and whole tiles (256 threads).
+  if ((p.R + 31) / 32 <= 4) {
+    if constexpr (Tag::kBytes == 2)
+      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, kRingDeep>), grid, dim3(512), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, 2>), grid, dim3(512), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 2, 1, 2>), grid, dim3(256), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = p.B * p.K * p.Hq;
-  hipLaunchKernelGGL((attn_merge_kernel<Tag, D>), dim3(rows), dim3(kThreads), 0, stream, p);
+  const dim3 mgrid(D / 32 * 4, (p.R + 31) / 32, p.B * p.Hkv);
+  hipLaunchKernelGGL((attn_merge_kernel<Tag, D>), mgrid, dim3(kMergeWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 

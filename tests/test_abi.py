@@ -64,10 +64,10 @@ def _ws(lib, d):
 def test_attention_workspace_query(lib):
     st, n = _ws(lib, _desc())
     assert st == OK
-    # 4 KV heads x splits x 112 rows x (128 fp32 + (m, l))
     assert n > 0
+    # 4 KV heads x 25 splits x (128 padded rows x 128 bf16 partial outputs + 112 rows x (m, l))
     st, n2 = _ws(lib, _desc(split_keys=1024))
-    assert st == OK and n2 == 4 * 25 * 112 * (128 * 2 + 8)
+    assert st == OK and n2 == 4 * 25 * (128 * 128 * 2 + 112 * 8)
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "LIB_PATH", "load", "SvError", "AttnDesc", "verify_attention", "verify_attention_into",
     "attention_workspace_bytes", "accept_greedy", "accept_sample", "latent_compress",
-    "kv_append", "make_desc", "SV_F32", "SV_BF16", "SV_F16",
+    "kv_append", "commit", "make_desc", "SV_F32", "SV_BF16", "SV_F16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
@@ -68,6 +68,7 @@ _SIGNATURES = {
                                    c_vp, c_sz, c_vp]),
     "sv_kv_append": (c_i32, [ctypes.POINTER(AttnDesc), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                              c_vp]),
+    "sv_commit": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
 }
 
 
@@ -293,3 +294,23 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, start: torch.Tensor,
     _check(load().sv_kv_append(ctypes.byref(desc), n, _ptr(k_new), _ptr(v_new), _ptr(start),
                                _ptr(page_table), _ptr(k_cache), _ptr(v_cache), _stream(stream)),
            "sv_kv_append")
+
+
+# ----------------------------------------------------------------------- cycle commit
+def commit(accept_len: torch.Tensor, out_tokens: torch.Tensor, ctx_lens: torch.Tensor,
+           next_anchor: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Close a cycle on the device: ctx_lens += accept_len + 1 (in place) and return the
+    next anchors out_tokens[b][accept_len[b]]."""
+    _require(accept_len, "accept_len", torch.int32)
+    _require(out_tokens, "out_tokens", torch.int32)
+    _require(ctx_lens, "ctx_lens", torch.int32)
+    B, K = out_tokens.shape
+    if accept_len.numel() != B or ctx_lens.numel() != B:
+        raise SvError("commit shape mismatch")
+    if next_anchor is None:
+        next_anchor = torch.empty(B, dtype=torch.int32, device=out_tokens.device)
+    _require(next_anchor, "next_anchor", torch.int32)
+    _check(load().sv_commit(B, K, _ptr(accept_len), _ptr(out_tokens), _ptr(ctx_lens),
+                            _ptr(next_anchor), _stream(stream)),
+           "sv_commit")
+    return next_anchor

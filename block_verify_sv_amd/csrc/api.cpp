@@ -411,4 +411,21 @@ sv_status sv_kv_append(const sv_attn_desc* desc, int32_t n, const void* k_new, c
                        "sv_kv_append launch");
 }
 
+// ---------------------------------------------------------------- cycle commit
+sv_status sv_commit(int32_t B, int32_t K, const int32_t* accept_len, const int32_t* out_tokens,
+                    int32_t* ctx_lens, int32_t* next_anchor, void* stream) {
+  if (B < 1 || B > (1 << 24)) return fail(SV_ERR_INVALID_ARG, "B must be in [1, 2^24] (got %d)", B);
+  if (K < 1 || K > sv::kMaxBlock) return fail(SV_ERR_INVALID_ARG, "K must be in [1, 64] (got %d)", K);
+  if (!accept_len || !out_tokens || !ctx_lens || !next_anchor)
+    return fail(SV_ERR_INVALID_ARG, "accept_len, out_tokens, ctx_lens and next_anchor are required");
+  sv::CommitParams p;
+  p.accept_len = accept_len;
+  p.out_tokens = out_tokens;
+  p.ctx_lens = ctx_lens;
+  p.next_anchor = next_anchor;
+  p.B = B;
+  p.K = K;
+  return device_status(sv::launch_commit(p, static_cast<hipStream_t>(stream)), "sv_commit launch");
+}
+
 }  // extern "C"

@@ -112,4 +112,15 @@ struct AppendParams {
 
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 
+// ---------------------------------------------------------------- cycle commit
+struct CommitParams {
+  const int32_t* accept_len;
+  const int32_t* out_tokens;
+  int32_t* ctx_lens;
+  int32_t* next_anchor;
+  int32_t B, K;
+};
+
+hipError_t launch_commit(const CommitParams& p, hipStream_t stream);
+
 }  // namespace sv

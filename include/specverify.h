@@ -191,6 +191,21 @@ sv_status sv_kv_append(const sv_attn_desc* desc, int32_t n, const void* k_new,
                        const void* v_new, const int32_t* start, const int32_t* page_table,
                        void* k_cache, void* v_cache, void* stream);
 
+/* -------------------------------------------------------------------------------------
+ * Cycle commit (VFlash-FM page, caption of the cycle figure: the accepted drafts and
+ * the target's token at the first disagreement are committed, and that token anchors
+ * the next cycle).  Per sequence b, with a = accept_len[b] (clamped to [0, K-1]):
+ *   next_anchor[b] = out_tokens[b][a];   ctx_lens[b] += a + 1
+ * -- the anchor and the a accepted drafts keep the K/V rows written before the verify
+ * pass; rejected drafts' rows are overwritten by the next block's sv_kv_append, so no
+ * rollback is needed.  accept_len [B], out_tokens [B][K] are the outputs of
+ * sv_accept_greedy / sv_accept_sample; ctx_lens [B] is updated in place; next_anchor
+ * [B] int32 is written.  All device pointers; no workspace.  The caller keeps
+ * ctx_lens[b] + K within max_pages_per_seq * page_size for the next cycle.
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_commit(int32_t B, int32_t K, const int32_t* accept_len, const int32_t* out_tokens,
+                    int32_t* ctx_lens, int32_t* next_anchor, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,9 @@ Every function follows a passage of the pages it cites:
   README, "components", compressor equation).
 * ``kv.kv_append_ref`` -- writing the block's rows into the preallocated paged
   KV cache (VFlash-FM page, demo setup).
+* ``kv.commit_ref`` -- closing a cycle: the context grows by the accepted drafts
+  plus the anchor, and the target's correction becomes the next anchor (VFlash-FM
+  page, caption of the cycle figure).
 
 Parity pins: every function is pinned in ``tests/test_oracle_*.py`` against
 something other than itself (worked example, library routine, closed form,
@@ -34,11 +37,11 @@ from .attention import verify_attention_ref, single_query_ref, merge_partials_re
 from .accept import accept_greedy_ref, sample_rule, accept_sample_ref, race_ref
 from .philox import philox4x64_10, uniforms, ACCEPT, RESAMPLE
 from .compress import latent_compress_ref
-from .kv import kv_append_ref
+from .kv import kv_append_ref, commit_ref
 
 __all__ = [
     "decode", "verify_attention_ref", "single_query_ref", "merge_partials_ref",
     "accept_greedy_ref", "sample_rule", "accept_sample_ref", "race_ref",
     "philox4x64_10", "uniforms", "ACCEPT", "RESAMPLE", "latent_compress_ref",
-    "kv_append_ref",
+    "kv_append_ref", "commit_ref",
 ]

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert lib.sv_version() == 1
@@ -153,6 +153,13 @@ def test_kv_append_validation(lib):
     assert lib.sv_kv_append(ctypes.byref(d), 16, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
     d2 = _desc(head_dim=80)
     assert lib.sv_kv_append(ctypes.byref(d2), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_commit_validation(lib):
+    assert lib.sv_commit(0, 16, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.sv_commit(4, 65, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.sv_commit(4, 16, FAKE, None, FAKE, FAKE, None) == INVALID
+    assert lib.sv_commit(4, 16, FAKE, FAKE, FAKE, None, None) == INVALID
 
 
 def test_status_strings(lib):

@@ -162,3 +162,40 @@ def test_sample_workspace_shape_change(gpu_lib):
         s = W.make_sample(rng, B=B, K=K, V=V, dtype="bf16", seed=5, offset=i)
         say(f"[sample] shape change {i}: B={B} K={K} V={V}")
         assert_sample(gpu_lib, s, f"shape{i}")
+
+
+# ------------------------------------------------------------------------- commit
+@pytest.mark.parametrize("name", ["qwen7b_25k", "batched_paged"])
+def test_commit_after_greedy(gpu_lib, name):
+    """Device-side cycle close on the acceptance kernel's own outputs, chained over
+    several cycles with the context kept on the device: bit-exact against the oracle."""
+    g0 = W.make_workload_greedy(name, 0)
+    ctx_dev = torch.arange(100, 100 + g0.B, dtype=torch.int32, device="cuda")
+    ctx_ref = ctx_dev.cpu().numpy()
+    for cycle in range(3):
+        g = W.make_workload_greedy(name, cycle)
+        say(f"[commit] workload={name} cycle={cycle} B={g.B}")
+        acc, toks, _ = gpu_lib.accept_greedy(to_dev(g.logits, g.dtype), i32(g.drafts))
+        anchor = gpu_lib.commit(acc, toks, ctx_dev)
+        torch.cuda.synchronize()
+        ctx_ref, anchor_ref = oracle.commit_ref(ctx_ref, acc.cpu().numpy(), toks.cpu().numpy())
+        np.testing.assert_array_equal(ctx_dev.cpu().numpy(), ctx_ref)
+        np.testing.assert_array_equal(anchor.cpu().numpy(), anchor_ref)
+
+
+def test_commit_edges(gpu_lib):
+    """accept_len 0 and K-1, K = 1, and a batch spanning several workgroups."""
+    rng = np.random.default_rng(77)
+    for B, K in [(1, 1), (3, 16), (1000, 8)]:
+        acc = rng.integers(0, K, B).astype(np.int32)
+        acc[0] = 0
+        acc[-1] = K - 1
+        toks = rng.integers(0, 152064, (B, K)).astype(np.int32)
+        ctx = rng.integers(0, 30000, B).astype(np.int32)
+        say(f"[commit] edges B={B} K={K}")
+        ctx_dev = i32(ctx)
+        anchor = gpu_lib.commit(i32(acc), i32(toks), ctx_dev)
+        torch.cuda.synchronize()
+        r_ctx, r_anchor = oracle.commit_ref(ctx, acc, toks)
+        np.testing.assert_array_equal(ctx_dev.cpu().numpy(), r_ctx)
+        np.testing.assert_array_equal(anchor.cpu().numpy(), r_anchor)

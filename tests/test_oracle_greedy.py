@@ -38,6 +38,11 @@ def test_worked_example_from_the_pages():
     assert committed == ex["autoregressive_tokens"]
     assert committed[-1] == ex["next_anchor"]
     assert (out[0, acc[0] + 1:] == -1).all()
+    # closing the cycle: anchor + 7 accepted drafts keep their K/V rows, "in" anchors next
+    ctx = 25119
+    new_ctx, anchor = oracle.commit_ref(np.array([ctx], np.int32), acc, out)
+    assert new_ctx[0] == ctx + ex["accepted"] + 1
+    assert vocab[anchor[0]] == ex["next_anchor"]
 
 
 def test_special_cases():
@@ -127,9 +132,11 @@ def _speculative(model, prompt, n, K, drafter, P=4):
         kc[j // P, 0, j % P] = k[j]
         vc[j // P, 0, :, j % P] = v[j]
     cycles = 0
+    ctx, anchor = len(committed) - 1, committed[-1]
     while len(committed) - len(prompt) < n:
-        ctx = len(committed) - 1
-        block = [committed[-1]] + list(drafter(committed, K - 1))
+        # the cycle state comes from commit_ref alone; it must agree with the token list
+        assert ctx == len(committed) - 1 and anchor == committed[-1]
+        block = [anchor] + list(drafter(committed, K - 1))
         x, q, k, v = model.proj(block)
         for t in range(K):                     # write the block's K/V at [ctx, ctx+K)
             j = ctx + t
@@ -142,6 +149,8 @@ def _speculative(model, prompt, n, K, drafter, P=4):
         acc, toks, _ = oracle.accept_greedy_ref(logits[None], np.array([block[1:]], np.int32),
                                                 "f32")
         committed += [int(t) for t in toks[0, :acc[0] + 1]]
+        new_ctx, new_anchor = oracle.commit_ref(np.array([ctx], np.int32), acc, toks)
+        ctx, anchor = int(new_ctx[0]), int(new_anchor[0])
         cycles += 1
     return committed[len(prompt):len(prompt) + n], cycles
 

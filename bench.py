@@ -91,8 +91,10 @@ def cpu_baseline(seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the verify path "
-                                   "is single-GPU (see DESIGN.md for how it would shard)"}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the verify path "
+                                   "is built and measured on one GPU's share (it would shard "
+                                   "by KV head, vocabulary or context); no figure at several "
+                                   "GPUs is produced"}))
         sys.exit(2)
     import torch
     import block_verify_sv_amd as sv

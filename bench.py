@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+COPY_BYTES = 256 << 20           # calibration copy: bytes read and written per launch
 WORKLOAD = "qwen7b_25k"
 
 
@@ -41,6 +42,10 @@ def parse():
                     help="attention-only launches timed for the roofline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--pmc-workload", choices=["attn", "copy"], default=None,
+                    help="run a fixed loop for rocprofv3 --pmc counter passes and exit: "
+                         "'attn' = --steps attention passes (rotating copies), 'copy' = "
+                         "--steps plain copies of a 256 MiB tensor (the calibration kernel)")
     return ap.parse_args()
 
 
@@ -103,6 +108,15 @@ def main():
     lib = sv.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.pmc_workload == "copy":
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_workload": "copy", "bytes_read": COPY_BYTES,
+                          "bytes_written": COPY_BYTES, "launches": args.steps}), flush=True)
+        return
     inp = W.make_workload_verify(WORKLOAD)
     g = W.make_workload_greedy(WORKLOAD)
     to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
@@ -150,6 +164,16 @@ def main():
     def cycle(i):
         attn(i)
         accept(i)
+
+    if args.pmc_workload == "attn":
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                attn(i % R)
+        stream.synchronize()
+        print(json.dumps({"pmc_workload": "attn", "passes": args.steps,
+                          "kv_bytes": inp.kv_bytes(), "source_digest": source_digest()}),
+              flush=True)
+        return
 
     graphs = None
     with torch.cuda.stream(stream):

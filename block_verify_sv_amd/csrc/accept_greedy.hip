@@ -2,13 +2,14 @@
 // draft prefix matching it plus the target's correction (VFlash-FM page, caption of
 // the cycle figure).
 //
-// One launch.  Grid (vocabulary chunk, block row).  Each workgroup scans a chunk of one
-// row with 16-byte loads and reduces a packed 64-bit key (orderable value bits << 32 |
-// ~index) -- so the maximum key is the largest value at the lowest index -- through the
-// wave and LDS into one atomicMax per workgroup.  The last workgroup to arrive for a
-// sequence (arrival counter, bumped only after the atomicMax has returned) decodes the
-// K row maxima, walks the draft prefix, writes the outputs and returns its keys and
-// counter to zero for the next call.
+// Two launches.  The argmax pass has grid (vocabulary chunk, block row): each workgroup
+// scans a chunk of one row with 16-byte loads (all issued before any is consumed) and
+// reduces a packed 64-bit key (orderable value bits << 32 | ~index) -- so the maximum
+// key is the largest value at the lowest index -- through the wave and LDS into one
+// non-returning device-scope atomicMax; nothing waits for it.  The walk pass has one
+// wave per sequence: lane i reads-and-clears row i's key (leaving the workspace zeroed
+// for the next call), and a ballot over the lanes whose draft differs from the
+// target's choice gives the accepted length.  The kernel boundary orders the two.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -25,15 +26,11 @@ __device__ __forceinline__ float load_logit(const void* base, size_t i) {
 }
 
 template <bool kBF16>
-__global__ void __launch_bounds__(kThreads) greedy_kernel(const GreedyParams p) {
+__global__ void __launch_bounds__(kThreads) greedy_argmax_kernel(const GreedyParams p) {
   __shared__ uint64_t red[kThreads / kWave];
-  __shared__ int32_t tok[kMaxBlock];
-  __shared__ int32_t acc_len;
-  __shared__ bool is_last;
 
   const int tid = threadIdx.x;
   const int row = blockIdx.y;                     // b * K + i
-  const int b = row / p.K;
   const int j0 = blockIdx.x * p.chunk;
   const int j1 = min(j0 + p.chunk, p.V);
   const size_t rbase = static_cast<size_t>(row) * p.V;
@@ -41,14 +38,14 @@ __global__ void __launch_bounds__(kThreads) greedy_kernel(const GreedyParams p) 
   uint64_t best = 0;
   constexpr int EPV = kBF16 ? 8 : 4;              // elements per 16-byte load
   if ((p.V % EPV) == 0) {
-    // every load of the chunk is issued before any is consumed
+    // every load of the chunk is issued before any is consumed; indices past the row
+    // end are clamped to its last 16 bytes (in bounds) and ignored below
     u32x4 v[kLoadsPerThread];
 #pragma unroll
     for (int u = 0; u < kLoadsPerThread; ++u) {
-      const int j = j0 + (tid + u * kThreads) * EPV;
-      v[u] = j < j1 ? *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.logits) +
-                                                     (rbase + j) * (kBF16 ? 2 : 4))
-                    : u32x4{0u, 0u, 0u, 0u};
+      const int j = min(j0 + (tid + u * kThreads) * EPV, p.V - EPV);
+      v[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.logits) +
+                                             (rbase + j) * (kBF16 ? 2 : 4));
     }
 #pragma unroll
     for (int u = 0; u < kLoadsPerThread; ++u) {
@@ -76,50 +73,41 @@ __global__ void __launch_bounds__(kThreads) greedy_kernel(const GreedyParams p) 
     uint64_t m = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / kWave; ++w) m = red[w] > m ? red[w] : m;
-    // The keys only ever move through device-scope atomics, so no fence is needed: the
-    // returning atomicMax has been performed at the coherence point before the arrival
-    // counter is bumped, and the last arrival reads the keys atomically.
-    const unsigned long long before = __hip_atomic_fetch_max(
-        &p.keys[row], static_cast<unsigned long long>(m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned prev = __hip_atomic_fetch_add(&p.counters[b], before == ~0ull ? 0u : 1u,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = prev == static_cast<unsigned>(p.nchunk * p.K - 1);
+    __hip_atomic_fetch_max(&p.keys[row], static_cast<unsigned long long>(m), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  if (!is_last) return;
+}
 
-  // ---- last workgroup of sequence b: decode maxima, walk the draft prefix
+constexpr int kWalkSeqs = kThreads / kWave;       // sequences per walk workgroup
+
+__global__ void __launch_bounds__(kThreads) greedy_walk_kernel(const GreedyParams p) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * kWalkSeqs + (threadIdx.x >> 6);
+  if (b >= p.B) return;                           // whole waves
   const int K = p.K;
-  if (tid < K) {
-    // read-and-clear in one RMW: it returns the latest value in the key's modification
-    // order and leaves the key zeroed for the next call
-    unsigned long long* kp = &p.keys[static_cast<size_t>(b) * K + tid];
-    const uint64_t key = __hip_atomic_exchange(kp, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int32_t t = static_cast<int32_t>(argmax_key_index(key));
-    tok[tid] = t;
-    if (p.argmax) p.argmax[static_cast<size_t>(b) * K + tid] = t;
+  const bool in = lane < K;
+  int32_t t = -1;
+  if (in) {
+    // read-and-clear: the latest value in the key's modification order, and a zeroed
+    // key for the next call
+    const uint64_t key = __hip_atomic_exchange(&p.keys[static_cast<size_t>(b) * K + lane], 0ull,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t = static_cast<int32_t>(argmax_key_index(key));
+    if (p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
   }
-  __syncthreads();
-  const int32_t* dr = p.drafts + static_cast<size_t>(b) * (K - 1);
-  if (tid == 0) {
-    int a = 0;
-    while (a < K - 1 && dr[a] == tok[a]) ++a;
-    acc_len = a;
-    p.accept_len[b] = a;
-    __hip_atomic_store(&p.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (tid < K) {
-    const int a = acc_len;
-    p.out_tokens[static_cast<size_t>(b) * K + tid] = tid < a ? dr[tid] : (tid == a ? tok[a] : -1);
-  }
+  // draft k+1 (drafts[b][k]) is checked against row k's choice, k = 0 .. K-2
+  const int32_t d = lane < K - 1 ? p.drafts[static_cast<size_t>(b) * (K - 1) + lane] : 0;
+  const uint64_t miss = __ballot(lane < K - 1 && d != t);
+  const int a = miss ? __builtin_ctzll(miss) : K - 1;   // accepted drafts
+  const int32_t corr = __shfl(t, a);
+  if (in) p.out_tokens[static_cast<size_t>(b) * K + lane] = lane < a ? d : (lane == a ? corr : -1);
+  if (lane == 0) p.accept_len[b] = a;
 }
 
 }  // namespace
 
 size_t greedy_workspace_bytes(int B, int K) {
-  const size_t keys = static_cast<size_t>(B) * K * sizeof(unsigned long long);
-  return keys + static_cast<size_t>(B) * sizeof(unsigned int);
+  return static_cast<size_t>(B) * K * sizeof(unsigned long long);
 }
 
 int greedy_chunk(int V, sv_dtype dtype) {
@@ -131,9 +119,13 @@ int greedy_chunk(int V, sv_dtype dtype) {
 hipError_t launch_greedy(const GreedyParams& p, sv_dtype dtype, hipStream_t stream) {
   const dim3 grid(p.nchunk, p.B * p.K);
   if (dtype == SV_BF16)
-    hipLaunchKernelGGL(greedy_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(greedy_argmax_kernel<true>, grid, dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(greedy_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(greedy_argmax_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(greedy_walk_kernel, dim3((p.B + kWalkSeqs - 1) / kWalkSeqs), dim3(kThreads),
+                     0, stream, p);
   return hipGetLastError();
 }
 

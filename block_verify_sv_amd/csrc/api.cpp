@@ -252,8 +252,6 @@ sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
   p.out_tokens = out_tokens;
   p.argmax = argmax;
   p.keys = static_cast<unsigned long long*>(workspace);
-  p.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) +
-                                               static_cast<size_t>(B) * K * sizeof(unsigned long long));
   p.B = B;
   p.K = K;
   p.V = V;

@@ -54,7 +54,6 @@ struct GreedyParams {
   int32_t* out_tokens;
   int32_t* argmax;
   unsigned long long* keys;   // [B][K] packed argmax keys (zero between calls)
-  unsigned int* counters;     // [B] arrival counters (zero between calls)
   int32_t B, K, V;
   int32_t chunk;              // vocabulary entries per workgroup
   int32_t nchunk;

@@ -15,6 +15,7 @@
  *                        by counter-based Philox4x64-10 uniforms
  *   sv_latent_compress   softmax(C . F^T) . F latent visual compressor
  *   sv_kv_append         write new K/V rows into the paged cache
+ *   sv_commit            close a cycle: grow the context, pick the next anchor
  *
  * Conventions for every call
  *   - Array arguments are DEVICE pointers unless stated otherwise.  The caller
@@ -27,7 +28,7 @@
  *     message for the last failure on the calling thread is in sv_last_error().
  *   - Inputs must be finite.  Results are bitwise reproducible for identical
  *     inputs, shapes and workspace contents.
- *   - The workspace of sv_accept_greedy holds counters: it must be zero-filled
+ *   - The workspace of sv_accept_greedy holds argmax keys: it must be zero-filled
  *     once before its first use, and every call leaves it zeroed again (so one
  *     buffer serves calls of any shape).  Two calls that share one workspace
  *     must not overlap in time.

@@ -42,6 +42,9 @@ def parse():
                     help="attention-only launches timed for the roofline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--row", choices=["cycle"] + sorted(ROWS), default="cycle",
+                    help="'cycle' (default) is the verify-cycle line; the others time one "
+                         "further entry point on its own workload and print its own line")
     ap.add_argument("--pmc-workload", choices=["attn", "copy"], default=None,
                     help="run a fixed loop for rocprofv3 --pmc counter passes and exit: "
                          "'attn' = --steps attention passes (rotating copies), 'copy' = "
@@ -93,8 +96,147 @@ def cpu_baseline(seconds):
                       f"heads x 16 rows + greedy accept over 16 x 152,064), {el:.1f} s"}
 
 
+# ------------------------------------------------------------------ further rows
+# name -> (workload, description, rotated copies)
+ROWS = {
+    "attn_batched": ("batched_paged", "verify attention, 8 sequences, log-uniform 4k-32k "
+                     "contexts, shuffled 16-token pages", 3),
+    "attn_72b": ("qwen72b_sampling", "verify attention, 72B geometry (64q/8kv, d 128), "
+                 "ctx 25,000 + block 32", 6),
+    "sample_72b": ("qwen72b_sampling", "sampling acceptance, block 32 over 152,064 "
+                   "(target + draft logits)", 28),
+    "compress": ("compressor_sar", "latent compressor, 32 images, D 4096, (C, N) = (64, 576)", 4),
+    "compress_qwen": ("compressor_sar", "latent compressor, 32 images, D 4096, (C, N) = "
+                      "(36, 324)", 4),
+}
+
+
+def graph_rounds(torch, stream, call, R, steps):
+    """HIP graphs that replay exactly `steps` calls: one graph holding a call on each of
+    the R rotated copies in turn (replayed steps // R times), plus one holding the first
+    steps % R calls.  Returns [(graph, replays)]."""
+    out = []
+    for n, reps in ((R, steps // R), (steps % R, 1)):
+        if n == 0 or reps == 0:
+            continue
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=stream):
+            for i in range(n):
+                call(i, stream)
+        out.append((gr, reps))
+    return out
+
+
+def run_row(args):
+    """Time one further entry point on its workload: HIP graphs over rotated input copies
+    on a side stream, HIP events around exactly --steps replays."""
+    import torch
+    import block_verify_sv_amd as sv
+    import workloads as W
+    sv.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl, desc_txt, R = ROWS[args.row]
+
+    def dev_t(a, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        if dtype == "f16":
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float16)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    flops = None
+    if args.row.startswith("attn"):
+        inp = W.make_workload_verify(wl)
+        q = dev_t(inp.q, inp.dtype)
+        ks = [dev_t(inp.k_cache, inp.dtype)]
+        vs = [dev_t(inp.v_cache, inp.dtype)]
+        ks += [ks[0].clone() for _ in range(R - 1)]
+        vs += [vs[0].clone() for _ in range(R - 1)]
+        pt, cl = i32(inp.page_table), i32(inp.ctx_lens)
+        desc = sv.make_desc(q, ks[0], pt, int(inp.ctx_lens.max()), 0.0, 0, int(inp.ctx_lens.sum()))
+        ws = torch.empty(sv.attention_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        nbytes = inp.kv_bytes()
+        keys = int(inp.ctx_lens.sum()) + inp.B * inp.K
+        flops = 4.0 * keys * inp.K * inp.Hq * inp.D    # QK^T and PV over every visible key
+        shape = {"B": inp.B, "K": inp.K, "Hq": inp.Hq, "Hkv": inp.Hkv, "d": inp.D,
+                 "ctx_sum": int(inp.ctx_lens.sum())}
+
+        def call(i, st):
+            sv.verify_attention_into(desc, q, ks[i], vs[i], pt, cl, out, lse, None, ws, st)
+    elif args.row == "sample_72b":
+        smp = W.make_workload_sample(wl, 0)
+        tl = [dev_t(smp.target_logits, smp.dtype)]
+        dl = [dev_t(smp.draft_logits, smp.dtype)]
+        tl += [tl[0].clone() for _ in range(R - 1)]
+        dl += [dl[0].clone() for _ in range(R - 1)]
+        dr = i32(smp.drafts)
+        acc = torch.empty(smp.B, dtype=torch.int32, device=dev)
+        toks = torch.empty(smp.B, smp.K, dtype=torch.int32, device=dev)
+        sv.accept_sample(tl[0], dl[0], dr, smp.temperature, smp.seed, 0, out=(acc, toks))
+        nbytes = (tl[0].numel() + dl[0].numel()) * tl[0].element_size()
+        shape = {"B": smp.B, "K": smp.K, "V": smp.V, "T": smp.temperature}
+
+        def call(i, st):
+            sv.accept_sample(tl[i], dl[i], dr, smp.temperature, smp.seed, i, out=(acc, toks),
+                             stream=st)
+    else:
+        p = W.WORKLOADS[wl].params
+        C, N = p["shapes"][0] if args.row == "compress" else p["shapes"][1]
+        ci = W.make_compress(W.rng_for(wl, 0), B=p["B"], C=C, N=N, D=p["D"])
+        qd = dev_t(ci.queries, "f16")
+        fs = [dev_t(ci.feats, "f16")]
+        fs += [fs[0].clone() for _ in range(R - 1)]
+        out = torch.empty(ci.B, C, ci.D, dtype=torch.float16, device=dev)
+        sv.latent_compress(qd, fs[0], 1.0, out=out)
+        nbytes = (fs[0].numel() + qd.numel() + out.numel()) * 2
+        flops = 4.0 * ci.B * C * N * ci.D
+        shape = {"B": ci.B, "C": C, "N": N, "D": ci.D}
+
+        def call(i, st):
+            sv.latent_compress(qd, fs[i], 1.0, out=out, stream=st)
+
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        for i in range(R):
+            call(i, stream)
+        stream.synchronize()
+        rounds = graph_rounds(torch, stream, call, R, args.steps)
+        for _ in range(max(1, args.warmup // R)):
+            rounds[0][0].replay()
+        stream.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for gr, reps in rounds:
+            for _ in range(reps):
+                gr.replay()
+        e1.record(stream)
+        e1.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / args.steps
+    gbps = nbytes / (us * 1e-6) / 1e9
+    line = {"row": args.row, "workload": wl, "what": desc_txt, "config": shape,
+            "us_per_call": us, "calls_per_s": 1e6 / us, "algorithmic_bytes": int(nbytes),
+            "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS, "steps": args.steps,
+            "warmup": args.warmup, "rotated_copies": R}
+    if flops is not None:
+        line["TFLOPs"] = flops / (us * 1e-6) / 1e12
+        line["flops_per_call"] = flops
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
+    if args.row != "cycle":
+        if args.gpus != 1:
+            print(json.dumps({"error": "one GPU only"}))
+            sys.exit(2)
+        run_row(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the verify path "
                                    "is built and measured on one GPU's share (it would shard "
@@ -175,35 +317,34 @@ def main():
               flush=True)
         return
 
-    graphs = None
     with torch.cuda.stream(stream):
         for i in range(R):                      # first touch of every copy
             cycle(i)
         stream.synchronize()
         if args.launch == "graph":
-            graphs = []
-            for i in range(R):
-                gr = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gr, stream=stream):
-                    cycle(i)
-                graphs.append(gr)
+            # graphs of R cycles (one per rotated copy) replayed back to back, plus a
+            # remainder graph, so exactly --steps cycles run in the timed region
+            rounds = graph_rounds(torch, stream, lambda i, st: cycle(i), R, args.steps)
+            warm = graph_rounds(torch, stream, lambda i, st: cycle(i), R, args.warmup)
             stream.synchronize()
 
-        def step(i):
-            if graphs is not None:
-                graphs[i % R].replay()
-            else:
-                cycle(i % R)
+            def run_all(rs):
+                for gr, reps in rs:
+                    for _ in range(reps):
+                        gr.replay()
+        else:
+            def run_all(n):
+                for i in range(n):
+                    cycle(i % R)
+            rounds, warm = args.steps, args.warmup
 
-        for i in range(args.warmup):
-            step(i)
+        run_all(warm)
         stream.synchronize()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(args.steps):
-            step(i)
+        run_all(rounds)
         e1.record(stream)
         e1.synchronize()
         torch.cuda.synchronize()

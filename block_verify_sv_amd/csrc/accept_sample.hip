@@ -1,21 +1,24 @@
 // Sampling acceptance: the standard speculative acceptance-rejection rule (SpecFLASH
 // README, "components"), driven by counter-based Philox4x64-10 uniforms.
 //
-// Launch 1 (row_lse_kernel), grid (vocabulary chunk, row) over the B*K target rows and
-// the B*(K-1) draft rows: per chunk the maximum m_c of the raw logits and
-// s_c = sum exp((x - m_c) / T), fp32 exponentials accumulated in fp64.
+// Launch 1 (row_lse_kernel), grid (8192-entry vocabulary chunk, row) over the B*K
+// target rows and the B*(K-1) draft rows: per chunk the maximum m_c of the raw logits
+// and s_c = sum exp((x - m_c) / T), fp32 exponentials accumulated in fp64.
 //
-// Launch 2 (sample_race_kernel), grid (vocabulary chunk, sequence): every workgroup
-// combines the chunk partials into the row log-normalisers L = m/T + log sum_c s_c
-// e^((m_c - m)/T) (fp64, fixed order), replays the K-1 ratio tests
+// Launch 2 (sample_race_kernel), grid (1024-entry vocabulary chunk, sequence).  Every
+// workgroup combines the chunk partials into the row log-normalisers
+//     L = m/T + log sum_c s_c e^((m_c - m)/T)            (fp64, fixed order),
+// replays the K-1 ratio tests (one lane per draft, the first failure by ballot)
 //     lambda_k = (lp[k-1][d_k] - lq[k-1][d_k]) / T - (Lp_{k-1} - Lq_k),
-//     accept d_k iff u_k < exp(min(0, lambda_k))            (fp64)
-// to find the first rejection, then runs its chunk of the exponential race
+//     accept d_k iff u_k < exp(min(0, lambda_k))         (fp64),
+// then runs its chunk of the exponential race
 //     key_j = -ln(1 - u_j) / r_j,  r = max(0, p_{k-1} - q_k) (or p_{K-1} for the bonus)
-// in fp64, keeping the smallest key (lowest index on ties).  The last workgroup of a
-// sequence reduces the chunk winners in chunk order and writes the outputs.  A race
-// over p itself is carried along for the (measure-zero) case r == 0 everywhere.  The
-// arrival counters are cleared by launch 1, so the workspace carries no state.
+// in fp64, one Philox block (4 tokens) per thread, keeping the smallest key (lowest
+// index on ties); a race over p itself is carried along for the (measure-zero) case
+// r == 0 everywhere.  Launch 3 (sample_finish_kernel), one workgroup per sequence,
+// reduces the chunk winners and writes the outputs.  The kernel boundaries order the
+// three launches, so no fences or arrival counters are needed and the workspace
+// carries no state between calls.
 #include <math.h>
 
 #include "common.hpp"
@@ -24,8 +27,10 @@
 namespace sv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;                     // race: 4 tokens per thread
 constexpr int kLseThreads = 256;
+constexpr int kLseChunk = 8192;                   // vocabulary entries per row_lse workgroup
+constexpr int kRaceChunk = 4 * kThreads;          // vocabulary entries per race workgroup
 
 // ---- Philox4x64-10 (Salmon et al., SC'11): multipliers and Weyl key increments of
 // the 4x64 variant; ten rounds.
@@ -83,22 +88,45 @@ __global__ void __launch_bounds__(kLseThreads) row_lse_kernel(const SampleParams
   const int tid = threadIdx.x;
   const int c = blockIdx.x;
   const int rho = blockIdx.y;
-  // The race launch runs after this one on the same stream: clear its arrival counters
-  // here, so the workspace needs no initial state whatever the previous call's shape.
-  if (c == 0 && rho == 0)
-    for (int i = tid; i < p.B; i += kLseThreads) p.counters[i] = 0u;
   const void* x = row_ptr<kBF16>(p, rho);
   const int j0 = c * p.chunk;
   const int j1 = min(j0 + p.chunk, p.V);
-  constexpr int kMaxPer = 32;                      // chunk <= 8192 elements
+  constexpr int EPL = kBF16 ? 8 : 4;               // elements per 16-byte load
+  constexpr int kLoads = kLseChunk / (kLseThreads * EPL);
+  constexpr int kMaxPer = kLoads * EPL;
   float v[kMaxPer];
+  if ((p.V % EPL) == 0) {
+    // every load issued before any is consumed; clamped (in-bounds) indices past the
+    // row end are masked afterwards
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int j = min(j0 + (tid + u * kLseThreads) * EPL, p.V - EPL);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const char*>(x) +
+                                                       static_cast<size_t>(j) * (kBF16 ? 2 : 4));
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        if constexpr (kBF16) v[u * EPL + e] = bf16_to_f32(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))));
+        else v[u * EPL + e] = __uint_as_float(w[e]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        if (j0 + (tid + u * kLseThreads) * EPL + e >= j1) v[u * EPL + e] = -INFINITY;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kMaxPer; ++e) {
+      const int j = j0 + tid + e * kLseThreads;
+      v[e] = logit_at<kBF16>(x, min(j, p.V - 1));
+    }
+#pragma unroll
+    for (int e = 0; e < kMaxPer; ++e)
+      if (j0 + tid + e * kLseThreads >= j1) v[e] = -INFINITY;
+  }
   float m = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < kMaxPer; ++e) {
-    const int j = j0 + tid + e * kLseThreads;
-    v[e] = j < j1 ? logit_at<kBF16>(x, j) : -INFINITY;
-    m = fmaxf(m, v[e]);
-  }
+  for (int e = 0; e < kMaxPer; ++e) m = fmaxf(m, v[e]);
   m = wave_max(m);
   if ((tid & 63) == 0) redf[tid >> 6] = m;
   __syncthreads();
@@ -121,103 +149,15 @@ __global__ void __launch_bounds__(kLseThreads) row_lse_kernel(const SampleParams
   }
 }
 
-struct Cand {
-  double key;
-  int32_t idx;
-};
 __device__ __forceinline__ bool better(double k, int32_t i, double bk, int32_t bi) {
   return k < bk || (k == bk && i < bi);
 }
 
-template <bool kBF16>
-__global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParams p) {
-  __shared__ double Lrow[2 * kMaxBlock];
-  __shared__ int32_t a_sh;
-  __shared__ double rk[2][kThreads / kWave];
-  __shared__ int32_t ri[2][kThreads / kWave];
-  __shared__ bool is_last;
-
+// Smallest (key, index) of a workgroup, for the residual race and the p race.
+__device__ __forceinline__ void block_best(double& bk_r, int32_t& bi_r, double& bk_p,
+                                           int32_t& bi_p, double (*rk)[kThreads / kWave],
+                                           int32_t (*ri)[kThreads / kWave]) {
   const int tid = threadIdx.x;
-  const int c = blockIdx.x;
-  const int b = blockIdx.y;
-  const int K = p.K;
-  const double it = p.inv_t;
-
-  // ---- row log-normalisers of this sequence: K target rows, then K-1 draft rows
-  if (tid < 2 * K - 1) {
-    const int rho = tid < K ? b * K + tid : p.B * K + b * (K - 1) + (tid - K);
-    const float* pm = p.part_m + static_cast<size_t>(rho) * p.nchunk;
-    const double* ps = p.part_s + static_cast<size_t>(rho) * p.nchunk;
-    float m = -INFINITY;
-    for (int q = 0; q < p.nchunk; ++q) m = fmaxf(m, pm[q]);
-    double s = 0.0;
-    for (int q = 0; q < p.nchunk; ++q)
-      s += ps[q] * exp((static_cast<double>(pm[q]) - static_cast<double>(m)) * it);
-    Lrow[tid] = static_cast<double>(m) * it + log(s);
-  }
-  __syncthreads();
-
-  // ---- ratio tests in draft order; a = drafts accepted
-  const int32_t* dr = p.drafts + static_cast<size_t>(b) * (K - 1);
-  if (tid == 0) {
-    int a = K - 1;
-    for (int k = 1; k < K; ++k) {
-      const int d = dr[k - 1];
-      if (d < 0 || d >= p.V) {                    // a token outside the vocabulary is rejected
-        a = k - 1;
-        break;
-      }
-      const double lp = logit_at<kBF16>(p.target, (static_cast<size_t>(b) * K + k - 1) * p.V + d);
-      const double lq = logit_at<kBF16>(p.draft, (static_cast<size_t>(b) * (K - 1) + k - 1) * p.V + d);
-      const double lam = (lp - lq) * it - (Lrow[k - 1] - Lrow[K + k - 1]);
-      const U64x4 w = philox(p.offset, static_cast<uint64_t>(b), static_cast<uint64_t>(k), 0,
-                             p.seed, 0);
-      const double u = to_uniform(w.x[0]);
-      if (!(u < exp(fmin(0.0, lam)))) {
-        a = k - 1;
-        break;
-      }
-    }
-    a_sh = a;
-  }
-  __syncthreads();
-  const int a = a_sh;
-  const bool resid = a < K - 1;
-  const double Lp = Lrow[a];
-  const double Lq = resid ? Lrow[K + a] : 0.0;
-  const size_t prow = (static_cast<size_t>(b) * K + a) * p.V;
-  const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (resid ? a : 0)) * p.V;
-
-  // ---- exponential race over this chunk (4 consecutive tokens per Philox block)
-  const int j0 = c * p.chunk;
-  const int j1 = min(j0 + p.chunk, p.V);
-  double bk_r = INFINITY, bk_p = INFINITY;
-  int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
-  const uint64_t c2 = (1ull << 32) | static_cast<uint64_t>(a);
-  for (int jb = j0 + 4 * tid; jb < j1; jb += 4 * kThreads) {
-    const U64x4 w = philox(p.offset, static_cast<uint64_t>(b), c2, static_cast<uint64_t>(jb >> 2),
-                           p.seed, 0);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = jb + e;
-      if (j >= j1) break;
-      const double pj = exp(static_cast<double>(logit_at<kBF16>(p.target, prow + j)) * it - Lp);
-      double rj = pj;
-      if (resid) {
-        const double qj = exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow + j)) * it - Lq);
-        rj = fmax(0.0, pj - qj);
-      }
-      const double ej = -log1p(-to_uniform(w.x[e]));
-      if (rj > 0.0) {
-        const double k = ej / rj;
-        if (better(k, j, bk_r, bi_r)) { bk_r = k; bi_r = j; }
-      }
-      if (pj > 0.0) {
-        const double k = ej / pj;
-        if (better(k, j, bk_p, bi_p)) { bk_p = k; bi_p = j; }
-      }
-    }
-  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const double kr = __shfl_xor(bk_r, o);
@@ -234,68 +174,179 @@ __global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParam
     ri[1][tid >> 6] = bi_p;
   }
   __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < kThreads / kWave; ++w) {
-      if (better(rk[0][w], ri[0][w], bk_r, bi_r)) { bk_r = rk[0][w]; bi_r = ri[0][w]; }
-      if (better(rk[1][w], ri[1][w], bk_p, bi_p)) { bk_p = rk[1][w]; bi_p = ri[1][w]; }
+  bk_r = rk[0][0]; bi_r = ri[0][0]; bk_p = rk[1][0]; bi_p = ri[1][0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) {
+    if (better(rk[0][w], ri[0][w], bk_r, bi_r)) { bk_r = rk[0][w]; bi_r = ri[0][w]; }
+    if (better(rk[1][w], ri[1][w], bk_p, bi_p)) { bk_p = rk[1][w]; bi_p = ri[1][w]; }
+  }
+}
+
+template <bool kBF16>
+__global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParams p) {
+  __shared__ double Lrow[2 * kMaxBlock];
+  __shared__ int32_t a_sh;
+  __shared__ double rk[2][kThreads / kWave];
+  __shared__ int32_t ri[2][kThreads / kWave];
+
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x;
+  const int b = blockIdx.y;
+  const int K = p.K;
+  const double it = p.inv_t;
+  const int32_t* dr = p.drafts + static_cast<size_t>(b) * (K - 1);
+
+  // ---- loads that need nothing computed here, issued together: the drafted tokens'
+  // logits for the ratio tests (lane k-1 of wave 0 tests draft k) ...
+  const bool tester = tid < K - 1;
+  int32_t d = tester ? dr[tid] : 0;
+  const bool in_vocab = d >= 0 && d < p.V;
+  const int dc = in_vocab ? d : 0;
+  const double lp = tester ? static_cast<double>(logit_at<kBF16>(
+      p.target, (static_cast<size_t>(b) * K + tid) * p.V + dc)) : 0.0;
+  const double lq = tester ? static_cast<double>(logit_at<kBF16>(
+      p.draft, (static_cast<size_t>(b) * (K - 1) + tid) * p.V + dc)) : 0.0;
+  // ... and the log-normaliser of row tid (K target rows, then K-1 draft rows)
+  if (tid < 2 * K - 1) {
+    const int rho = tid < K ? b * K + tid : p.B * K + b * (K - 1) + (tid - K);
+    const float* pm = p.part_m + static_cast<size_t>(rho) * p.nchunk;
+    const double* ps = p.part_s + static_cast<size_t>(rho) * p.nchunk;
+    float m = -INFINITY;
+    for (int q = 0; q < p.nchunk; ++q) m = fmaxf(m, pm[q]);
+    double s = 0.0;
+    for (int q = 0; q < p.nchunk; ++q)
+      s += ps[q] * exp((static_cast<double>(pm[q]) - static_cast<double>(m)) * it);
+    Lrow[tid] = static_cast<double>(m) * it + log(s);
+  }
+  __syncthreads();
+
+  // ---- ratio tests, one lane per draft; a = drafts accepted = the first failure
+  if (tid < 64) {
+    bool fail = false;
+    if (tester) {
+      if (!in_vocab) {
+        fail = true;                              // a token outside the vocabulary is rejected
+      } else {
+        const int k = tid + 1;
+        const double lam = (lp - lq) * it - (Lrow[k - 1] - Lrow[K + k - 1]);
+        const U64x4 w = philox(p.offset, static_cast<uint64_t>(b), static_cast<uint64_t>(k), 0,
+                               p.seed, 0);
+        fail = !(to_uniform(w.x[0]) < exp(fmin(0.0, lam)));
+      }
     }
-    const size_t slot = (static_cast<size_t>(b) * p.nchunk + c) * 2;
+    const uint64_t fails = __ballot(fail);
+    if (tid == 0) {
+      const int a = fails ? __builtin_ctzll(fails) : K - 1;
+      a_sh = a;
+      if (c == 0) p.decision[b] = a;
+    }
+  }
+  __syncthreads();
+  const int a = a_sh;
+  const bool resid = a < K - 1;
+  const double Lp = Lrow[a];
+  const double Lq = resid ? Lrow[K + a] : 0.0;
+  const size_t prow = (static_cast<size_t>(b) * K + a) * p.V;
+  const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (resid ? a : 0)) * p.V;
+
+  // ---- exponential race over this chunk: one Philox block of 4 tokens per thread
+  const int jb = c * p.race_chunk + 4 * tid;
+  double bk_r = INFINITY, bk_p = INFINITY;
+  int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
+  if (jb < p.V) {
+    float xp[4], xq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {                 // clamped, in bounds; masked below
+      const int j = min(jb + e, p.V - 1);
+      xp[e] = logit_at<kBF16>(p.target, prow + j);
+      xq[e] = logit_at<kBF16>(p.draft, qrow + j);
+    }
+    const uint64_t c2 = (1ull << 32) | static_cast<uint64_t>(a);
+    const U64x4 w = philox(p.offset, static_cast<uint64_t>(b), c2, static_cast<uint64_t>(jb >> 2),
+                           p.seed, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = jb + e;
+      if (j >= p.V) break;
+      const double pj = exp(static_cast<double>(xp[e]) * it - Lp);
+      double rj = pj;
+      if (resid) rj = fmax(0.0, pj - exp(static_cast<double>(xq[e]) * it - Lq));
+      const double ej = -log1p(-to_uniform(w.x[e]));
+      if (rj > 0.0) {
+        const double k = ej / rj;
+        if (better(k, j, bk_r, bi_r)) { bk_r = k; bi_r = j; }
+      }
+      if (pj > 0.0) {
+        const double k = ej / pj;
+        if (better(k, j, bk_p, bi_p)) { bk_p = k; bi_p = j; }
+      }
+    }
+  }
+  block_best(bk_r, bi_r, bk_p, bi_p, rk, ri);
+  if (tid == 0) {
+    const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + c) * 2;
     p.race_key[slot] = bk_r;
     p.race_idx[slot] = bi_r;
     p.race_key[slot + 1] = bk_p;
     p.race_idx[slot + 1] = bi_p;
-    __threadfence();
-    const unsigned prev = atomicAdd(&p.counters[b], 1u);
-    is_last = prev == static_cast<unsigned>(p.nchunk - 1);
   }
-  __syncthreads();
-  if (!is_last) return;
+}
 
-  // ---- last workgroup of sequence b: winner over chunks in chunk order
-  __threadfence();
-  if (tid == 0) {
-    double kr = INFINITY, kp = INFINITY;
-    int32_t ir = 0x7FFFFFFF, ip = 0x7FFFFFFF;
-    for (int q = 0; q < p.nchunk; ++q) {
-      const size_t slot = (static_cast<size_t>(b) * p.nchunk + q) * 2;
-      const double k0 = __hip_atomic_load(&p.race_key[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int32_t i0 = __hip_atomic_load(&p.race_idx[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const double k1 = __hip_atomic_load(&p.race_key[slot + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int32_t i1 = __hip_atomic_load(&p.race_idx[slot + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (better(k0, i0, kr, ir)) { kr = k0; ir = i0; }
-      if (better(k1, i1, kp, ip)) { kp = k1; ip = i1; }
-    }
-    const int32_t token = (kr < INFINITY) ? ir : ip;
-    p.accept_len[b] = a;
-    int32_t* out = p.out_tokens + static_cast<size_t>(b) * K;
-    for (int i = 0; i < K; ++i) out[i] = i < a ? dr[i] : (i == a ? token : -1);
-    __hip_atomic_store(&p.counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// One workgroup per sequence: the race winner over every chunk (the (key, index) minimum
+// is order-independent), then the outputs.
+__global__ void __launch_bounds__(kThreads) sample_finish_kernel(const SampleParams p) {
+  __shared__ double rk[2][kThreads / kWave];
+  __shared__ int32_t ri[2][kThreads / kWave];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int K = p.K;
+  double bk_r = INFINITY, bk_p = INFINITY;
+  int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
+  for (int q = tid; q < p.race_nchunk; q += kThreads) {
+    const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + q) * 2;
+    const double k0 = p.race_key[slot], k1 = p.race_key[slot + 1];
+    const int32_t i0 = p.race_idx[slot], i1 = p.race_idx[slot + 1];
+    if (better(k0, i0, bk_r, bi_r)) { bk_r = k0; bi_r = i0; }
+    if (better(k1, i1, bk_p, bi_p)) { bk_p = k1; bi_p = i1; }
   }
+  block_best(bk_r, bi_r, bk_p, bi_p, rk, ri);
+  const int a = p.decision[b];
+  const int32_t token = (bk_r < INFINITY) ? bi_r : bi_p;
+  if (tid < K) {
+    const int32_t* dr = p.drafts + static_cast<size_t>(b) * (K - 1);
+    p.out_tokens[static_cast<size_t>(b) * K + tid] = tid < a ? dr[tid] : (tid == a ? token : -1);
+  }
+  if (tid == 0) p.accept_len[b] = a;
 }
 
 }  // namespace
 
 int sample_chunk(int V) {
   (void)V;
-  return 8192;
+  return kLseChunk;
 }
 
-size_t sample_workspace_bytes(int B, int K, int V, int nchunk) {
+int sample_race_chunk(int V) {
   (void)V;
+  return kRaceChunk;
+}
+
+size_t sample_workspace_bytes(int B, int K, int V) {
   const size_t rows = static_cast<size_t>(B) * (2 * K - 1);
+  const size_t nchunk = (static_cast<size_t>(V) + kLseChunk - 1) / kLseChunk;
+  const size_t nrace = (static_cast<size_t>(V) + kRaceChunk - 1) / kRaceChunk;
   size_t off = 0;
-  off += rows * nchunk * sizeof(double);          // part_s
-  off += static_cast<size_t>(B) * nchunk * 2 * sizeof(double);  // race_key
-  off += rows * nchunk * sizeof(float);           // part_m
-  off += static_cast<size_t>(B) * nchunk * 2 * sizeof(int32_t); // race_idx
-  off = (off + 15) & ~static_cast<size_t>(15);
-  off += static_cast<size_t>(B) * sizeof(unsigned int);         // counters
-  return off;
+  off += rows * nchunk * sizeof(double);                    // part_s
+  off += static_cast<size_t>(B) * nrace * 2 * sizeof(double);  // race_key
+  off += rows * nchunk * sizeof(float);                     // part_m
+  off += static_cast<size_t>(B) * nrace * 2 * sizeof(int32_t); // race_idx
+  off += static_cast<size_t>(B) * sizeof(int32_t);          // decision
+  return (off + 15) & ~static_cast<size_t>(15);
 }
 
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stream) {
   const dim3 g1(p.nchunk, p.B * (2 * p.K - 1));
-  const dim3 g2(p.nchunk, p.B);
+  const dim3 g2(p.race_nchunk, p.B);
   if (dtype == SV_BF16) {
     hipLaunchKernelGGL(row_lse_kernel<true>, g1, dim3(kLseThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
@@ -307,6 +358,9 @@ hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stre
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sample_race_kernel<false>, g2, dim3(kThreads), 0, stream, p);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sample_finish_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -270,8 +270,7 @@ sv_status sv_accept_sample_workspace(int32_t B, int32_t K, int32_t V, size_t* by
   if (static_cast<int64_t>(B) * (2 * K - 1) > 65535)
     return fail(SV_ERR_INVALID_ARG, "B * (2K - 1) must be <= 65535");
   if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
-  const int chunk = sv::sample_chunk(V);
-  *bytes = sv::sample_workspace_bytes(B, K, V, (V + chunk - 1) / chunk);
+  *bytes = sv::sample_workspace_bytes(B, K, V);
   return ok();
 }
 
@@ -292,7 +291,9 @@ sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
     return fail(SV_ERR_INVALID_ARG, "logits, drafts and outputs are required");
   const int chunk = sv::sample_chunk(V);
   const int nchunk = (V + chunk - 1) / chunk;
-  const size_t need = sv::sample_workspace_bytes(B, K, V, nchunk);
+  const int race_chunk = sv::sample_race_chunk(V);
+  const int race_nchunk = (V + race_chunk - 1) / race_chunk;
+  const size_t need = sv::sample_workspace_bytes(B, K, V);
   if (!workspace || workspace_bytes < need)
     return fail(SV_ERR_WORKSPACE, "sampling accept needs %zu workspace bytes", need);
   if (!aligned16(workspace)) return fail(SV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
@@ -307,18 +308,19 @@ sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
   p.part_s = reinterpret_cast<double*>(w);
   w += rows * nchunk * sizeof(double);
   p.race_key = reinterpret_cast<double*>(w);
-  w += static_cast<size_t>(B) * nchunk * 2 * sizeof(double);
+  w += static_cast<size_t>(B) * race_nchunk * 2 * sizeof(double);
   p.part_m = reinterpret_cast<float*>(w);
   w += rows * nchunk * sizeof(float);
   p.race_idx = reinterpret_cast<int32_t*>(w);
-  w += static_cast<size_t>(B) * nchunk * 2 * sizeof(int32_t);
-  const size_t used = static_cast<size_t>(w - static_cast<char*>(workspace));
-  p.counters = reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + ((used + 15) & ~static_cast<size_t>(15)));
+  w += static_cast<size_t>(B) * race_nchunk * 2 * sizeof(int32_t);
+  p.decision = reinterpret_cast<int32_t*>(w);
   p.B = B;
   p.K = K;
   p.V = V;
   p.chunk = chunk;
   p.nchunk = nchunk;
+  p.race_chunk = race_chunk;
+  p.race_nchunk = race_nchunk;
   p.inv_t = 1.0 / static_cast<double>(temperature);
   p.seed = seed;
   p.offset = offset;

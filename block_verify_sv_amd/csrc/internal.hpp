@@ -72,17 +72,19 @@ struct SampleParams {
   int32_t* out_tokens;
   float* part_m;              // [rows][nchunk] chunk maxima of the raw logits
   double* part_s;             // [rows][nchunk] chunk sums of exp((x - m) / T)
-  double* race_key;           // [B][nchunk][2] chunk winners' keys (residual, p)
-  int32_t* race_idx;          // [B][nchunk][2]
-  unsigned int* counters;     // [B] (zero between calls)
+  double* race_key;           // [B][race_nchunk][2] chunk winners' keys (residual, p)
+  int32_t* race_idx;          // [B][race_nchunk][2]
+  int32_t* decision;          // [B] drafts accepted
   int32_t B, K, V;
-  int32_t chunk, nchunk;
-  float inv_t;
+  int32_t chunk, nchunk;      // vocabulary chunks of the normaliser pass
+  int32_t race_chunk, race_nchunk;
+  double inv_t;
   uint64_t seed, offset;
 };
 
-size_t sample_workspace_bytes(int B, int K, int V, int nchunk);
+size_t sample_workspace_bytes(int B, int K, int V);
 int sample_chunk(int V);
+int sample_race_chunk(int V);
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------- latent compressor

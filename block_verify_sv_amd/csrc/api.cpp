@@ -363,12 +363,12 @@ sv_status sv_latent_compress(int32_t B, int32_t C, int32_t N, int32_t D, sv_dtyp
   p.queries = queries;
   p.feats = feats;
   p.out = out;
-  p.scores = static_cast<float*>(workspace);
   p.B = B;
   p.C = C;
   p.N = N;
   p.D = D;
   p.scale = scale > 0.0f ? scale : 1.0f;
+  sv::compress_bind_workspace(p, workspace);
   return device_status(sv::launch_compress(p, static_cast<hipStream_t>(stream)),
                        "sv_latent_compress launch");
 }

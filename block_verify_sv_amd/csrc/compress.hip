@@ -1,15 +1,17 @@
 // Latent visual compressor (SpecFLASH README, "components", compressor equation):
 //     out[b] = softmax(scale * C . F_b^T) . F_b,   softmax over the N feature rows.
 //
-// Pass 1 (scores_kernel): S_b = scale * C . F_b^T on MFMA 32x32x16 fp16.  Grid (N/64
-// tile, b); four waves own 32x32 blocks of the 64 (queries) x 64 (features) tile and
-// read both operands straight from global memory (each lane 16 contiguous bytes of a
-// query row and of a feature row per step), fp32 scores to the workspace.
-// Pass 2 (out_kernel): grid (D/128 tile, b).  The workgroup turns its C score rows into
-// unnormalised fp16 weights exp(s - max) in LDS with fp32 row sums, then streams F_b in
-// 32-row tiles, transposing each tile into LDS (the contraction runs over the feature
-// rows, so the MFMA operand needs 8 consecutive rows of one column), and accumulates
-// out = W . F_b / rowsum on MFMA.
+// Pass 1 (scores_kernel): C . F_b^T on MFMA 32x32x16 fp16, as two partial sums over
+// the halves of d.  Grid (64-feature tile, b, half); both operands are staged through
+// LDS in 64-d steps from coalesced loads held in a register ring.
+// Pass 2 (softmax_kernel): one wave per query row adds the two partial sums, scales,
+// and turns the scores into fp16 weights exp(s - max) and their fp32 sum (of the
+// rounded weights).
+// Pass 3 (out_kernel): grid (D/128 tile, b).  The workgroup streams F_b in 32-row tiles
+// through a register ring (several tiles in flight, each with its weight operands read
+// from the cache-resident workspace), transposes each tile into LDS -- the contraction
+// runs over the feature rows, so the MFMA operand needs 8 consecutive rows of one
+// column -- and accumulates out = W . F_b / rowsum on MFMA.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -17,109 +19,186 @@ namespace sv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxN = 1024;
-constexpr int kNT = 32;                 // feature rows per pass-2 tile
-constexpr int kDT = 128;                // output columns per pass-2 workgroup
+constexpr int kMaxC = 64;
+constexpr int kSK = 64;                 // pass-1 contraction step (d per LDS tile)
+constexpr int kSRing = 4;               // pass-1 register ring (kSRing - 1 steps in flight)
+constexpr int kNT = 32;                 // feature rows per pass-3 tile
+constexpr int kDT = 128;                // output columns per pass-3 workgroup
+constexpr int kRing = 6;                // pass-3 register ring (kRing - 1 tiles in flight)
 
+__host__ __device__ __forceinline__ int pad_n(int N) { return (N + kNT - 1) / kNT * kNT; }
+
+// Pass 1.  Workgroup (64-feature tile, image b, contraction half kh): the 64 x 64 score
+// tile over d in [kh*D/2, (kh+1)*D/2), as the kh-th of two partial sums (the softmax
+// pass adds them in order).  Both operands are staged in 64-d steps: coalesced 16-byte
+// loads (8 lanes per 128-byte row segment) into a register ring kSRing-1 steps ahead,
+// then padded LDS tiles that the four 32x32 MFMA blocks read.
 __global__ void __launch_bounds__(kThreads) scores_kernel(const CompressParams p) {
+  constexpr int ROW = kSK + 8;                     // LDS row: 64 d + 16 bytes of padding
+  __shared__ __align__(16) uint16_t q_lds[2][64 * ROW];
+  __shared__ __align__(16) uint16_t f_lds[2][64 * ROW];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wc = wave >> 1, wn = wave & 1;
+  const int n0 = blockIdx.x * 64;
   const int b = blockIdx.y;
-  const int n0 = blockIdx.x * 64 + wn * 32;
-  const int c = wc * 32 + l32;            // query row of the A operand
-  const int n = n0 + l32;                 // feature row of the B operand
-  const uint16_t* qrow = static_cast<const uint16_t*>(p.queries) + static_cast<size_t>(c) * p.D;
-  const uint16_t* frow =
-      static_cast<const uint16_t*>(p.feats) + (static_cast<size_t>(b) * p.N + n) * p.D;
-  const bool qa = c < p.C, fa = n < p.N;
-  if (wc * 32 >= p.C) return;            // no query rows for this wave
+  const int kh = blockIdx.z;
+  const bool active = wc * 32 < p.C;
+  const int steps = (p.D >> 1) / kSK;
+  const int dbeg = kh * (p.D >> 1);
+  // load mapping: chunk ch = tid + 256u covers row ch/8, 8 halves at column 8*(ch%8);
+  // rows past C (queries) or N (features) are clamped in bounds and never stored
+  const uint16_t* qsrc[2];
+  const uint16_t* fsrc[2];
+  int loff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ch = tid + kThreads * u;
+    const int r = ch >> 3, col = (ch & 7) * 8;
+    qsrc[u] = static_cast<const uint16_t*>(p.queries) + static_cast<size_t>(min(r, p.C - 1)) * p.D + dbeg + col;
+    fsrc[u] = static_cast<const uint16_t*>(p.feats) +
+              (static_cast<size_t>(b) * p.N + min(n0 + r, p.N - 1)) * p.D + dbeg + col;
+    loff[u] = r * ROW + col;
+  }
+  struct ST { u32x4 q[2], f[2]; };
+  auto load = [&](ST& t, int st) {
+    const int d = min(st, steps - 1) * kSK;       // past the end: re-read the last step
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      t.q[u] = *reinterpret_cast<const u32x4*>(qsrc[u] + d);
+      t.f[u] = *reinterpret_cast<const u32x4*>(fsrc[u] + d);
+    }
+  };
   f32x16 acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  constexpr int U = 8;
-  for (int d0 = 0; d0 < p.D; d0 += 16 * U) {
-    u32x4 av[U], bv[U];
+  auto step = [&](const ST& t, int st) {
+    uint16_t* ql = q_lds[st & 1];
+    uint16_t* fl = f_lds[st & 1];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int d = d0 + u * 16 + h * 8;
-      av[u] = qa ? *reinterpret_cast<const u32x4*>(qrow + d) : u32x4{0u, 0u, 0u, 0u};
-      bv[u] = fa ? *reinterpret_cast<const u32x4*>(frow + d) : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < 2; ++u) {
+      *reinterpret_cast<u32x4*>(&ql[loff[u]]) = t.q[u];
+      *reinterpret_cast<u32x4*>(&fl[loff[u]]) = t.f[u];
     }
+    __syncthreads();                               // step st in LDS; st-1's buffer free
+    if (active) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc = Mfma<TagF16>::step(av[u], bv[u], acc);
+      for (int ks = 0; ks < kSK / 16; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&ql[(wc * 32 + l32) * ROW + ks * 16 + h * 8]);
+        const u32x4 bo = *reinterpret_cast<const u32x4*>(&fl[(wn * 32 + l32) * ROW + ks * 16 + h * 8]);
+        acc = Mfma<TagF16>::step(a, bo, acc);
+      }
+    }
+  };
+  ST ring[kSRing];
+#pragma unroll
+  for (int u = 0; u < kSRing - 1; ++u) load(ring[u], u);
+  for (int s0 = 0; s0 < steps; s0 += kSRing) {
+#pragma unroll
+    for (int u = 0; u < kSRing; ++u) {
+      const int st = s0 + u;
+      if (st >= steps) break;
+      load(ring[(u + kSRing - 1) % kSRing], st + kSRing - 1);
+      step(ring[u], st);
+    }
   }
-  if (!fa) return;
-  float* srow = p.scores + static_cast<size_t>(b) * p.C * p.N + n;
+  const int n = n0 + wn * 32 + l32;
+  if (!active || n >= p.N) return;
+  float* srow = p.scores + (static_cast<size_t>(kh) * p.B + b) * p.C * p.N + n;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int cc = wc * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (cc < p.C) srow[static_cast<size_t>(cc) * p.N] = acc[r] * p.scale;
+    if (cc < p.C) srow[static_cast<size_t>(cc) * p.N] = acc[r];
   }
 }
 
+// One wave per query row (rows C..63 get zero weights and sum 1).
+__global__ void __launch_bounds__(kThreads) softmax_kernel(const CompressParams p) {
+  constexpr int kPer = 1024 / 64;                  // scores per lane (N <= 1024)
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  const int Nw = pad_n(p.N);
+  uint16_t* wr = p.weights + (static_cast<size_t>(b) * kMaxC + c) * Nw;
+  if (c >= p.C) {
+    for (int n = lane; n < Nw; n += 64) wr[n] = 0;
+    if (lane == 0) p.rowsum[b * kMaxC + c] = 1.0f;
+    return;
+  }
+  const float* s0 = p.scores + (static_cast<size_t>(b) * p.C + c) * p.N;
+  const float* s1 = s0 + static_cast<size_t>(p.B) * p.C * p.N;   // second contraction half
+  float s[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {                 // all loads in flight
+    const int n = min(lane + 64 * i, p.N - 1);
+    s[i] = (s0[n] + s1[n]) * p.scale;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (lane + 64 * i < p.N) m = fmaxf(m, s[i]);
+  m = wave_max(m);
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int n = lane + 64 * i;
+    if (n >= Nw) break;
+    uint16_t wv = 0;
+    if (n < p.N) {
+      wv = f32_to_f16(__expf(s[i] - m));
+      sum += f16_to_f32(wv);
+    }
+    wr[n] = wv;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if (lane == 0) p.rowsum[b * kMaxC + c] = sum;
+}
+
 __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
-  constexpr int WROW = kMaxN + 8;                 // fp16 weight row (padded)
-  constexpr int FROW = kNT + 8;                   // transposed feature tile row (padded)
-  __shared__ __align__(16) uint16_t w_lds[64 * WROW];
-  __shared__ __align__(16) uint16_t f_lds[kDT * FROW];
-  __shared__ float rsum[64];
+  constexpr int FROW = kNT + 8;                    // transposed feature tile row (padded)
+  __shared__ __align__(16) uint16_t f_lds[2][kDT * FROW];
+  __shared__ float rsum[kMaxC];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int b = blockIdx.y;
   const int dbase = blockIdx.x * kDT;
   const int N = p.N;
-  const int Npad = (N + kNT - 1) / kNT * kNT;
+  const int Nw = pad_n(N);
+  if (tid < kMaxC) rsum[tid] = p.rowsum[b * kMaxC + tid];
 
-  // ---- weights: wave w owns query rows w, w+4, ...
-  for (int c = wave; c < 64; c += 4) {
-    uint16_t* wr = &w_lds[c * WROW];
-    if (c >= p.C) {
-      for (int n = lane; n < Npad; n += 64) wr[n] = 0;
-      if (lane == 0) rsum[c] = 1.0f;
-      continue;
-    }
-    const float* srow = p.scores + (static_cast<size_t>(b) * p.C + c) * N;
-    float m = -INFINITY;
-    for (int n = lane; n < N; n += 64) m = fmaxf(m, srow[n]);
-    m = wave_max(m);
-    float sum = 0.0f;
-    for (int n = lane; n < Npad; n += 64) {
-      uint16_t wv = 0;
-      if (n < N) {
-        wv = f32_to_f16(__expf(srow[n] - m));
-        sum += f16_to_f32(wv);
-      }
-      wr[n] = wv;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-    if (lane == 0) rsum[c] = sum;
-  }
-
-  // ---- out tile: wave (wc, wd) owns query rows 32*wc.. and columns 64*wd.. (2 blocks)
+  // ---- out tile: wave (wc, wd) owns query rows 32*wc.. and columns 64*wd.. (2 blocks).
+  // The weight operand (8 consecutive feature rows of one query row per lane) comes
+  // straight from the workspace (cache-resident: every d tile of the image reads it).
   const int wc = wave >> 1, wd = wave & 1;
   const bool active = wc * 32 < p.C;
+  const uint16_t* wsrc = p.weights + (static_cast<size_t>(b) * kMaxC + wc * 32 + l32) * Nw + h * 8;
   f32x16 acc[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
 
-  // feature tile load: kNT rows x kDT columns = 512 chunks of 16 B, 2 per thread
+  // feature tiles: kNT rows x kDT columns = 512 chunks of 16 B, 2 per thread, held in a
+  // register ring with the tile's weight operands; tile rows past N (the last tile)
+  // re-read row N-1 and meet weights that are zero
   const uint16_t* fb = static_cast<const uint16_t*>(p.feats) + static_cast<size_t>(b) * N * p.D;
-  for (int nt = 0; nt < Npad; nt += kNT) {
-    u32x4 v[2];
+  const int nt_count = Nw / kNT;
+  struct FT { u32x4 v[2]; u32x4 a[kNT / 16]; };
+  auto load = [&](FT& f, int t) {
+    const int nt = min(t, nt_count - 1) * kNT;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int ch = tid + kThreads * u;
-      const int r = ch >> 4;                      // feature row in the tile
-      const int col = (ch & 15) * 8;              // first of 8 columns
-      v[u] = (nt + r < N) ? *reinterpret_cast<const u32x4*>(fb + static_cast<size_t>(nt + r) * p.D + dbase + col)
-                          : u32x4{0u, 0u, 0u, 0u};
+      const int r = min(nt + (ch >> 4), N - 1);
+      f.v[u] = *reinterpret_cast<const u32x4*>(fb + static_cast<size_t>(r) * p.D + dbase + (ch & 15) * 8);
     }
-    __syncthreads();                              // previous tile fully consumed
+#pragma unroll
+    for (int ks = 0; ks < kNT / 16; ++ks) f.a[ks] = *reinterpret_cast<const u32x4*>(wsrc + nt + ks * 16);
+  };
+  auto tile = [&](const FT& f, int t) {
+    uint16_t* fl = f_lds[t & 1];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int ch = tid + kThreads * u;
@@ -127,19 +206,30 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
       const int col = (ch & 15) * 8;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        f_lds[(col + e) * FROW + r] = static_cast<uint16_t>(v[u][e >> 1] >> (16 * (e & 1)));
+        fl[(col + e) * FROW + r] = static_cast<uint16_t>(f.v[u][e >> 1] >> (16 * (e & 1)));
     }
-    __syncthreads();
+    __syncthreads();                               // tile t in LDS; tile t-1's buffer free
     if (active) {
 #pragma unroll
       for (int ks = 0; ks < kNT / 16; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&w_lds[(wc * 32 + l32) * WROW + nt + ks * 16 + h * 8]);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4 bo = *reinterpret_cast<const u32x4*>(&f_lds[(wd * 64 + t * 32 + l32) * FROW + ks * 16 + h * 8]);
-          acc[t] = Mfma<TagF16>::step(a, bo, acc[t]);
+        for (int tt = 0; tt < 2; ++tt) {
+          const u32x4 bo = *reinterpret_cast<const u32x4*>(&fl[(wd * 64 + tt * 32 + l32) * FROW + ks * 16 + h * 8]);
+          acc[tt] = Mfma<TagF16>::step(f.a[ks], bo, acc[tt]);
         }
       }
+    }
+  };
+  FT ring[kRing];
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u) load(ring[u], u);
+  for (int t0 = 0; t0 < nt_count; t0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int t = t0 + u;
+      if (t >= nt_count) break;
+      load(ring[(u + kRing - 1) % kRing], t + kRing - 1);
+      tile(ring[u], t);
     }
   }
   if (!active) return;
@@ -157,12 +247,26 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
 }  // namespace
 
 size_t compress_workspace_bytes(int B, int C, int N) {
-  return static_cast<size_t>(B) * C * N * sizeof(float);
+  const size_t scores = (2 * static_cast<size_t>(B) * C * N * sizeof(float) + 15) / 16 * 16;
+  const size_t weights = static_cast<size_t>(B) * kMaxC * pad_n(N) * sizeof(uint16_t);
+  return scores + weights + static_cast<size_t>(B) * kMaxC * sizeof(float);
+}
+
+void compress_bind_workspace(CompressParams& p, void* workspace) {
+  char* w = static_cast<char*>(workspace);
+  p.scores = reinterpret_cast<float*>(w);
+  w += (2 * static_cast<size_t>(p.B) * p.C * p.N * sizeof(float) + 15) / 16 * 16;
+  p.weights = reinterpret_cast<uint16_t*>(w);
+  w += static_cast<size_t>(p.B) * kMaxC * pad_n(p.N) * sizeof(uint16_t);
+  p.rowsum = reinterpret_cast<float*>(w);
 }
 
 hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(scores_kernel, dim3((p.N + 63) / 64, p.B), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(scores_kernel, dim3((p.N + 63) / 64, p.B, 2), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(softmax_kernel, dim3(kMaxC / (kThreads / 64), p.B), dim3(kThreads), 0, stream, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(out_kernel, dim3(p.D / kDT, p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();

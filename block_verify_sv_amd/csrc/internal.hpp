@@ -93,11 +93,14 @@ struct CompressParams {
   const void* feats;
   void* out;
   float* scores;              // [B][C][N] fp32
+  uint16_t* weights;          // [B][64][N rounded up to 32] fp16 softmax numerators
+  float* rowsum;              // [B][64] sums of the rounded weights
   int32_t B, C, N, D;
   float scale;
 };
 
 size_t compress_workspace_bytes(int B, int C, int N);
+void compress_bind_workspace(CompressParams& p, void* workspace);
 hipError_t launch_compress(const CompressParams& p, hipStream_t stream);
 
 // ---------------------------------------------------------------- KV append

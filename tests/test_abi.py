@@ -137,7 +137,8 @@ def test_sample_validation(lib):
 def test_compress_validation(lib):
     n = ctypes.c_size_t()
     assert lib.sv_latent_compress_workspace(32, 64, 576, 4096, ctypes.byref(n)) == OK
-    assert n.value == 32 * 64 * 576 * 4
+    # two fp32 partial score sets, fp16 weights over 64 padded rows x N rounded up to 32, fp32 row sums
+    assert n.value == 2 * 32 * 64 * 576 * 4 + 32 * 64 * 576 * 2 + 32 * 64 * 4
     for B, C, N, D in [(0, 64, 576, 4096), (32, 65, 576, 4096), (32, 64, 0, 4096),
                        (32, 64, 2000, 4096), (32, 64, 576, 100)]:
         assert lib.sv_latent_compress_workspace(B, C, N, D, ctypes.byref(n)) == INVALID

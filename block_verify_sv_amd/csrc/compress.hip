@@ -9,9 +9,9 @@
 // rounded weights).
 // Pass 3 (out_kernel): grid (D/128 tile, b).  The workgroup streams F_b in 32-row tiles
 // through a register ring (several tiles in flight, each with its weight operands read
-// from the cache-resident workspace), transposes each tile into LDS -- the contraction
-// runs over the feature rows, so the MFMA operand needs 8 consecutive rows of one
-// column -- and accumulates out = W . F_b / rowsum on MFMA.
+// from the cache-resident workspace) into LDS as loaded; the contraction runs over the
+// feature rows, so each MFMA operand gathers 8 consecutive rows of one column with
+// 16-bit LDS reads.  out = W . F_b / rowsum accumulates on MFMA.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -156,8 +156,8 @@ __global__ void __launch_bounds__(kThreads) softmax_kernel(const CompressParams 
 }
 
 __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
-  constexpr int FROW = kNT + 8;                    // transposed feature tile row (padded)
-  __shared__ __align__(16) uint16_t f_lds[2][kDT * FROW];
+  constexpr int FROW = kDT + 8;                    // feature tile row (padded)
+  __shared__ __align__(16) uint16_t f_lds[2][kNT * FROW];
   __shared__ float rsum[kMaxC];
 
   const int tid = threadIdx.x;
@@ -200,13 +200,9 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
   auto tile = [&](const FT& f, int t) {
     uint16_t* fl = f_lds[t & 1];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u) {                  // row-major, as loaded
       const int ch = tid + kThreads * u;
-      const int r = ch >> 4;
-      const int col = (ch & 15) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        fl[(col + e) * FROW + r] = static_cast<uint16_t>(f.v[u][e >> 1] >> (16 * (e & 1)));
+      *reinterpret_cast<u32x4*>(&fl[(ch >> 4) * FROW + (ch & 15) * 8]) = f.v[u];
     }
     __syncthreads();                               // tile t in LDS; tile t-1's buffer free
     if (active) {
@@ -214,7 +210,14 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
       for (int ks = 0; ks < kNT / 16; ++ks) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const u32x4 bo = *reinterpret_cast<const u32x4*>(&fl[(wd * 64 + tt * 32 + l32) * FROW + ks * 16 + h * 8]);
+          // the operand's 8 consecutive feature rows of one column, gathered as 16-bit
+          // reads (consecutive lanes read consecutive columns: no bank conflicts)
+          const uint16_t* col = &fl[(ks * 16 + h * 8) * FROW + wd * 64 + tt * 32 + l32];
+          u32x4 bo;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            bo[q] = static_cast<uint32_t>(col[(2 * q) * FROW]) |
+                    (static_cast<uint32_t>(col[(2 * q + 1) * FROW]) << 16);
           acc[tt] = Mfma<TagF16>::step(f.a[ks], bo, acc[tt]);
         }
       }

@@ -99,15 +99,17 @@ AttnPlan plan_attention(const sv_attn_desc& d) {
   AttnPlan pl;
   const int64_t n_max = static_cast<int64_t>(d.max_ctx) + d.block;
   pl.rows = d.block * (d.num_q_heads / d.num_kv_heads);
+  pl.row_halves = pl.rows > 128 ? 2 : 1;         // a workgroup holds 4 row blocks of 32
   int64_t chunk = d.split_keys;
   if (chunk == 0) {
-    // one key split per compute unit: total (context + block) keys over all KV heads,
-    // spread over the 256 CUs, in multiples of min(P, 64) keys (a split then starts on
-    // a page boundary or a 64-key boundary inside a page)
+    // one workgroup per compute unit: total (context + block) keys over all KV heads and
+    // row halves, spread over the 256 CUs, in multiples of min(P, 64) keys (a split then
+    // starts on a page boundary or a 64-key boundary inside a page)
     const int64_t gran = d.page_size < 64 ? d.page_size : 64;
     const int64_t ctx_sum =
         d.sum_ctx_hint > 0 ? d.sum_ctx_hint : static_cast<int64_t>(d.batch) * d.max_ctx;
-    const int64_t work = (ctx_sum + static_cast<int64_t>(d.batch) * d.block) * d.num_kv_heads;
+    const int64_t work =
+        (ctx_sum + static_cast<int64_t>(d.batch) * d.block) * d.num_kv_heads * pl.row_halves;
     chunk = (work + kNumCUs - 1) / kNumCUs;
     chunk = (chunk + gran - 1) / gran * gran;
     if (chunk < 64) chunk = 64;
@@ -202,6 +204,8 @@ sv_status sv_verify_attention(const sv_attn_desc* desc, const void* q, const voi
   p.max_ctx = desc->max_ctx;
   p.chunk = pl.chunk;
   p.nsplit = pl.nsplit;
+  p.nsplit_pad = (pl.nsplit + 7) / 8 * 8;
+  p.row_halves = pl.row_halves;
   const float scale = desc->scale > 0.0f ? desc->scale : 1.0f / sqrtf(static_cast<float>(desc->head_dim));
   p.scale_log2 = scale * 1.4426950408889634f;
   return device_status(sv::launch_attention(p, desc->head_dim, desc->dtype,

@@ -102,9 +102,15 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   const int l32 = lane & 31;
   const int rg = wave % RG;                      // row group: row blocks rg + RG*t
   const int kh = wave / RG;                      // key part of each tile
-  const int s = blockIdx.x;
+  // blockIdx.x = half * nsplit_pad + s: the row halves of one split are nsplit_pad (a
+  // multiple of 8) workgroups apart, so round-robin dispatch puts both on one XCD and
+  // the second read of each KV tile comes from that XCD's L2
+  const int half = blockIdx.x / p.nsplit_pad;
+  const int s = blockIdx.x - half * p.nsplit_pad;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
+  if (s >= p.nsplit) return;                     // padding of the split index
+  const int rb0 = half * RG * NRB;               // first row block of this half
 
   // ---- start-up.  Nothing below needs the context length until the early-exit test,
   // so every independent load is issued before the first wait and they share one round
@@ -142,7 +148,7 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   bool active[NRB];
 #pragma unroll
   for (int t = 0; t < NRB; ++t) {
-    const int rb = rg + RG * t;
+    const int rb = rb0 + rg + RG * t;
     const int r = min(rb * 32 + l32, p.R - 1);
     active[t] = rb * 32 < p.R;
     const int i = r / p.G;
@@ -449,7 +455,7 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
 #pragma unroll
   for (int t = 0; t < NRB; ++t) {
     if (!active[t]) continue;
-    const int rb = rg + RG * t;
+    const int rb = rb0 + rg + RG * t;
     const int r = rb * 32 + l32;
     if (r < p.R) {
       const float inv = l_run[t] > 0.0f ? 1.0f / l_run[t] : 0.0f;
@@ -592,18 +598,14 @@ __global__ void __launch_bounds__(kMergeWaves * 64) attn_merge_kernel(const Attn
 
 template <class Tag, int D>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
-  const dim3 grid(p.nsplit, p.Hkv, p.B);
-  // up to 4 row blocks: 4 row-group waves x 2 key halves, one row block each (512
-  // threads, two waves per SIMD); a deep register ring for 16-bit data.  Up to 8 row
-  // blocks: 4 row-group waves with two row blocks each and whole tiles (256 threads).
-  if ((p.R + 31) / 32 <= 4) {
-    if constexpr (Tag::kBytes == 2)
-      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, kRingDeep>), grid, dim3(512), 0, stream, p);
-    else
-      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, 2>), grid, dim3(512), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 2, 1, 2>), grid, dim3(256), 0, stream, p);
-  }
+  // 4 row-group waves x 2 key halves, one row block each (512 threads, two waves per
+  // SIMD), a deep register ring for 16-bit data.  More than 4 row blocks (K*G > 128)
+  // run as two row halves of the same split.
+  const dim3 grid(p.nsplit_pad * p.row_halves, p.Hkv, p.B);
+  if constexpr (Tag::kBytes == 2)
+    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, kRingDeep>), grid, dim3(512), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, 2>), grid, dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 mgrid(D / 32 * 4, (p.R + 31) / 32, p.B * p.Hkv);

@@ -30,6 +30,8 @@ struct AttnParams {
   int32_t P_log2, max_pages, num_pages, max_ctx;
   int32_t chunk;        // keys per split
   int32_t nsplit;       // splits allocated per (b, g)
+  int32_t nsplit_pad;   // nsplit rounded up to a multiple of 8 (grid spacing of halves)
+  int32_t row_halves;   // 1, or 2 when K*G > 128 rows (each half: 4 row blocks)
   float scale_log2;     // scale * log2(e)
   uint64_t mask[kMaxBlock];
 };
@@ -37,6 +39,7 @@ struct AttnParams {
 struct AttnPlan {
   int chunk;
   int nsplit;
+  int row_halves;
   int rows;             // R = K * G
   size_t o_bytes;       // partial outputs (16-byte aligned), then (m, l) pairs
   size_t ws_bytes;

@@ -308,23 +308,29 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
     for (int t = 0; t < NRB; ++t) {
       if (!active[t]) continue;
       scores(t);
-      float sv[16 * KBW];
+      // masked scores are overwritten in place (a separate array would cost a copy of
+      // every score on the unmasked path)
+      if (need_mask) {
 #pragma unroll
-      for (int kbi = 0; kbi < KBW; ++kbi) {
-        const int kb = kh * KBW + kbi;
-        if (!need_mask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sv[kbi * 16 + r] = sacc[t][kbi][r];
-        } else {
+        for (int kbi = 0; kbi < KBW; ++kbi) {
+          const int kb = kh * KBW + kbi;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
+            // branch-free: context keys are visible, block key t2 iff bit t2 of the row's
+            // mask, nothing at or past the split end
             const int pos = kt + kb * 32 + key_of_reg(r, h);
             const int t2 = pos - ctx;
-            const bool vis = pos < k1 && (t2 < 0 || ((rmask[t] >> (t2 & 63)) & 1ull));
-            sv[kbi * 16 + r] = vis ? sacc[t][kbi][r] : -INFINITY;
+            const uint32_t bit = static_cast<uint32_t>(rmask[t] >> (t2 & 63)) & 1u;
+            const uint32_t vis = static_cast<uint32_t>(pos < k1) & (static_cast<uint32_t>(t2 < 0) | bit);
+            sacc[t][kbi][r] = vis ? sacc[t][kbi][r] : -INFINITY;
           }
         }
       }
+      float sv[16 * KBW];
+#pragma unroll
+      for (int kbi = 0; kbi < KBW; ++kbi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sv[kbi * 16 + r] = sacc[t][kbi][r];
       float mt = sv[0];
 #pragma unroll
       for (int e = 1; e < 16 * KBW; ++e) mt = fmaxf(mt, sv[e]);

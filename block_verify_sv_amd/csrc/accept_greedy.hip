@@ -6,10 +6,10 @@
 // scans a chunk of one row with 16-byte loads (all issued before any is consumed) and
 // reduces a packed 64-bit key (orderable value bits << 32 | ~index) -- so the maximum
 // key is the largest value at the lowest index -- through the wave and LDS into one
-// non-returning device-scope atomicMax; nothing waits for it.  The walk pass has one
-// wave per sequence: lane i reads-and-clears row i's key (leaving the workspace zeroed
-// for the next call), and a ballot over the lanes whose draft differs from the
-// target's choice gives the accepted length.  The kernel boundary orders the two.
+// plain store per (row, chunk).  The walk pass has one wave per sequence: it reduces
+// the K rows' chunk keys (an order-independent maximum), and a ballot over the lanes
+// whose draft differs from the target's choice gives the accepted length.  The kernel
+// boundary orders the two; the workspace carries no state between calls.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -17,7 +17,8 @@ namespace sv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLoadsPerThread = 4;                // 16-byte loads per thread per chunk
+constexpr int kLoadsPerThread = 4;                // 16-byte loads per thread per round
+constexpr int kMaxChunks = 32;                    // vocabulary chunks per row, at most
 
 template <bool kBF16>
 __device__ __forceinline__ float load_logit(const void* base, size_t i) {
@@ -38,26 +39,28 @@ __global__ void __launch_bounds__(kThreads) greedy_argmax_kernel(const GreedyPar
   uint64_t best = 0;
   constexpr int EPV = kBF16 ? 8 : 4;              // elements per 16-byte load
   if ((p.V % EPV) == 0) {
-    // every load of the chunk is issued before any is consumed; indices past the row
-    // end are clamped to its last 16 bytes (in bounds) and ignored below
-    u32x4 v[kLoadsPerThread];
+    // per round every load is issued before any is consumed; indices past the row end
+    // are clamped to its last 16 bytes (in bounds) and ignored below
+    for (int jr = j0; jr < j1; jr += kLoadsPerThread * kThreads * EPV) {
+      u32x4 v[kLoadsPerThread];
 #pragma unroll
-    for (int u = 0; u < kLoadsPerThread; ++u) {
-      const int j = min(j0 + (tid + u * kThreads) * EPV, p.V - EPV);
-      v[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.logits) +
-                                             (rbase + j) * (kBF16 ? 2 : 4));
-    }
+      for (int u = 0; u < kLoadsPerThread; ++u) {
+        const int j = min(jr + (tid + u * kThreads) * EPV, p.V - EPV);
+        v[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.logits) +
+                                               (rbase + j) * (kBF16 ? 2 : 4));
+      }
 #pragma unroll
-    for (int u = 0; u < kLoadsPerThread; ++u) {
-      const int j = j0 + (tid + u * kThreads) * EPV;
-      if (j >= j1) continue;
+      for (int u = 0; u < kLoadsPerThread; ++u) {
+        const int j = jr + (tid + u * kThreads) * EPV;
+        if (j >= j1) continue;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        float x;
-        if constexpr (kBF16) x = bf16_to_f32(static_cast<uint16_t>(v[u][e >> 1] >> (16 * (e & 1))));
-        else x = __uint_as_float(v[u][e]);
-        const uint64_t key = argmax_key(x, static_cast<uint32_t>(j + e));
-        best = key > best ? key : best;
+        for (int e = 0; e < EPV; ++e) {
+          float x;
+          if constexpr (kBF16) x = bf16_to_f32(static_cast<uint16_t>(v[u][e >> 1] >> (16 * (e & 1))));
+          else x = __uint_as_float(v[u][e]);
+          const uint64_t key = argmax_key(x, static_cast<uint32_t>(j + e));
+          best = key > best ? key : best;
+        }
       }
     }
   } else {
@@ -73,8 +76,7 @@ __global__ void __launch_bounds__(kThreads) greedy_argmax_kernel(const GreedyPar
     uint64_t m = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / kWave; ++w) m = red[w] > m ? red[w] : m;
-    __hip_atomic_fetch_max(&p.keys[row], static_cast<unsigned long long>(m), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    p.keys[static_cast<size_t>(row) * p.nchunk + blockIdx.x] = m;
   }
 }
 
@@ -86,13 +88,21 @@ __global__ void __launch_bounds__(kThreads) greedy_walk_kernel(const GreedyParam
   if (b >= p.B) return;                           // whole waves
   const int K = p.K;
   const bool in = lane < K;
+  // lane i reduces row i's chunk keys (at most kMaxChunks; plain data written by the
+  // argmax pass; all loads in flight, clamped index)
+  const unsigned long long* keys = p.keys + static_cast<size_t>(b) * K * p.nchunk;
+  uint64_t best = 0;
+  if (in) {
+    uint64_t k[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      k[c] = keys[static_cast<size_t>(lane) * p.nchunk + min(c, p.nchunk - 1)];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) best = k[c] > best ? k[c] : best;
+  }
   int32_t t = -1;
   if (in) {
-    // read-and-clear: the latest value in the key's modification order, and a zeroed
-    // key for the next call
-    const uint64_t key = __hip_atomic_exchange(&p.keys[static_cast<size_t>(b) * K + lane], 0ull,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    t = static_cast<int32_t>(argmax_key_index(key));
+    t = static_cast<int32_t>(argmax_key_index(best));
     if (p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
   }
   // draft k+1 (drafts[b][k]) is checked against row k's choice, k = 0 .. K-2
@@ -107,13 +117,15 @@ __global__ void __launch_bounds__(kThreads) greedy_walk_kernel(const GreedyParam
 }  // namespace
 
 size_t greedy_workspace_bytes(int B, int K) {
-  return static_cast<size_t>(B) * K * sizeof(unsigned long long);
+  return static_cast<size_t>(B) * K * kMaxChunks * sizeof(unsigned long long);
 }
 
 int greedy_chunk(int V, sv_dtype dtype) {
-  (void)V;
-  // 16 KB of logits per workgroup: kLoadsPerThread 16-byte loads per thread
-  return kLoadsPerThread * kThreads * (dtype == SV_BF16 ? 8 : 4);
+  // rounds of kLoadsPerThread 16-byte loads per thread (16 KB per workgroup), and at
+  // most kMaxChunks chunks per row
+  const int round = kLoadsPerThread * kThreads * (dtype == SV_BF16 ? 8 : 4);
+  const int rounds = (V + round - 1) / round;
+  return round * ((rounds + kMaxChunks - 1) / kMaxChunks);
 }
 
 hipError_t launch_greedy(const GreedyParams& p, sv_dtype dtype, hipStream_t stream) {

@@ -56,7 +56,7 @@ struct GreedyParams {
   int32_t* accept_len;
   int32_t* out_tokens;
   int32_t* argmax;
-  unsigned long long* keys;   // [B][K] packed argmax keys (zero between calls)
+  unsigned long long* keys;   // [B][K][nchunk] packed argmax keys of every chunk
   int32_t B, K, V;
   int32_t chunk;              // vocabulary entries per workgroup
   int32_t nchunk;

@@ -28,10 +28,8 @@
  *     message for the last failure on the calling thread is in sv_last_error().
  *   - Inputs must be finite.  Results are bitwise reproducible for identical
  *     inputs, shapes and workspace contents.
- *   - The workspace of sv_accept_greedy holds argmax keys: it must be zero-filled
- *     once before its first use, and every call leaves it zeroed again (so one
- *     buffer serves calls of any shape).  Two calls that share one workspace
- *     must not overlap in time.
+ *   - Workspaces carry no state between calls and need no initialisation; two
+ *     calls that share one workspace must not overlap in time.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -131,7 +129,7 @@ sv_status sv_verify_attention(const sv_attn_desc* desc, const void* q, const voi
  *   argmax[b][i]  = t_i (optional, NULL = not written)
  * Layouts: logits [B][K][V] (SV_F32 or SV_BF16); drafts [B][K-1] int32 (draft d_k at
  * index k-1); accept_len [B], out_tokens [B][K], argmax [B][K] int32.
- * Limits: 1 <= K <= 64, 1 <= V < 2^31.  The workspace must be zeroed before first use.
+ * Limits: 1 <= K <= 64, 1 <= V < 2^31.  Workspace: B*K*32 packed keys (no initial state).
  * ------------------------------------------------------------------------------------ */
 sv_status sv_accept_greedy_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes);
 sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,

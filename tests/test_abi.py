@@ -111,7 +111,7 @@ def test_attention_rejects_bad_masks_and_buffers(lib):
 def test_greedy_validation(lib):
     n = ctypes.c_size_t()
     assert lib.sv_accept_greedy_workspace(1, 16, 152064, ctypes.byref(n)) == OK
-    assert n.value == 16 * 8             # one packed argmax key per row
+    assert n.value == 16 * 32 * 8        # packed argmax keys of up to 32 chunks per row
     for B, K, V in [(0, 16, 10), (1, 0, 10), (1, 65, 10), (1, 16, 0), (5000, 16, 10)]:
         assert lib.sv_accept_greedy_workspace(B, K, V, ctypes.byref(n)) == INVALID
     args = lambda dt, ws: (1, 16, 1000, dt, FAKE, FAKE, FAKE, FAKE, None, ws, 1 << 20, None)

@@ -41,6 +41,8 @@ def test_greedy_named_workloads(gpu_lib, name):
     (5, 1, 5000, "bf16"),       # K = 1: no drafts, the target's token only
     (64, 16, 20000, "bf16"),    # many sequences
     (2, 64, 9000, "f32"),       # K = 64
+    (2, 8, 150000, "f32"),      # several load rounds per vocabulary chunk
+    (1, 4, 300000, "bf16"),
 ])
 def test_greedy_shapes(gpu_lib, B, K, V, dtype):
     rng = np.random.default_rng(B * 1000 + K)
@@ -70,8 +72,8 @@ def test_greedy_ties_across_chunks_and_signed_zero(gpu_lib):
 
 
 def test_greedy_workspace_reuse(gpu_lib):
-    """Back-to-back calls of different shapes share the cached workspace: each call must
-    leave its counters and keys zeroed."""
+    """Back-to-back calls of different shapes share the cached workspace, which carries
+    no state from one call to the next."""
     for i, (B, K, V) in enumerate([(2, 16, 3000), (8, 4, 500), (2, 16, 3000), (1, 64, 700)]):
         g = W.make_greedy(np.random.default_rng(50 + i), B=B, K=K, V=V, dtype="bf16")
         say(f"[greedy] reuse {i}")

@@ -3,7 +3,8 @@
 //
 // Launch 1 (row_lse_kernel), grid (8192-entry vocabulary chunk, row) over the B*K
 // target rows and the B*(K-1) draft rows: per chunk the maximum m_c of the raw logits
-// and s_c = sum exp((x - m_c) / T), fp32 exponentials accumulated in fp64.
+// and s_c = sum exp((x - m_c) / T), fp32 exponentials (the hardware exp2 unit)
+// accumulated in fp64.
 //
 // Launch 2 (sample_race_kernel), grid (1024-entry vocabulary chunk, sequence).  Every
 // workgroup combines the chunk partials into the row log-normalisers
@@ -133,10 +134,11 @@ __global__ void __launch_bounds__(kLseThreads) row_lse_kernel(const SampleParams
   m = redf[0];
 #pragma unroll
   for (int w = 1; w < kLseThreads / kWave; ++w) m = fmaxf(m, redf[w]);
-  const float it = static_cast<float>(p.inv_t);
+  // e^((x - m)/T) = 2^((x - m) * log2(e)/T) on the hardware exp unit
+  const float it2 = static_cast<float>(p.inv_t * 1.4426950408889634);
   double s = 0.0;
 #pragma unroll
-  for (int e = 0; e < kMaxPer; ++e) s += static_cast<double>(expf((v[e] - m) * it));
+  for (int e = 0; e < kMaxPer; ++e) s += static_cast<double>(fast_exp2((v[e] - m) * it2));
   s = wave_sum_f64(s);
   if ((tid & 63) == 0) redd[tid >> 6] = s;
   __syncthreads();
@@ -206,17 +208,27 @@ __global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParam
       p.target, (static_cast<size_t>(b) * K + tid) * p.V + dc)) : 0.0;
   const double lq = tester ? static_cast<double>(logit_at<kBF16>(
       p.draft, (static_cast<size_t>(b) * (K - 1) + tid) * p.V + dc)) : 0.0;
-  // ... and the log-normaliser of row tid (K target rows, then K-1 draft rows)
-  if (tid < 2 * K - 1) {
-    const int rho = tid < K ? b * K + tid : p.B * K + b * (K - 1) + (tid - K);
+  // ... and the log-normalisers of the K target rows, then the K-1 draft rows: lpr
+  // lanes (a power of two, aligned in the wave) share a row, each folding every lpr-th
+  // chunk partial, then combine by shuffles
+  {
+    const int nrows = 2 * K - 1;
+    int lpr = 1;
+    while (lpr * 2 * nrows <= kThreads && lpr < 16) lpr *= 2;
+    const int row = tid / lpr, sub = tid - row * lpr;
+    const bool has = row < nrows;
+    const int rr = has ? row : 0;
+    const int rho = rr < K ? b * K + rr : p.B * K + b * (K - 1) + (rr - K);
     const float* pm = p.part_m + static_cast<size_t>(rho) * p.nchunk;
     const double* ps = p.part_s + static_cast<size_t>(rho) * p.nchunk;
     float m = -INFINITY;
-    for (int q = 0; q < p.nchunk; ++q) m = fmaxf(m, pm[q]);
+    for (int q = sub; q < p.nchunk; q += lpr) m = fmaxf(m, pm[q]);
+    for (int o = 1; o < lpr; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
     double s = 0.0;
-    for (int q = 0; q < p.nchunk; ++q)
+    for (int q = sub; q < p.nchunk; q += lpr)
       s += ps[q] * exp((static_cast<double>(pm[q]) - static_cast<double>(m)) * it);
-    Lrow[tid] = static_cast<double>(m) * it + log(s);
+    for (int o = 1; o < lpr; o <<= 1) s += __shfl_xor(s, o);
+    if (has && sub == 0) Lrow[row] = static_cast<double>(m) * it + log(s);
   }
   __syncthreads();
 

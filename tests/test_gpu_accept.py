@@ -201,3 +201,22 @@ def test_commit_edges(gpu_lib):
         r_ctx, r_anchor = oracle.commit_ref(ctx, acc, toks)
         np.testing.assert_array_equal(ctx_dev.cpu().numpy(), r_ctx)
         np.testing.assert_array_equal(anchor.cpu().numpy(), r_anchor)
+
+
+def test_sample_a_thousand_sequence_cycles(gpu_lib):
+    """1,024 seeded sequence-cycles of the 72B block shape (K = 32) on a smaller
+    vocabulary: every accept length and token bit-exact; the smallest distance of any
+    uniform from its threshold and the smallest race gap are reported."""
+    rng = np.random.default_rng(4242)
+    margins, gaps, accepted = [], [], 0
+    for off in range(128):
+        s = W.make_sample(rng, B=8, K=32, V=3000, dtype="bf16", seed=0x5EED, offset=off)
+        if off % 32 == 0:
+            say(f"[sample] thousand cycles: offset {off}")
+        acc, m, gp = assert_sample(gpu_lib, s, f"offset {off}")
+        margins.append(m)
+        gaps.append(gp)
+        accepted += int(acc.sum())
+    say(f"  accepted drafts {accepted} over 1024 sequence-cycles; smallest margin "
+        f"{min(margins):.2e}, smallest race gap {min(gaps):.2e}")
+    assert accepted > 0

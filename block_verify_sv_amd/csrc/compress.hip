@@ -10,8 +10,8 @@
 // Pass 3 (out_kernel): grid (D/128 tile, b).  The workgroup streams F_b in 32-row tiles
 // through a register ring (several tiles in flight, each with its weight operands read
 // from the cache-resident workspace) into LDS as loaded; the contraction runs over the
-// feature rows, so each MFMA operand gathers 8 consecutive rows of one column with
-// 16-bit LDS reads.  out = W . F_b / rowsum accumulates on MFMA.
+// feature rows, so each MFMA operand (8 consecutive rows of one column) comes from two
+// LDS transpose reads.  out = W . F_b / rowsum accumulates on MFMA.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -24,7 +24,7 @@ constexpr int kSK = 64;                 // pass-1 contraction step (d per LDS ti
 constexpr int kSRing = 4;               // pass-1 register ring (kSRing - 1 steps in flight)
 constexpr int kNT = 32;                 // feature rows per pass-3 tile
 constexpr int kDT = 128;                // output columns per pass-3 workgroup
-constexpr int kRing = 6;                // pass-3 register ring (kRing - 1 tiles in flight)
+constexpr int kRing = 3;                // pass-3 register ring (kRing - 1 tiles in flight)
 
 __host__ __device__ __forceinline__ int pad_n(int N) { return (N + kNT - 1) / kNT * kNT; }
 
@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(kThreads) scores_kernel(const CompressParams p
       *reinterpret_cast<u32x4*>(&fl[loff[u]]) = t.f[u];
     }
     __syncthreads();                               // step st in LDS; st-1's buffer free
-    if (active) {
+    if (active && st < steps) {
 #pragma unroll
       for (int ks = 0; ks < kSK / 16; ++ks) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(&ql[(wc * 32 + l32) * ROW + ks * 16 + h * 8]);
@@ -92,14 +92,20 @@ __global__ void __launch_bounds__(kThreads) scores_kernel(const CompressParams p
   };
   ST ring[kSRing];
 #pragma unroll
-  for (int u = 0; u < kSRing - 1; ++u) load(ring[u], u);
+  // The prologue loads are kept in step order, and the loop runs whole groups of kSRing
+  // steps (past the last step: loads re-read it, the MFMAs are skipped).  The compiler's
+  // wait counts merge every path into the loop head: loads issued out of order, or an
+  // exit from the middle of a group, would make them drain the ring once per group.
+  for (int u = 0; u < kSRing - 1; ++u) {
+    load(ring[u], u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   for (int s0 = 0; s0 < steps; s0 += kSRing) {
 #pragma unroll
     for (int u = 0; u < kSRing; ++u) {
       const int st = s0 + u;
-      if (st >= steps) break;
       load(ring[(u + kSRing - 1) % kSRing], st + kSRing - 1);
-      step(ring[u], st);
+      step(ring[u], st);                         // past the last step: no MFMA
     }
   }
   const int n = n0 + wn * 32 + l32;
@@ -155,8 +161,20 @@ __global__ void __launch_bounds__(kThreads) softmax_kernel(const CompressParams 
   if (lane == 0) p.rowsum[b * kMaxC + c] = sum;
 }
 
+// LDS transpose read (gfx950): within each 16-lane group, lane i receives 16-bit element
+// i % 4 of the 8-byte rows addressed by lanes i/4, 4 + i/4, 8 + i/4 and 12 + i/4.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
-  constexpr int FROW = kDT + 8;                    // feature tile row (padded)
+  // feature tile row: kDT columns padded to 160 halves (80 banks), so the four rows one
+  // half-wave's transpose read touches start 16 banks apart
+  constexpr int FROW = 160;
+  static_assert(FROW >= kDT, "feature tile row");
   __shared__ __align__(16) uint16_t f_lds[2][kNT * FROW];
   __shared__ float rsum[kMaxC];
 
@@ -173,6 +191,11 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
   // straight from the workspace (cache-resident: every d tile of the image reads it).
   const int wc = wave >> 1, wd = wave & 1;
   const bool active = wc * 32 < p.C;
+  // transpose-read address of this lane: lane 4j + q of a 16-lane group points at row
+  // 8h + j, columns 16*(group & 1) + 4q .. +3, so lane i of the group receives rows
+  // 8h .. 8h+3 of column 16*(group & 1) + i: the MFMA B operand's layout
+  const int grp = lane >> 4, i16 = lane & 15;
+  const int tr_off = (h * 8 + (i16 >> 2)) * FROW + (grp & 1) * 16 + 4 * (i16 & 3);
   const uint16_t* wsrc = p.weights + (static_cast<size_t>(b) * kMaxC + wc * 32 + l32) * Nw + h * 8;
   f32x16 acc[2];
 #pragma unroll
@@ -205,19 +228,17 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
       *reinterpret_cast<u32x4*>(&fl[(ch >> 4) * FROW + (ch & 15) * 8]) = f.v[u];
     }
     __syncthreads();                               // tile t in LDS; tile t-1's buffer free
-    if (active) {
+    if (active && t < nt_count) {
 #pragma unroll
       for (int ks = 0; ks < kNT / 16; ++ks) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          // the operand's 8 consecutive feature rows of one column, gathered as 16-bit
-          // reads (consecutive lanes read consecutive columns: no bank conflicts)
-          const uint16_t* col = &fl[(ks * 16 + h * 8) * FROW + wd * 64 + tt * 32 + l32];
-          u32x4 bo;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            bo[q] = static_cast<uint32_t>(col[(2 * q) * FROW]) |
-                    (static_cast<uint32_t>(col[(2 * q + 1) * FROW]) << 16);
+          // the operand (feature rows 16ks + 8h .. +7 of one column) as two transpose
+          // reads of 4 rows each
+          const uint16_t* src = &fl[ks * 16 * FROW + wd * 64 + tt * 32 + tr_off];
+          const uint2 lo = lds_read_tr16(src);
+          const uint2 hi = lds_read_tr16(src + 4 * FROW);
+          const u32x4 bo = {lo.x, lo.y, hi.x, hi.y};
           acc[tt] = Mfma<TagF16>::step(f.a[ks], bo, acc[tt]);
         }
       }
@@ -225,14 +246,16 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
   };
   FT ring[kRing];
 #pragma unroll
-  for (int u = 0; u < kRing - 1; ++u) load(ring[u], u);
+  for (int u = 0; u < kRing - 1; ++u) {          // in tile order; whole groups (as in pass 1)
+    load(ring[u], u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   for (int t0 = 0; t0 < nt_count; t0 += kRing) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int t = t0 + u;
-      if (t >= nt_count) break;
       load(ring[(u + kRing - 1) % kRing], t + kRing - 1);
-      tile(ring[u], t);
+      tile(ring[u], t);                          // past the last tile: no MFMA
     }
   }
   if (!active) return;

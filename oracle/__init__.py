@@ -27,6 +27,10 @@ Every function follows a passage of the pages it cites:
 * ``kv.commit_ref`` -- closing a cycle: the context grows by the accepted drafts
   plus the anchor, and the target's correction becomes the next anchor (VFlash-FM
   page, caption of the cycle figure).
+* ``tree.accept_greedy_tree_ref`` / ``tree.tree_commit_ref`` -- greedy verification
+  of a draft tree (the "Tree-60" row of the VFlash-FM results table) read as the
+  chain rule walked from the anchor, and the commit that moves the accepted path's
+  K/V rows into place.
 
 Parity pins: every function is pinned in ``tests/test_oracle_*.py`` against
 something other than itself (worked example, library routine, closed form,
@@ -38,10 +42,11 @@ from .accept import accept_greedy_ref, sample_rule, accept_sample_ref, race_ref
 from .philox import philox4x64_10, uniforms, ACCEPT, RESAMPLE
 from .compress import latent_compress_ref
 from .kv import kv_append_ref, commit_ref
+from .tree import accept_greedy_tree_ref, tree_commit_ref
 
 __all__ = [
     "decode", "verify_attention_ref", "single_query_ref", "merge_partials_ref",
     "accept_greedy_ref", "sample_rule", "accept_sample_ref", "race_ref",
     "philox4x64_10", "uniforms", "ACCEPT", "RESAMPLE", "latent_compress_ref",
-    "kv_append_ref", "commit_ref",
+    "kv_append_ref", "commit_ref", "accept_greedy_tree_ref", "tree_commit_ref",
 ]

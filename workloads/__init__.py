@@ -24,6 +24,9 @@ Workloads (shapes taken from the pages' measurement setups):
 * ``qwen72b_sampling`` -- 72B-shaped sampling verify (64 q heads, 8 KV heads,
   d 128), bf16 KV of 25,000 context tokens, block 32, target logits ~ N(0,3),
   draft logits = bf16(target + N(0,1)), temperature 1.
+* ``qwen7b_tree60`` -- the 7B layer verifying a static draft tree of 60 nodes
+  below the anchor (the "Tree-60" variant of the VFlash-FM results table): 61
+  block rows with ancestor masks, planted greedy path through the tree.
 
 Conventions (fixed here, used by both sides):
 
@@ -55,7 +58,9 @@ __all__ = [
     "WORKLOADS", "bf16_bits", "bf16_bits_to_f32", "VerifyInputs", "GreedyInputs",
     "SampleInputs", "CompressInputs", "SarInputs", "make_verify", "make_greedy",
     "make_sample", "make_compress", "make_sar", "build_page_table", "causal_mask",
-    "all_ones_mask", "rng_for",
+    "all_ones_mask", "rng_for", "TreeInputs", "TREE60_LEVELS", "make_tree_topology",
+    "chain_topology", "tree_mask", "make_tree_greedy", "workload_tree",
+    "make_workload_tree",
 ]
 
 BASE_SEED = 1000
@@ -210,8 +215,9 @@ class GreedyInputs:
     planted_tok: np.ndarray    # int32 [B][K]: lowest-index maximum of each row
 
 
-def make_greedy(rng: np.random.Generator, *, B: int, K: int, V: int, dtype: str = "bf16",
-                std: float = 3.0) -> GreedyInputs:
+def _planted_logits(rng: np.random.Generator, B: int, K: int, V: int, dtype: str,
+                    std: float):
+    """Target logits [B][K][V] with one planted maximum per row (and planted ties)."""
     x = rng.standard_normal(size=(B, K, V), dtype=np.float32)
     x *= np.float32(std)
     np.clip(x, -PLANT_CLIP, PLANT_CLIP, out=x)
@@ -226,7 +232,12 @@ def make_greedy(rng: np.random.Generator, *, B: int, K: int, V: int, dtype: str 
             if tie[b, k] and t < V - 1:
                 j = t + 1 + int(tie_u[b, k] * (V - 1 - t))
                 x[b, k, min(j, V - 1)] = PLANT_VALUE
-    logits = _round_to(x, dtype)
+    return _round_to(x, dtype), tok
+
+
+def make_greedy(rng: np.random.Generator, *, B: int, K: int, V: int, dtype: str = "bf16",
+                std: float = 3.0) -> GreedyInputs:
+    logits, tok = _planted_logits(rng, B, K, V, dtype, std)
     L = np.minimum(rng.geometric(0.25, size=B) - 1, K - 1).astype(np.int32)
     drafts = rng.integers(0, V, size=(B, K - 1)).astype(np.int32)
     other = rng.integers(0, max(V - 1, 1), size=B).astype(np.int32)
@@ -240,6 +251,115 @@ def make_greedy(rng: np.random.Generator, *, B: int, K: int, V: int, dtype: str 
             o = int(other[b])
             drafts[b, n] = o if o < t else o + 1
     return GreedyInputs(B, K, V, dtype, logits, drafts, L, tok)
+
+
+# --------------------------------------------------------------------------- trees
+
+# Tree-60: 60 draft nodes below the anchor, by depth (a static draft tree of the kind
+# the VFlash-FM results table verifies as "Tree-60"; the level sizes are this module's
+# choice, the pages give only the node count).
+TREE60_LEVELS = (10, 20, 16, 8, 4, 2)
+
+
+def make_tree_topology(rng: np.random.Generator, levels=TREE60_LEVELS) -> np.ndarray:
+    """Parents int32 [n] of draft nodes 1..n (node 0 is the anchor).
+
+    Nodes are numbered level by level; each node of a level hangs under a uniformly
+    drawn node of the better-ranked half of the previous level (the anchor for level
+    1), so a parent always has a smaller number than its children.
+    """
+    parents = []
+    prev = [0]
+    nid = 1
+    for size in levels:
+        top = prev[:max(1, (len(prev) + 1) // 2)]
+        cur = []
+        for _ in range(size):
+            parents.append(top[int(rng.integers(0, len(top)))])
+            cur.append(nid)
+            nid += 1
+        prev = cur
+    return np.asarray(parents, dtype=np.int32)
+
+
+def chain_topology(n: int) -> np.ndarray:
+    """The chain as a tree: node i hangs under node i-1."""
+    return np.arange(n, dtype=np.int32)
+
+
+def tree_mask(parents) -> np.ndarray:
+    """Block-mask rows of a tree: row i sees node i and every ancestor of it."""
+    parents = np.asarray(parents)
+    K = len(parents) + 1
+    rows = [1]
+    for i in range(1, K):
+        rows.append((1 << i) | rows[int(parents[i - 1])])
+    return np.array(rows, dtype=np.uint64)
+
+
+@dataclass
+class TreeInputs:
+    B: int
+    K: int                     # nodes, anchor included
+    V: int
+    dtype: str
+    logits: np.ndarray         # [B][K][V]: target row of every node
+    parents: np.ndarray        # int32 [B][K-1]: parent of node i at [b][i-1]
+    tokens: np.ndarray         # int32 [B][K-1]: draft token of node i at [b][i-1]
+    planted_len: np.ndarray    # int32 [B]: accepted depth by construction
+    planted_path: np.ndarray   # int32 [B][K]: anchor, accepted nodes, then -1
+    planted_tok: np.ndarray    # int32 [B][K]: lowest-index maximum of each row
+
+
+def make_tree_greedy(rng: np.random.Generator, *, B: int, V: int, parents,
+                     dtype: str = "bf16", std: float = 3.0) -> TreeInputs:
+    """Planted target rows over a draft tree with a planted accepted path.
+
+    Siblings carry distinct tokens.  A Geometric(0.25) depth L is drawn per sequence;
+    from the anchor, L times (while the node has children) a uniformly drawn child
+    takes the planted maximum of its parent's row (trading tokens with the sibling
+    that held it), and finally no child of the last node keeps that node's maximum.
+    """
+    parents = np.asarray(parents, dtype=np.int32)
+    K = len(parents) + 1
+    logits, tok = _planted_logits(rng, B, K, V, dtype, std)
+    children = [[] for _ in range(K)]
+    for i in range(1, K):
+        children[int(parents[i - 1])].append(i)
+    tokens = np.zeros((B, K), dtype=np.int64)
+    for b in range(B):
+        for u in range(K):
+            if children[u]:
+                tokens[b, children[u]] = rng.choice(V, size=len(children[u]), replace=False)
+    L = rng.geometric(0.25, size=B) - 1
+    plen = np.zeros(B, dtype=np.int32)
+    path = np.full((B, K), -1, dtype=np.int32)
+    for b in range(B):
+        cur, depth = 0, 0
+        path[b, 0] = 0
+        while depth < L[b] and children[cur]:
+            ch = children[cur]
+            c = ch[int(rng.integers(0, len(ch)))]
+            want = int(tok[b, cur])
+            for sib in ch:
+                if tokens[b, sib] == want:
+                    tokens[b, sib] = tokens[b, c]
+            tokens[b, c] = want
+            cur = c
+            depth += 1
+            path[b, depth] = c
+        want = int(tok[b, cur])
+        taken = {int(tokens[b, s]) for s in children[cur]}
+        for s in children[cur]:
+            if tokens[b, s] == want:
+                t = int(rng.integers(0, V))
+                while t == want or t in taken:
+                    t = int(rng.integers(0, V))
+                tokens[b, s] = t
+                taken.add(t)
+        plen[b] = depth
+    return TreeInputs(B, K, V, dtype, logits, np.tile(parents, (B, 1)),
+                      tokens[:, 1:].astype(np.int32), plen, path, tok)
 
 
 # --------------------------------------------------------------------------- sampling
@@ -346,13 +466,25 @@ WORKLOADS = {
     "qwen72b_sampling": Workload("qwen72b_sampling", "64q/8kv d128 bf16, ctx 25000 + block 32",
                                  dict(B=1, K=32, Hq=64, Hkv=8, D=128, ctx=25000, V=152064,
                                       dtype="bf16", T=1.0)),
+    "qwen7b_tree60": Workload("qwen7b_tree60", "7B layer, ctx 25119 + Tree-60 (61 nodes), V 152064",
+                              dict(B=1, K=61, Hq=28, Hkv=4, D=128, ctx=25119, V=152064,
+                                   dtype="bf16", levels=TREE60_LEVELS)),
 }
+
+
+def workload_tree(name: str) -> np.ndarray:
+    """The static draft tree of a tree workload (parents of nodes 1..K-1)."""
+    return make_tree_topology(rng_for(name, 20_000), WORKLOADS[name].params["levels"])
 
 
 def make_workload_verify(name: str, cycle: int = 0) -> VerifyInputs:
     """Verify-attention inputs of a named workload (draw order: contexts, pages, Q, K, V)."""
     p = WORKLOADS[name].params
     rng = rng_for(name, cycle)
+    if name == "qwen7b_tree60":
+        return make_verify(rng, B=p["B"], K=p["K"], Hq=p["Hq"], Hkv=p["Hkv"], D=p["D"],
+                           ctx_lens=[p["ctx"]] * p["B"], P=16, dtype=p["dtype"],
+                           mask=tree_mask(workload_tree(name)))
     if name == "batched_paged":
         ctx = log_uniform_contexts(rng, p["B"])
         return make_verify(rng, B=p["B"], K=p["K"], Hq=p["Hq"], Hkv=p["Hkv"], D=p["D"],
@@ -372,3 +504,10 @@ def make_workload_sample(name: str, cycle: int = 0) -> SampleInputs:
     rng = rng_for(name, 10_000 + cycle)
     return make_sample(rng, B=p["B"], K=p["K"], V=p["V"], dtype=p["dtype"],
                        temperature=p["T"], seed=0x5EED, offset=cycle)
+
+
+def make_workload_tree(name: str, cycle: int = 0) -> TreeInputs:
+    p = WORKLOADS[name].params
+    rng = rng_for(name, 10_000 + cycle)
+    return make_tree_greedy(rng, B=p["B"], V=p["V"], parents=workload_tree(name),
+                            dtype=p["dtype"])

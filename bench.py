@@ -108,6 +108,9 @@ ROWS = {
     "compress": ("compressor_sar", "latent compressor, 32 images, D 4096, (C, N) = (64, 576)", 4),
     "compress_qwen": ("compressor_sar", "latent compressor, 32 images, D 4096, (C, N) = "
                       "(36, 324)", 4),
+    "attn_tree60": ("qwen7b_tree60", "verify attention with the Tree-60 mask (61 nodes, 427 "
+                    "rows per KV head), 7B layer, ctx 25,119", 12),
+    "tree60_accept": ("qwen7b_tree60", "greedy tree acceptance, 61 nodes over 152,064", 28),
 }
 
 
@@ -166,8 +169,24 @@ def run_row(args):
         shape = {"B": inp.B, "K": inp.K, "Hq": inp.Hq, "Hkv": inp.Hkv, "d": inp.D,
                  "ctx_sum": int(inp.ctx_lens.sum())}
 
+        mask = sv.mask_array(inp.mask) if wl == "qwen7b_tree60" else None
+
         def call(i, st):
-            sv.verify_attention_into(desc, q, ks[i], vs[i], pt, cl, out, lse, None, ws, st)
+            sv.verify_attention_into(desc, q, ks[i], vs[i], pt, cl, out, lse, mask, ws, st)
+    elif args.row == "tree60_accept":
+        ti = W.make_workload_tree(wl)
+        lg = [dev_t(ti.logits, ti.dtype)]
+        lg += [lg[0].clone() for _ in range(R - 1)]
+        par, tok = i32(ti.parents), i32(ti.tokens)
+        outs = (torch.empty(ti.B, dtype=torch.int32, device=dev),
+                torch.empty(ti.B, ti.K, dtype=torch.int32, device=dev),
+                torch.empty(ti.B, ti.K, dtype=torch.int32, device=dev), None)
+        sv.accept_greedy_tree(lg[0], par, tok, want_argmax=False, out=outs)
+        nbytes = lg[0].numel() * lg[0].element_size()
+        shape = {"B": ti.B, "K": ti.K, "V": ti.V}
+
+        def call(i, st):
+            sv.accept_greedy_tree(lg[i], par, tok, want_argmax=False, out=outs, stream=st)
     elif args.row == "sample_72b":
         smp = W.make_workload_sample(wl, 0)
         tl = [dev_t(smp.target_logits, smp.dtype)]

@@ -69,6 +69,10 @@ _SIGNATURES = {
     "sv_kv_append": (c_i32, [ctypes.POINTER(AttnDesc), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                              c_vp]),
     "sv_commit": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "sv_accept_greedy_tree": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                      c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "sv_commit_tree": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                               c_vp, c_vp, c_vp]),
 }
 
 
@@ -220,6 +224,39 @@ def accept_greedy(logits: torch.Tensor, drafts: torch.Tensor, want_argmax: bool 
     return acc, toks, am
 
 
+def accept_greedy_tree(logits: torch.Tensor, parents: torch.Tensor, tokens: torch.Tensor,
+                       want_argmax: bool = True, out=None, workspace=None, stream=None):
+    """Greedy acceptance over a draft tree (node 0 = anchor; parents/tokens [B][K-1] of
+    nodes 1..K-1).  Returns (accept_len [B], out_tokens [B][K], accept_path [B][K],
+    argmax [B][K] or None)."""
+    _require(logits, "logits")
+    _require(parents, "parents", torch.int32)
+    _require(tokens, "tokens", torch.int32)
+    B, K, V = logits.shape
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise SvError("greedy logits must be float32 or bfloat16")
+    if tuple(parents.shape) != (B, K - 1) or tuple(tokens.shape) != (B, K - 1):
+        raise SvError(f"parents and tokens must be [B][K-1] = {(B, K - 1)}")
+    lib = load()
+    n = c_sz()
+    _check(lib.sv_accept_greedy_workspace(B, K, V, ctypes.byref(n)), "sv_accept_greedy_workspace")
+    if workspace is None:
+        workspace = _workspace("greedy", n.value, logits.device, zero=True)
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=logits.device)
+        toks = torch.empty(B, K, dtype=torch.int32, device=logits.device)
+        path = torch.empty(B, K, dtype=torch.int32, device=logits.device)
+        am = torch.empty(B, K, dtype=torch.int32, device=logits.device) if want_argmax else None
+    else:
+        acc, toks, path, am = out
+    _check(lib.sv_accept_greedy_tree(B, K, V, _DTYPES[logits.dtype], _ptr(logits),
+                                     _ptr(parents), _ptr(tokens), _ptr(acc), _ptr(toks),
+                                     _ptr(path), _ptr(am), _ptr(workspace), workspace.numel(),
+                                     _stream(stream)),
+           "sv_accept_greedy_tree")
+    return acc, toks, path, am
+
+
 def accept_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, drafts: torch.Tensor,
                   temperature: float, seed: int, offset: int, out=None, workspace=None,
                   stream=None):
@@ -313,4 +350,34 @@ def commit(accept_len: torch.Tensor, out_tokens: torch.Tensor, ctx_lens: torch.T
     _check(load().sv_commit(B, K, _ptr(accept_len), _ptr(out_tokens), _ptr(ctx_lens),
                             _ptr(next_anchor), _stream(stream)),
            "sv_commit")
+    return next_anchor
+
+
+def commit_tree(accept_len: torch.Tensor, out_tokens: torch.Tensor, accept_path: torch.Tensor,
+                page_table: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                ctx_lens: torch.Tensor, next_anchor: torch.Tensor = None,
+                stream=None) -> torch.Tensor:
+    """Close a tree cycle on the device: move the accepted path's K/V rows to
+    ctx+1 .. ctx+a, then ctx_lens += accept_len + 1 (in place); returns the next anchors."""
+    for name, t in (("accept_len", accept_len), ("out_tokens", out_tokens),
+                    ("accept_path", accept_path), ("page_table", page_table),
+                    ("ctx_lens", ctx_lens)):
+        _require(t, name, torch.int32)
+    _require(k_cache, "k_cache")
+    _require(v_cache, "v_cache", k_cache.dtype)
+    B, K = out_tokens.shape
+    num_pages, Hkv, P, D = k_cache.shape
+    if (accept_len.numel() != B or ctx_lens.numel() != B or tuple(accept_path.shape) != (B, K)
+            or page_table.shape[0] != B or tuple(v_cache.shape) != (num_pages, Hkv, D, P)):
+        raise SvError("commit_tree shape mismatch")
+    if next_anchor is None:
+        next_anchor = torch.empty(B, dtype=torch.int32, device=out_tokens.device)
+    _require(next_anchor, "next_anchor", torch.int32)
+    desc = AttnDesc(B, K, Hkv, Hkv, D, P, page_table.shape[1], num_pages, 0, 0, 0.0,
+                    _DTYPES[k_cache.dtype], 0)
+    _check(load().sv_commit_tree(ctypes.byref(desc), _ptr(accept_len), _ptr(out_tokens),
+                                 _ptr(accept_path), _ptr(page_table), _ptr(k_cache),
+                                 _ptr(v_cache), _ptr(ctx_lens), _ptr(next_anchor),
+                                 _stream(stream)),
+           "sv_commit_tree")
     return next_anchor

@@ -9,7 +9,8 @@
 // plain store per (row, chunk).  The walk pass has one wave per sequence: it reduces
 // the K rows' chunk keys (an order-independent maximum), and a ballot over the lanes
 // whose draft differs from the target's choice gives the accepted length.  The kernel
-// boundary orders the two; the workspace carries no state between calls.
+// boundary orders the two; the workspace carries no state between calls.  A draft tree
+// uses the same argmax pass and a walk from the anchor through the tree (see below).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -114,6 +115,58 @@ __global__ void __launch_bounds__(kThreads) greedy_walk_kernel(const GreedyParam
   if (lane == 0) p.accept_len[b] = a;
 }
 
+// Tree walk (a draft tree verified greedily: the chain rule walked from the anchor).
+// One wave per sequence; lane i holds node i's greedy token, parent and draft token.
+// From the anchor, a ballot over the lanes that hang under the current node, are
+// numbered above it and hold its greedy token picks the lowest such lane as the next
+// node.  Each step raises the node number, so the walk ends within K-1 steps whatever
+// the parent array holds.
+__global__ void __launch_bounds__(kThreads) greedy_tree_walk_kernel(const GreedyParams p) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * kWalkSeqs + (threadIdx.x >> 6);
+  if (b >= p.B) return;                           // whole waves
+  const int K = p.K;
+  const bool in = lane < K;
+  const unsigned long long* keys = p.keys + static_cast<size_t>(b) * K * p.nchunk;
+  uint64_t best = 0;
+  if (in) {
+    uint64_t k[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      k[c] = keys[static_cast<size_t>(lane) * p.nchunk + min(c, p.nchunk - 1)];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) best = k[c] > best ? k[c] : best;
+  }
+  int32_t t = -1;
+  if (in) {
+    t = static_cast<int32_t>(argmax_key_index(best));
+    if (p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
+  }
+  const bool node = lane >= 1 && lane < K;        // a draft node
+  const size_t nb = static_cast<size_t>(b) * (K - 1) + (lane - 1);
+  const int32_t par = node ? p.parents[nb] : -1;
+  const int32_t tok = node ? p.drafts[nb] : 0;
+  int cur = 0, a = 0;
+  int32_t my_path = lane == 0 ? 0 : -1;           // lane j ends up holding path[j]
+  for (int step = 1; step < K; ++step) {
+    const int32_t want = __shfl(t, cur);
+    const uint64_t hit = __ballot(node && lane > cur && par == cur && tok == want);
+    if (!hit) break;
+    cur = __builtin_ctzll(hit);
+    a = step;
+    if (lane == step) my_path = cur;
+  }
+  const int32_t next_node = __shfl(my_path, lane < 63 ? lane + 1 : 63);   // path[j+1]
+  const int32_t next_tok = __shfl(tok, next_node > 0 ? next_node : 0);
+  const int32_t corr = __shfl(t, cur);
+  if (in) {
+    const size_t o = static_cast<size_t>(b) * K + lane;
+    p.out_tokens[o] = lane < a ? next_tok : (lane == a ? corr : -1);
+    p.path[o] = my_path;
+  }
+  if (lane == 0) p.accept_len[b] = a;
+}
+
 }  // namespace
 
 size_t greedy_workspace_bytes(int B, int K) {
@@ -136,8 +189,12 @@ hipError_t launch_greedy(const GreedyParams& p, sv_dtype dtype, hipStream_t stre
     hipLaunchKernelGGL(greedy_argmax_kernel<false>, grid, dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(greedy_walk_kernel, dim3((p.B + kWalkSeqs - 1) / kWalkSeqs), dim3(kThreads),
-                     0, stream, p);
+  if (p.tree)
+    hipLaunchKernelGGL(greedy_tree_walk_kernel, dim3((p.B + kWalkSeqs - 1) / kWalkSeqs),
+                       dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(greedy_walk_kernel, dim3((p.B + kWalkSeqs - 1) / kWalkSeqs),
+                       dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

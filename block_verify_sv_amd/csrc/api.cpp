@@ -60,8 +60,8 @@ sv_status check_attn_desc(const sv_attn_desc* d) {
                 d->num_q_heads, d->num_kv_heads);
   const int G = d->num_q_heads / d->num_kv_heads;
   if (d->block * G > sv::kMaxRows)
-    return fail(SV_ERR_INVALID_ARG, "block * (num_q_heads / num_kv_heads) = %d exceeds 256",
-                d->block * G);
+    return fail(SV_ERR_INVALID_ARG, "block * (num_q_heads / num_kv_heads) = %d exceeds %d",
+                d->block * G, sv::kMaxRows);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(SV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
   if (d->dtype != SV_F32 && d->dtype != SV_BF16 && d->dtype != SV_F16)
@@ -99,7 +99,7 @@ AttnPlan plan_attention(const sv_attn_desc& d) {
   AttnPlan pl;
   const int64_t n_max = static_cast<int64_t>(d.max_ctx) + d.block;
   pl.rows = d.block * (d.num_q_heads / d.num_kv_heads);
-  pl.row_halves = pl.rows > 128 ? 2 : 1;         // a workgroup holds 4 row blocks of 32
+  pl.row_halves = (pl.rows + 127) / 128;         // a workgroup holds 4 row blocks of 32
   int64_t chunk = d.split_keys;
   if (chunk == 0) {
     // one workgroup per compute unit: total (context + block) keys over all KV heads and
@@ -233,10 +233,12 @@ sv_status sv_accept_greedy_workspace(int32_t B, int32_t K, int32_t V, size_t* by
   return ok();
 }
 
-sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
-                           const void* logits, const int32_t* drafts, int32_t* accept_len,
-                           int32_t* out_tokens, int32_t* argmax, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+// The chain (parents == nullptr) and the tree walk share the argmax pass.
+static sv_status greedy_call(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                             const void* logits, const int32_t* drafts, const int32_t* parents,
+                             int32_t* path, int32_t* accept_len, int32_t* out_tokens,
+                             int32_t* argmax, void* workspace, size_t workspace_bytes,
+                             void* stream, const char* what) {
   sv_status st = check_accept_shape(B, K, V, 1);
   if (st != SV_OK) return st;
   if (logit_dtype != SV_F32 && logit_dtype != SV_BF16)
@@ -252,6 +254,9 @@ sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
   sv::GreedyParams p;
   p.logits = logits;
   p.drafts = drafts;
+  p.parents = parents;
+  p.path = path;
+  p.tree = path != nullptr;
   p.accept_len = accept_len;
   p.out_tokens = out_tokens;
   p.argmax = argmax;
@@ -263,8 +268,28 @@ sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
   p.nchunk = (V + p.chunk - 1) / p.chunk;
   if (static_cast<int64_t>(p.nchunk) * K >= (1ll << 31))
     return fail(SV_ERR_INVALID_ARG, "V too large");
-  return device_status(sv::launch_greedy(p, logit_dtype, static_cast<hipStream_t>(stream)),
-                       "sv_accept_greedy launch");
+  return device_status(sv::launch_greedy(p, logit_dtype, static_cast<hipStream_t>(stream)), what);
+}
+
+sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                           const void* logits, const int32_t* drafts, int32_t* accept_len,
+                           int32_t* out_tokens, int32_t* argmax, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return greedy_call(B, K, V, logit_dtype, logits, drafts, nullptr, nullptr, accept_len,
+                     out_tokens, argmax, workspace, workspace_bytes, stream,
+                     "sv_accept_greedy launch");
+}
+
+sv_status sv_accept_greedy_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                                const void* logits, const int32_t* parents,
+                                const int32_t* tokens, int32_t* accept_len,
+                                int32_t* out_tokens, int32_t* accept_path, int32_t* argmax,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (K > 1 && !parents) return fail(SV_ERR_INVALID_ARG, "parents is required");
+  if (!accept_path) return fail(SV_ERR_INVALID_ARG, "accept_path is required");
+  return greedy_call(B, K, V, logit_dtype, logits, tokens, parents, accept_path, accept_len,
+                     out_tokens, argmax, workspace, workspace_bytes, stream,
+                     "sv_accept_greedy_tree launch");
 }
 
 // ---------------------------------------------------------------- sampling
@@ -430,6 +455,57 @@ sv_status sv_commit(int32_t B, int32_t K, const int32_t* accept_len, const int32
   p.B = B;
   p.K = K;
   return device_status(sv::launch_commit(p, static_cast<hipStream_t>(stream)), "sv_commit launch");
+}
+
+sv_status sv_commit_tree(const sv_attn_desc* desc, const int32_t* accept_len,
+                         const int32_t* out_tokens, const int32_t* accept_path,
+                         const int32_t* page_table, void* k_cache, void* v_cache,
+                         int32_t* ctx_lens, int32_t* next_anchor, void* stream) {
+  if (!desc) return fail(SV_ERR_INVALID_ARG, "desc is NULL");
+  const int B = desc->batch, K = desc->block;
+  if (B < 1 || B > 65535) return fail(SV_ERR_INVALID_ARG, "batch out of range");
+  if (K < 1 || K > sv::kMaxBlock) return fail(SV_ERR_INVALID_ARG, "block must be in [1, 64] (got %d)", K);
+  if (desc->num_kv_heads < 1 || desc->num_kv_heads > 65535)
+    return fail(SV_ERR_INVALID_ARG, "num_kv_heads out of range");
+  if (desc->head_dim != 64 && desc->head_dim != 128)
+    return fail(SV_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!pow2(desc->page_size) || desc->page_size < 16 || desc->page_size > 256)
+    return fail(SV_ERR_INVALID_ARG, "page_size must be a power of two in [16, 256]");
+  if (desc->max_pages_per_seq < 1 || desc->num_pages < 1)
+    return fail(SV_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
+  if (desc->dtype != SV_F32 && desc->dtype != SV_BF16 && desc->dtype != SV_F16)
+    return fail(SV_ERR_UNSUPPORTED, "unknown dtype");
+  if (!accept_len || !out_tokens || !accept_path || !page_table || !k_cache || !v_cache ||
+      !ctx_lens || !next_anchor)
+    return fail(SV_ERR_INVALID_ARG, "all arrays are required");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K > 1) {
+    sv::TreeCompactParams t;
+    t.accept_len = accept_len;
+    t.path = accept_path;
+    t.ctx_lens = ctx_lens;
+    t.page_table = page_table;
+    t.k_cache = k_cache;
+    t.v_cache = v_cache;
+    t.B = B;
+    t.K = K;
+    t.Hkv = desc->num_kv_heads;
+    t.D = desc->head_dim;
+    t.P_log2 = log2i(desc->page_size);
+    t.max_pages = desc->max_pages_per_seq;
+    t.num_pages = desc->num_pages;
+    t.esz = desc->dtype == SV_F32 ? 4 : 2;
+    const sv_status st = device_status(sv::launch_tree_compact(t, s), "sv_commit_tree launch");
+    if (st != SV_OK) return st;
+  }
+  sv::CommitParams p;
+  p.accept_len = accept_len;
+  p.out_tokens = out_tokens;
+  p.ctx_lens = ctx_lens;
+  p.next_anchor = next_anchor;
+  p.B = B;
+  p.K = K;
+  return device_status(sv::launch_commit(p, s), "sv_commit_tree launch");
 }
 
 }  // extern "C"

@@ -102,15 +102,15 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   const int l32 = lane & 31;
   const int rg = wave % RG;                      // row group: row blocks rg + RG*t
   const int kh = wave / RG;                      // key part of each tile
-  // blockIdx.x = half * nsplit_pad + s: the row halves of one split are nsplit_pad (a
-  // multiple of 8) workgroups apart, so round-robin dispatch puts both on one XCD and
-  // the second read of each KV tile comes from that XCD's L2
-  const int half = blockIdx.x / p.nsplit_pad;
-  const int s = blockIdx.x - half * p.nsplit_pad;
+  // blockIdx.x = rgroup * nsplit_pad + s: the row groups of 128 rows of one split are
+  // nsplit_pad (a multiple of 8) workgroups apart, so round-robin dispatch puts them on
+  // one XCD and the later reads of each KV tile come from that XCD's L2
+  const int rgroup = blockIdx.x / p.nsplit_pad;
+  const int s = blockIdx.x - rgroup * p.nsplit_pad;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   if (s >= p.nsplit) return;                     // padding of the split index
-  const int rb0 = half * RG * NRB;               // first row block of this half
+  const int rb0 = rgroup * RG * NRB;               // first row block of this row group
 
   // ---- start-up.  Nothing below needs the context length until the early-exit test,
   // so every independent load is issued before the first wait and they share one round

@@ -20,7 +20,70 @@ __global__ void __launch_bounds__(kThreads) commit_kernel(const CommitParams p) 
   p.ctx_lens[b] += a + 1;
 }
 
+// Tree commit, before the commit above: the block was appended in node order at
+// ctx .. ctx+K-1, and the accepted path's rows move to ctx+1 .. ctx+a (the j-th path node
+// from ctx + path[j] to ctx + j; the anchor stays).  One workgroup per (KV head,
+// sequence), one thread per element of a K row and of a V column.  Every source row is
+// read (into LDS) before any destination is written, so a destination that is also a
+// later node's source is never overwritten early.  Positions outside the page table and
+// table entries outside the pool are skipped.
+template <typename T>
+__global__ void __launch_bounds__(128) tree_compact_kernel(const TreeCompactParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* const ks = reinterpret_cast<T*>(smem);      // [K-1][D]
+  T* const vs = ks + static_cast<size_t>(p.K - 1) * p.D;
+  const int g = blockIdx.x, b = blockIdx.y, x = threadIdx.x;
+  if (x >= p.D) return;
+  int a = p.accept_len[b];
+  a = a < 0 ? 0 : (a > p.K - 1 ? p.K - 1 : a);
+  const int ctx = p.ctx_lens[b];
+  if (ctx < 0 || static_cast<int64_t>(ctx) + p.K > (static_cast<int64_t>(p.max_pages) << p.P_log2))
+    return;
+  const int Pm1 = (1 << p.P_log2) - 1;
+  const int32_t* table = p.page_table + static_cast<size_t>(b) * p.max_pages;
+  const int32_t* path = p.path + static_cast<size_t>(b) * p.K;
+  T* const kc = static_cast<T*>(p.k_cache);
+  T* const vc = static_cast<T*>(p.v_cache);
+  auto k_at = [&](int page, int slot) {
+    return (static_cast<size_t>(page * p.Hkv + g) * (Pm1 + 1) + slot) * p.D + x;
+  };
+  auto v_at = [&](int page, int slot) {
+    return (static_cast<size_t>(page * p.Hkv + g) * p.D + x) * (Pm1 + 1) + slot;
+  };
+  auto page_of = [&](int pos) {
+    const int pg = table[pos >> p.P_log2];
+    return (pg >= 0 && pg < p.num_pages) ? pg : -1;
+  };
+  for (int j = 1; j <= a; ++j) {
+    const int node = path[j];
+    if (node <= j || node >= p.K) continue;       // in place, or not a path node
+    const int src = ctx + node;
+    const int pg = page_of(src);
+    if (pg < 0) continue;
+    ks[(j - 1) * p.D + x] = kc[k_at(pg, src & Pm1)];
+    vs[(j - 1) * p.D + x] = vc[v_at(pg, src & Pm1)];
+  }
+  for (int j = 1; j <= a; ++j) {
+    const int node = path[j];
+    if (node <= j || node >= p.K) continue;
+    const int src = ctx + node, dst = ctx + j;
+    const int ps = page_of(src), pd = page_of(dst);
+    if (ps < 0 || pd < 0) continue;
+    kc[k_at(pd, dst & Pm1)] = ks[(j - 1) * p.D + x];
+    vc[v_at(pd, dst & Pm1)] = vs[(j - 1) * p.D + x];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tree_compact(const TreeCompactParams& p, hipStream_t stream) {
+  const size_t lds = 2 * static_cast<size_t>(p.K - 1) * p.D * p.esz;
+  if (p.esz == 4)
+    hipLaunchKernelGGL(tree_compact_kernel<uint32_t>, dim3(p.Hkv, p.B), dim3(128), lds, stream, p);
+  else
+    hipLaunchKernelGGL(tree_compact_kernel<uint16_t>, dim3(p.Hkv, p.B), dim3(128), lds, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_commit(const CommitParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(commit_kernel, dim3((p.B + kThreads - 1) / kThreads), dim3(kThreads), 0,

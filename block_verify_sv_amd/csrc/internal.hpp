@@ -11,7 +11,7 @@ namespace sv {
 
 constexpr int kNumCUs = 256;      // MI355X compute units (8 XCDs x 32)
 constexpr int kMaxBlock = 64;     // K limit (one uint64 mask row per block row)
-constexpr int kMaxRows = 256;     // K * G limit of one KV-head tile
+constexpr int kMaxRows = 512;     // K * G limit of one KV head (4 row groups of 128)
 constexpr int kMaxSplitKeys = 16384;  // keys of one split-KV work item
 
 // ---------------------------------------------------------------- verify attention
@@ -31,7 +31,7 @@ struct AttnParams {
   int32_t chunk;        // keys per split
   int32_t nsplit;       // splits allocated per (b, g)
   int32_t nsplit_pad;   // nsplit rounded up to a multiple of 8 (grid spacing of halves)
-  int32_t row_halves;   // 1, or 2 when K*G > 128 rows (each half: 4 row blocks)
+  int32_t row_halves;   // row groups of 128 rows (4 row blocks each): ceil(K*G / 128)
   float scale_log2;     // scale * log2(e)
   uint64_t mask[kMaxBlock];
 };
@@ -52,7 +52,10 @@ hipError_t launch_attention(const AttnParams& p, int head_dim, sv_dtype dtype,
 // ---------------------------------------------------------------- greedy accept
 struct GreedyParams {
   const void* logits;
-  const int32_t* drafts;
+  const int32_t* drafts;      // chain: d_1 .. d_{K-1}; tree: the token of nodes 1 .. K-1
+  const int32_t* parents;     // tree: parent of nodes 1 .. K-1
+  int32_t* path;              // tree: accepted path [B][K]
+  int32_t tree;               // 1: walk a draft tree, 0: a chain
   int32_t* accept_len;
   int32_t* out_tokens;
   int32_t* argmax;
@@ -129,5 +132,18 @@ struct CommitParams {
 };
 
 hipError_t launch_commit(const CommitParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------- tree commit
+struct TreeCompactParams {
+  const int32_t* accept_len;
+  const int32_t* path;        // [B][K]
+  const int32_t* ctx_lens;
+  const int32_t* page_table;
+  void* k_cache;
+  void* v_cache;
+  int32_t B, K, Hkv, D, P_log2, max_pages, num_pages, esz;
+};
+
+hipError_t launch_tree_compact(const TreeCompactParams& p, hipStream_t stream);
 
 }  // namespace sv

@@ -16,6 +16,8 @@
  *   sv_latent_compress   softmax(C . F^T) . F latent visual compressor
  *   sv_kv_append         write new K/V rows into the paged cache
  *   sv_commit            close a cycle: grow the context, pick the next anchor
+ *   sv_accept_greedy_tree  greedy verification of a draft tree (walk from the anchor)
+ *   sv_commit_tree       close a tree cycle: move the accepted path's K/V into place
  *
  * Conventions for every call
  *   - Array arguments are DEVICE pointers unless stated otherwise.  The caller
@@ -85,7 +87,7 @@ const char* sv_last_error(void);
  *   out        [B][K][Hq][d]               dtype (round to nearest even from fp32)
  *   lse        [B][K][Hq]                  fp32, optional (NULL = not written)
  *
- * Limits: 1 <= K <= 64; Hq % Hkv == 0; K * G <= 256; d in {64, 128}; P a power of two
+ * Limits: 1 <= K <= 64; Hq % Hkv == 0; K * G <= 512; d in {64, 128}; P a power of two
  * in [16, 256]; every block_mask row i must contain bit i and no bit >= K.
  * ctx_lens[b] must lie in [0, max_ctx] and ctx_lens[b] + K <= max_pages_per_seq * P.
  * Device-side, keys beyond max_ctx + K and table entries outside [0, num_pages) are
@@ -204,6 +206,47 @@ sv_status sv_kv_append(const sv_attn_desc* desc, int32_t n, const void* k_new,
  * ------------------------------------------------------------------------------------ */
 sv_status sv_commit(int32_t B, int32_t K, const int32_t* accept_len, const int32_t* out_tokens,
                     int32_t* ctx_lens, int32_t* next_anchor, void* stream);
+
+/* -------------------------------------------------------------------------------------
+ * Draft trees (the tree-verified "Tree-60" variant of the VFlash-FM results table).
+ * Node 0 is the anchor (block row 0); nodes 1 .. K-1 carry the drafts, and a parent has
+ * a smaller number than its children.  The block is appended in node order and verified
+ * with sv_verify_attention using the tree's mask rows (row i: bit j set iff node j is
+ * node i or an ancestor of it), so row i is the target's prediction after node i.
+ *
+ * Greedy tree acceptance: the chain rule walked from the anchor.  At the current node,
+ * the child (numbered above it) whose token equals the target's greedy token of the
+ * current node's row is accepted and becomes the current node -- the lowest-numbered
+ * one if several siblings share that token; the walk stops at the first node with no
+ * such child, whose greedy token is the correction.
+ *   logits [B][K][V] (SV_F32 or SV_BF16); parents [B][K-1], tokens [B][K-1] int32:
+ *   parent and draft token of node i at [b][i-1].
+ *   accept_len [B]: accepted depth a; out_tokens [B][K]: the accepted nodes' tokens, then
+ *   the correction, then -1; accept_path [B][K]: 0, the accepted nodes, then -1;
+ *   argmax [B][K] optional.  Workspace: sv_accept_greedy_workspace(B, K, V) bytes.
+ * A parent array that is not a tree (parent >= node) never makes the walk leave [0, K)
+ * or run more than K-1 steps; such nodes are simply never reached.
+ * Limits as for sv_accept_greedy.
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_accept_greedy_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                                const void* logits, const int32_t* parents,
+                                const int32_t* tokens, int32_t* accept_len,
+                                int32_t* out_tokens, int32_t* accept_path, int32_t* argmax,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tree commit: per sequence b with a = accept_len[b] (clamped to [0, K-1]) and
+ * K = desc->block, the K/V rows of the j-th accepted node move from position
+ * ctx + accept_path[b][j] to ctx + j (j = 1 .. a; every source is read before any
+ * destination is written), then as sv_commit: next_anchor[b] = out_tokens[b][a] and
+ * ctx_lens[b] += a + 1.  desc gives B, K, Hkv, d, P, the table stride, the pool size and
+ * the dtype of the caches (laid out as for sv_verify_attention).  Sequences whose
+ * ctx_lens[b] + K exceeds the page table, and table entries outside [0, num_pages), move
+ * nothing.  All device pointers; no workspace.
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_commit_tree(const sv_attn_desc* desc, const int32_t* accept_len,
+                         const int32_t* out_tokens, const int32_t* accept_path,
+                         const int32_t* page_table, void* k_cache, void* v_cache,
+                         int32_t* ctx_lens, int32_t* next_anchor, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert lib.sv_version() == 1
@@ -161,6 +161,35 @@ def test_commit_validation(lib):
     assert lib.sv_commit(4, 65, FAKE, FAKE, FAKE, FAKE, None) == INVALID
     assert lib.sv_commit(4, 16, FAKE, None, FAKE, FAKE, None) == INVALID
     assert lib.sv_commit(4, 16, FAKE, FAKE, FAKE, None, None) == INVALID
+
+
+def test_row_limit(lib):
+    """A KV head holds up to 512 query rows (4 groups of 128): Tree-60 at the 7B shape
+    (61 nodes x 7 query heads = 427 rows) is accepted, 64 x 9 = 576 rows are not."""
+    st, n = _ws(lib, _desc(block=61, max_pages_per_seq=1574, num_pages=1574))
+    assert st == OK and n > 0
+    st, _ = _ws(lib, _desc(block=64, num_q_heads=36))
+    assert st == INVALID and "512" in lib.sv_last_error().decode()
+
+
+def test_tree_validation(lib):
+    call = lambda dt, par, path, ws: lib.sv_accept_greedy_tree(
+        1, 61, 1000, dt, FAKE, par, FAKE, FAKE, FAKE, path, None, ws, 1 << 20, None)
+    assert call(sv.SV_BF16, None, FAKE, FAKE) == INVALID          # no parents
+    assert call(sv.SV_BF16, FAKE, None, FAKE) == INVALID          # no path output
+    assert call(sv.SV_F16, FAKE, FAKE, FAKE) == UNSUPPORTED
+    assert call(sv.SV_BF16, FAKE, FAKE, None) == WORKSPACE
+    assert lib.sv_accept_greedy_tree(1, 65, 1000, sv.SV_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      None, FAKE, 1 << 20, None) == INVALID
+    d = _desc(block=61, max_pages_per_seq=1574, num_pages=1574)
+    arrays = [FAKE] * 8
+    assert lib.sv_commit_tree(None, *arrays, None) == INVALID
+    assert lib.sv_commit_tree(ctypes.byref(_desc(block=65)), *arrays, None) == INVALID
+    assert lib.sv_commit_tree(ctypes.byref(_desc(head_dim=96)), *arrays, None) == UNSUPPORTED
+    for i in range(8):
+        a = list(arrays)
+        a[i] = None
+        assert lib.sv_commit_tree(ctypes.byref(d), *a, None) == INVALID
 
 
 def test_status_strings(lib):

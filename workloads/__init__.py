@@ -27,6 +27,9 @@ Workloads (shapes taken from the pages' measurement setups):
 * ``qwen7b_tree60`` -- the 7B layer verifying a static draft tree of 60 nodes
   below the anchor (the "Tree-60" variant of the VFlash-FM results table): 61
   block rows with ancestor masks, planted greedy path through the tree.
+* ``qwen7b_lmhead`` -- the 7B target's LM head over the block: 16 hidden states of
+  width 3584 against a 152,064 x 3584 bf16 output embedding ~ N(0, 0.02), each
+  hidden state steered to a planted token, drafts with a planted prefix.
 
 Conventions (fixed here, used by both sides):
 
@@ -60,7 +63,7 @@ __all__ = [
     "make_sample", "make_compress", "make_sar", "build_page_table", "causal_mask",
     "all_ones_mask", "rng_for", "TreeInputs", "TREE60_LEVELS", "make_tree_topology",
     "chain_topology", "tree_mask", "make_tree_greedy", "workload_tree",
-    "make_workload_tree",
+    "make_workload_tree", "LmHeadInputs", "make_lm_head", "make_workload_lm_head",
 ]
 
 BASE_SEED = 1000
@@ -73,8 +76,14 @@ TIE_FRACTION = 0.25      # rows that repeat the planted maximum at a later index
 
 def bf16_bits(x) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round to nearest even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    if u.size and int(u.max()) >= 0xFFFF8000:   # negative NaN payloads: widen to 64 bits
+        w = u.astype(np.uint64)
+        return ((w + 0x7FFF + ((w >> 16) & 1)) >> 16).astype(np.uint16)
+    r = (u >> 16) & 1                           # round half to even, in place
+    r += 0x7FFF
+    r += u
+    r >>= 16
     return r.astype(np.uint16)
 
 
@@ -362,6 +371,54 @@ def make_tree_greedy(rng: np.random.Generator, *, B: int, V: int, parents,
                       tokens[:, 1:].astype(np.int32), plen, path, tok)
 
 
+# --------------------------------------------------------------------------- LM head
+
+@dataclass
+class LmHeadInputs:
+    B: int
+    K: int
+    hidden: int
+    V: int
+    dtype: str                 # "bf16"
+    hidden_states: np.ndarray  # [B][K][hidden]: the verify pass's last hidden states
+    weight: np.ndarray         # [V][hidden]: the LM head (output embedding)
+    drafts: np.ndarray         # int32 [B][K-1]
+    planted_len: np.ndarray    # int32 [B]
+    planted_tok: np.ndarray    # int32 [B][K]: the token each row is steered to
+
+
+def make_lm_head(rng: np.random.Generator, *, B: int, K: int, hidden: int, V: int,
+                 dtype: str = "bf16", w_std: float = 0.02, margin: float = 20.0,
+                 chunk: int = 1 << 14) -> LmHeadInputs:
+    """Random LM head W ~ N(0, w_std) [V][hidden]; hidden state of row i =
+    s * W[t_i] + N(0, 1) with s = margin / (hidden * w_std^2), which puts the planted
+    token t_i's logit near `margin` while the others stay within a few units of 0; drafts
+    follow the planted tokens for a Geometric(0.25) prefix, as for planted logits."""
+    steer = margin / (hidden * w_std * w_std)
+    w = np.empty((V, hidden), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    for v0 in range(0, V, chunk):                  # drawn in row chunks, in order
+        v1 = min(V, v0 + chunk)
+        part = rng.standard_normal(size=(v1 - v0, hidden), dtype=np.float32)
+        part *= np.float32(w_std)
+        w[v0:v1] = _round_to(part, dtype)
+    tok = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    wf = bf16_bits_to_f32(w[tok.reshape(-1)]) if dtype == "bf16" else w[tok.reshape(-1)]
+    h = rng.standard_normal(size=(B * K, hidden), dtype=np.float32)
+    h += np.float32(steer) * wf
+    hs = _round_to(h.reshape(B, K, hidden), dtype)
+    L = np.minimum(rng.geometric(0.25, size=B) - 1, K - 1).astype(np.int32)
+    drafts = rng.integers(0, V, size=(B, K - 1)).astype(np.int32)
+    other = rng.integers(0, max(V - 1, 1), size=B).astype(np.int32)
+    for b in range(B):
+        n = int(L[b])
+        drafts[b, :n] = tok[b, :n]
+        if n < K - 1:
+            t = int(tok[b, n])
+            o = int(other[b])
+            drafts[b, n] = o if o < t else o + 1
+    return LmHeadInputs(B, K, hidden, V, dtype, hs, w, drafts, L, tok)
+
+
 # --------------------------------------------------------------------------- sampling
 
 @dataclass
@@ -469,6 +526,8 @@ WORKLOADS = {
     "qwen7b_tree60": Workload("qwen7b_tree60", "7B layer, ctx 25119 + Tree-60 (61 nodes), V 152064",
                               dict(B=1, K=61, Hq=28, Hkv=4, D=128, ctx=25119, V=152064,
                                    dtype="bf16", levels=TREE60_LEVELS)),
+    "qwen7b_lmhead": Workload("qwen7b_lmhead", "7B LM head: 16 rows x hidden 3584 x V 152064",
+                              dict(B=1, K=16, hidden=3584, V=152064, dtype="bf16")),
 }
 
 
@@ -511,3 +570,9 @@ def make_workload_tree(name: str, cycle: int = 0) -> TreeInputs:
     rng = rng_for(name, 10_000 + cycle)
     return make_tree_greedy(rng, B=p["B"], V=p["V"], parents=workload_tree(name),
                             dtype=p["dtype"])
+
+
+def make_workload_lm_head(name: str = "qwen7b_lmhead", cycle: int = 0) -> LmHeadInputs:
+    p = WORKLOADS[name].params
+    return make_lm_head(rng_for(name, cycle), B=p["B"], K=p["K"], hidden=p["hidden"], V=p["V"],
+                        dtype=p["dtype"])

@@ -111,6 +111,9 @@ ROWS = {
     "attn_tree60": ("qwen7b_tree60", "verify attention with the Tree-60 mask (61 nodes, 427 "
                     "rows per KV head), 7B layer, ctx 25,119", 12),
     "tree60_accept": ("qwen7b_tree60", "greedy tree acceptance, 61 nodes over 152,064", 28),
+    "lm_head": ("qwen7b_lmhead", "LM head fused with greedy acceptance: 16 x 3584 hidden "
+                "states against the 152,064 x 3584 bf16 output embedding (1.09 GB, more than "
+                "twice the Infinity Cache, so no rotation)", 1),
 }
 
 
@@ -187,6 +190,20 @@ def run_row(args):
 
         def call(i, st):
             sv.accept_greedy_tree(lg[i], par, tok, want_argmax=False, out=outs, stream=st)
+    elif args.row == "lm_head":
+        li = W.make_workload_lm_head(wl)
+        hs = dev_t(li.hidden_states, li.dtype)
+        wt = dev_t(li.weight, li.dtype)
+        dr = i32(li.drafts)
+        outs = (torch.empty(li.B, dtype=torch.int32, device=dev),
+                torch.empty(li.B, li.K, dtype=torch.int32, device=dev), None)
+        sv.lm_head_greedy(hs, wt, dr, want_argmax=False, out=outs)
+        nbytes = (wt.numel() + hs.numel()) * 2
+        flops = 2.0 * li.B * li.K * li.V * li.hidden
+        shape = {"B": li.B, "K": li.K, "hidden": li.hidden, "V": li.V}
+
+        def call(i, st):
+            sv.lm_head_greedy(hs, wt, dr, want_argmax=False, out=outs, stream=st)
     elif args.row == "sample_72b":
         smp = W.make_workload_sample(wl, 0)
         tl = [dev_t(smp.target_logits, smp.dtype)]

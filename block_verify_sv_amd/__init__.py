@@ -73,6 +73,9 @@ _SIGNATURES = {
                                       c_vp, c_vp, c_vp, c_sz, c_vp]),
     "sv_commit_tree": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                c_vp, c_vp, c_vp]),
+    "sv_lm_head_greedy_workspace": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]),
+    "sv_lm_head_greedy": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                  c_vp, c_vp, c_vp, c_sz, c_vp]),
 }
 
 
@@ -121,8 +124,8 @@ _WS: dict = {}
 
 
 def _workspace(kind: str, nbytes: int, device, zero: bool) -> torch.Tensor:
-    """A per-(kind, device) workspace grown on demand.  Counter workspaces are created
-    zeroed; every library call leaves their counters at zero again."""
+    """A per-(kind, device) workspace grown on demand (the library needs no initial
+    contents; ``zero`` only picks a zero-filled first allocation)."""
     key = (kind, str(device))
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -255,6 +258,38 @@ def accept_greedy_tree(logits: torch.Tensor, parents: torch.Tensor, tokens: torc
                                      _stream(stream)),
            "sv_accept_greedy_tree")
     return acc, toks, path, am
+
+
+def lm_head_greedy(hidden_states: torch.Tensor, weight: torch.Tensor, drafts: torch.Tensor,
+                   want_argmax: bool = True, out=None, workspace=None, stream=None):
+    """LM head + greedy acceptance: hidden_states [B][K][hidden], weight [V][hidden] (bf16
+    or fp16).  Returns (accept_len [B], out_tokens [B][K], argmax [B][K] or None)."""
+    _require(hidden_states, "hidden_states")
+    _require(weight, "weight", hidden_states.dtype)
+    _require(drafts, "drafts", torch.int32)
+    B, K, Hd = hidden_states.shape
+    V = weight.shape[0]
+    if hidden_states.dtype not in (torch.bfloat16, torch.float16):
+        raise SvError("LM head operands must be bfloat16 or float16")
+    if weight.shape[1] != Hd or tuple(drafts.shape) != (B, K - 1):
+        raise SvError("weight must be [V][hidden] and drafts [B][K-1]")
+    lib = load()
+    n = c_sz()
+    _check(lib.sv_lm_head_greedy_workspace(B, K, V, Hd, ctypes.byref(n)),
+           "sv_lm_head_greedy_workspace")
+    if workspace is None:
+        workspace = _workspace("lm_head", n.value, weight.device, zero=False)
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=weight.device)
+        toks = torch.empty(B, K, dtype=torch.int32, device=weight.device)
+        am = torch.empty(B, K, dtype=torch.int32, device=weight.device) if want_argmax else None
+    else:
+        acc, toks, am = out
+    _check(lib.sv_lm_head_greedy(B, K, V, Hd, _DTYPES[hidden_states.dtype], _ptr(hidden_states),
+                                 _ptr(weight), _ptr(drafts), _ptr(acc), _ptr(toks), _ptr(am),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)),
+           "sv_lm_head_greedy")
+    return acc, toks, am
 
 
 def accept_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, drafts: torch.Tensor,

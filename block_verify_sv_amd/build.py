@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libspecverify.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "attention.hip", "accept_greedy.hip", "accept_sample.hip",
-           "compress.hip", "kv_append.hip", "commit.hip"]
+           "compress.hip", "kv_append.hip", "commit.hip", "lm_head.hip"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -189,6 +189,10 @@ hipError_t launch_greedy(const GreedyParams& p, sv_dtype dtype, hipStream_t stre
     hipLaunchKernelGGL(greedy_argmax_kernel<false>, grid, dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_greedy_walk(p, stream);
+}
+
+hipError_t launch_greedy_walk(const GreedyParams& p, hipStream_t stream) {
   if (p.tree)
     hipLaunchKernelGGL(greedy_tree_walk_kernel, dim3((p.B + kWalkSeqs - 1) / kWalkSeqs),
                        dim3(kThreads), 0, stream, p);

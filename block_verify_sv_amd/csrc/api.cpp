@@ -292,6 +292,70 @@ sv_status sv_accept_greedy_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_
                      "sv_accept_greedy_tree launch");
 }
 
+// ---------------------------------------------------------------- LM head + greedy
+static sv_status check_lm_head(int32_t B, int32_t K, int32_t V, int32_t hidden) {
+  sv_status st = check_accept_shape(B, K, V, 1);
+  if (st != SV_OK) return st;
+  if (static_cast<int64_t>(B) * K > 64)
+    return fail(SV_ERR_INVALID_ARG, "B * K must be <= 64 (got %lld)", static_cast<long long>(B) * K);
+  if (hidden < 32 || hidden % 32 != 0 || hidden > (1 << 20))
+    return fail(SV_ERR_INVALID_ARG, "hidden must be a positive multiple of 32 (got %d)", hidden);
+  return SV_OK;
+}
+
+sv_status sv_lm_head_greedy_workspace(int32_t B, int32_t K, int32_t V, int32_t hidden,
+                                      size_t* bytes) {
+  sv_status st = check_lm_head(B, K, V, hidden);
+  if (st != SV_OK) return st;
+  if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = sv::lm_head_workspace_bytes(B * K, V);
+  return ok();
+}
+
+sv_status sv_lm_head_greedy(int32_t B, int32_t K, int32_t V, int32_t hidden, sv_dtype dtype,
+                            const void* hidden_states, const void* weight,
+                            const int32_t* drafts, int32_t* accept_len, int32_t* out_tokens,
+                            int32_t* argmax, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  sv_status st = check_lm_head(B, K, V, hidden);
+  if (st != SV_OK) return st;
+  if (dtype != SV_BF16 && dtype != SV_F16)
+    return fail(SV_ERR_UNSUPPORTED, "LM head operands must be SV_BF16 or SV_F16");
+  if (!hidden_states || !weight || !accept_len || !out_tokens || (K > 1 && !drafts))
+    return fail(SV_ERR_INVALID_ARG, "hidden_states, weight, drafts and outputs are required");
+  if (!aligned16(hidden_states) || !aligned16(weight))
+    return fail(SV_ERR_INVALID_ARG, "hidden_states and weight must be 16-byte aligned");
+  const int M = B * K;
+  const size_t need = sv::lm_head_workspace_bytes(M, V);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "LM head needs %zu workspace bytes", need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 7u) != 0)
+    return fail(SV_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
+  sv::LmHeadParams p;
+  p.hidden = hidden_states;
+  p.weight = weight;
+  p.nwg = sv::lm_head_workgroups(V);
+  p.part = static_cast<unsigned long long*>(workspace);
+  p.keys = p.part + static_cast<size_t>(M) * p.nwg;
+  p.M = M;
+  p.V = V;
+  p.Hd = hidden;
+  sv::GreedyParams w;
+  memset(&w, 0, sizeof w);
+  w.drafts = drafts;
+  w.accept_len = accept_len;
+  w.out_tokens = out_tokens;
+  w.argmax = argmax;
+  w.keys = p.keys;
+  w.B = B;
+  w.K = K;
+  w.V = V;
+  w.chunk = V;
+  w.nchunk = 1;
+  return device_status(sv::launch_lm_head(p, w, dtype, static_cast<hipStream_t>(stream)),
+                       "sv_lm_head_greedy launch");
+}
+
 // ---------------------------------------------------------------- sampling
 sv_status sv_accept_sample_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes) {
   sv_status st = check_accept_shape(B, K, V, 2);

@@ -68,6 +68,22 @@ struct GreedyParams {
 size_t greedy_workspace_bytes(int B, int K);
 int greedy_chunk(int V, sv_dtype dtype);
 hipError_t launch_greedy(const GreedyParams& p, sv_dtype dtype, hipStream_t stream);
+hipError_t launch_greedy_walk(const GreedyParams& p, hipStream_t stream);   // walk only
+
+// ---------------------------------------------------------------- LM head + greedy
+struct LmHeadParams {
+  const void* hidden;         // [M][Hd]
+  const void* weight;         // [V][Hd]
+  unsigned long long* part;   // [M][nwg] per-workgroup argmax keys
+  unsigned long long* keys;   // [M] row argmax keys (the walk's nchunk = 1)
+  int32_t M, V, Hd;
+  int32_t nwg;
+};
+
+int lm_head_workgroups(int V);
+size_t lm_head_workspace_bytes(int M, int V);
+hipError_t launch_lm_head(const LmHeadParams& p, const GreedyParams& walk, sv_dtype dtype,
+                          hipStream_t stream);
 
 // ---------------------------------------------------------------- sampling accept
 struct SampleParams {

@@ -1,0 +1,183 @@
+// The target's LM head fused with greedy acceptance: logits = H . W^T for the block's
+// hidden states H [M = B*K][Hd] against the output embedding W [V][Hd] (bf16 or fp16),
+// reduced to each row's argmax without ever storing a logit, then the chain rule (the
+// verify forward's last step before the acceptance of the VFlash-FM cycle figure).
+//
+// Pass 1 (lm_head_argmax_kernel): each workgroup owns 256 vocabulary rows, 64 per wave
+// as four 16-row MFMA blocks (16x16x32 bf16/f16, fp32 accumulate).  The contraction
+// runs over Hd in 32-wide steps: lane (j, g) of a wave loads the 16 bytes of W row
+// v0 + 16*blk + j at columns 8g .. 8g+7 of the step (four 64-byte runs per row and
+// step), and H the same way, straight into MFMA operand registers through a register
+// ring several steps deep; no LDS staging, no barriers in the loop.  The weight is read
+// exactly once, so the pass is bound by HBM on it.  The epilogue turns every logit into
+// a packed key (orderable value bits << 32 | ~index), reduces each row over the wave's
+// 64 columns with shuffles and over the four waves through LDS, and stores one key per
+// (row, workgroup).
+// Pass 2 (lm_head_reduce_kernel): one workgroup per row folds its keys into one.
+// Pass 3: the greedy walk of the chain rule over those keys.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace sv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerWave = 64;                  // four 16-row MFMA blocks
+constexpr int kRing = 6;                          // k-steps of loads (kRing - 1 in flight)
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <class Tag>
+__device__ __forceinline__ f32x4v mfma16(u32x4 a, u32x4 b, f32x4v c);
+template <>
+__device__ __forceinline__ f32x4v mfma16<TagBF16>(u32x4 a, u32x4 b, f32x4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4v mfma16<TagF16>(u32x4 a, u32x4 b, f32x4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// MT = row tiles of 16 (M <= 16*MT).  The MFMA contraction pairs element e of lane
+// (i, g) in A with element e of lane (j, g) in B, so loading both operands with the
+// same (g, e) -> column map sums every column of the step exactly once.
+template <class Tag, int MT>
+__global__ void __launch_bounds__(kThreads) lm_head_argmax_kernel(const LmHeadParams p) {
+  __shared__ uint64_t red[kThreads / kWave][16 * MT];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int v0 = blockIdx.x * (kThreads / kWave) * kRowsPerWave + wave * kRowsPerWave;
+  const uint16_t* W = static_cast<const uint16_t*>(p.weight);
+  const uint16_t* H = static_cast<const uint16_t*>(p.hidden);
+  // rows past V or M are clamped in bounds; their keys are never kept
+  const uint16_t* wrow[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    wrow[nb] = W + static_cast<size_t>(min(v0 + 16 * nb + l16, p.V - 1)) * p.Hd + 8 * g;
+  const uint16_t* hrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    hrow[mt] = H + static_cast<size_t>(min(16 * mt + l16, p.M - 1)) * p.Hd + 8 * g;
+
+  const int steps = p.Hd / 32;
+  struct St { u32x4 w[4]; u32x4 h[MT]; };
+  auto load = [&](St& s, int st) {
+    const int k = min(st, steps - 1) * 32;        // past the end: re-read the last step
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) s.w[nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + k);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) s.h[mt] = *reinterpret_cast<const u32x4*>(hrow[mt] + k);
+  };
+  f32x4v acc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mt][nb] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // The prologue loads are kept in step order and the loop runs whole groups of kRing
+  // steps (only the MFMAs are skipped past the end): the compiler merges the wait
+  // counts of every path into the loop head, and a reordered prologue or an exit from
+  // the middle of a group would make it drain the ring once per group.
+  St ring[kRing];
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u) {
+    load(ring[u], u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int s0 = 0; s0 < steps; s0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int st = s0 + u;
+      load(ring[(u + kRing - 1) % kRing], st + kRing - 1);
+      if (st < steps) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mt][nb] = mfma16<Tag>(ring[u].h[mt], ring[u].w[nb], acc[mt][nb]);
+      }
+    }
+  }
+
+  // epilogue: lane (j, g) holds logit (row 16mt + 4g + r, column v0 + 16nb + j)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int v = v0 + 16 * nb + l16;
+        const uint64_t key = v < p.V ? argmax_key(acc[mt][nb][r], static_cast<uint32_t>(v)) : 0;
+        best = key > best ? key : best;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {          // over the 16 columns of the lane group
+        const uint64_t w = __shfl_xor(best, o);
+        best = w > best ? w : best;
+      }
+      if (l16 == 0) red[wave][16 * mt + 4 * g + r] = best;
+    }
+  }
+  __syncthreads();
+  if (tid < p.M) {
+    uint64_t best = red[0][tid];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) best = red[w][tid] > best ? red[w][tid] : best;
+    p.part[static_cast<size_t>(tid) * p.nwg + blockIdx.x] = best;
+  }
+}
+
+// One workgroup per row: the maximum of the row's per-workgroup keys.
+__global__ void __launch_bounds__(kThreads) lm_head_reduce_kernel(const LmHeadParams p) {
+  __shared__ uint64_t red[kThreads / kWave];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const unsigned long long* src = p.part + static_cast<size_t>(row) * p.nwg;
+  uint64_t best = 0;
+  for (int i = tid; i < p.nwg; i += kThreads) best = src[i] > best ? static_cast<uint64_t>(src[i]) : best;
+  best = wave_max_u64(best);
+  if ((tid & 63) == 0) red[tid >> 6] = best;
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kThreads / kWave; ++w) best = red[w] > best ? red[w] : best;
+    p.keys[row] = best;                           // wave 0's maximum is already in best
+  }
+}
+
+template <class Tag>
+hipError_t launch_typed(const LmHeadParams& p, hipStream_t stream) {
+  const dim3 grid(p.nwg), block(kThreads);
+  if (p.M <= 16)
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1>), grid, block, 0, stream, p);
+  else if (p.M <= 32)
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 2>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 4>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int lm_head_workgroups(int V) {
+  const int per = (kThreads / kWave) * kRowsPerWave;
+  return (V + per - 1) / per;
+}
+
+size_t lm_head_workspace_bytes(int M, int V) {
+  return (static_cast<size_t>(M) * lm_head_workgroups(V) + M) * sizeof(uint64_t);
+}
+
+hipError_t launch_lm_head(const LmHeadParams& p, const GreedyParams& walk, sv_dtype dtype,
+                          hipStream_t stream) {
+  hipError_t e = dtype == SV_F16 ? launch_typed<TagF16>(p, stream) : launch_typed<TagBF16>(p, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lm_head_reduce_kernel, dim3(p.M), dim3(kThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_greedy_walk(walk, stream);
+}
+
+}  // namespace sv

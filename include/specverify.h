@@ -18,6 +18,7 @@
  *   sv_commit            close a cycle: grow the context, pick the next anchor
  *   sv_accept_greedy_tree  greedy verification of a draft tree (walk from the anchor)
  *   sv_commit_tree       close a tree cycle: move the accepted path's K/V into place
+ *   sv_lm_head_greedy    the target's LM head fused with greedy acceptance
  *
  * Conventions for every call
  *   - Array arguments are DEVICE pointers unless stated otherwise.  The caller
@@ -247,6 +248,24 @@ sv_status sv_commit_tree(const sv_attn_desc* desc, const int32_t* accept_len,
                          const int32_t* out_tokens, const int32_t* accept_path,
                          const int32_t* page_table, void* k_cache, void* v_cache,
                          int32_t* ctx_lens, int32_t* next_anchor, void* stream);
+
+/* -------------------------------------------------------------------------------------
+ * LM head fused with greedy acceptance (the last step of the verify forward, then the
+ * greedy rule of the VFlash-FM cycle figure): logits[b][i][v] = <hidden_states[b][i],
+ * weight[v]> accumulated in fp32, never written to memory; t_i = the lowest-index argmax
+ * of row i; then the chain rule exactly as sv_accept_greedy (same outputs).
+ * Layouts: hidden_states [B][K][hidden], weight [V][hidden] (the output embedding, row
+ * per token), both SV_BF16 or SV_F16; drafts [B][K-1].  The weight is read once.
+ * Limits: B * K <= 64, hidden a multiple of 32, 1 <= V < 2^31, 1 <= K <= 64.
+ * Workspace: sv_lm_head_greedy_workspace bytes, 8-byte aligned, no initial contents.
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_lm_head_greedy_workspace(int32_t B, int32_t K, int32_t V, int32_t hidden,
+                                      size_t* bytes);
+sv_status sv_lm_head_greedy(int32_t B, int32_t K, int32_t V, int32_t hidden, sv_dtype dtype,
+                            const void* hidden_states, const void* weight,
+                            const int32_t* drafts, int32_t* accept_len, int32_t* out_tokens,
+                            int32_t* argmax, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 #ifdef __cplusplus
 }

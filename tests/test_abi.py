@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert lib.sv_version() == 1
@@ -190,6 +190,21 @@ def test_tree_validation(lib):
         a = list(arrays)
         a[i] = None
         assert lib.sv_commit_tree(ctypes.byref(d), *a, None) == INVALID
+
+
+def test_lm_head_validation(lib):
+    n = ctypes.c_size_t()
+    assert lib.sv_lm_head_greedy_workspace(1, 16, 152064, 3584, ctypes.byref(n)) == OK
+    assert n.value == (16 * 594 + 16) * 8      # one key per (row, 256-row workgroup) + rows
+    for B, K, V, Hd in [(5, 16, 10, 64), (1, 16, 10, 48), (1, 16, 10, 0), (1, 0, 10, 64),
+                        (1, 16, 0, 64)]:
+        assert lib.sv_lm_head_greedy_workspace(B, K, V, Hd, ctypes.byref(n)) == INVALID
+    call = lambda dt, h, ws, nbytes: lib.sv_lm_head_greedy(
+        1, 16, 1000, 64, dt, h, FAKE, FAKE, FAKE, FAKE, None, ws, nbytes, None)
+    assert call(sv.SV_F32, FAKE, FAKE, 1 << 20) == UNSUPPORTED
+    assert call(sv.SV_BF16, None, FAKE, 1 << 20) == INVALID
+    assert call(sv.SV_BF16, ctypes.c_void_p(0x1008), FAKE, 1 << 20) == INVALID
+    assert call(sv.SV_BF16, FAKE, FAKE, 8) == WORKSPACE
 
 
 def test_status_strings(lib):

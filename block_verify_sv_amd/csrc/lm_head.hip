@@ -3,15 +3,15 @@
 // reduced to each row's argmax without ever storing a logit, then the chain rule (the
 // verify forward's last step before the acceptance of the VFlash-FM cycle figure).
 //
-// Pass 1 (lm_head_argmax_kernel): each workgroup owns 256 vocabulary rows, 64 per wave
-// as four 16-row MFMA blocks (16x16x32 bf16/f16, fp32 accumulate).  The contraction
-// runs over Hd in 32-wide steps: lane (j, g) of a wave loads the 16 bytes of W row
-// v0 + 16*blk + j at columns 8g .. 8g+7 of the step (four 64-byte runs per row and
-// step), and H the same way, straight into MFMA operand registers through a register
-// ring several steps deep; no LDS staging, no barriers in the loop.  The weight is read
+// Pass 1 (lm_head_argmax_kernel): each workgroup owns 128 vocabulary rows, 32 per wave
+// as two 16-row MFMA blocks (16x16x32 bf16/f16, fp32 accumulate).  The contraction
+// runs over Hd in 64-wide load steps (two MFMA steps): lane (j, g) of a wave loads 32
+// contiguous bytes of W row v0 + 16*blk + j, so the four lanes of a row read one whole
+// 128-byte line per step, and H the same way, straight into MFMA operand registers
+// through a register ring; no LDS staging, no barriers in the loop.  The weight is read
 // exactly once, so the pass is bound by HBM on it.  The epilogue turns every logit into
 // a packed key (orderable value bits << 32 | ~index), reduces each row over the wave's
-// 64 columns with shuffles and over the four waves through LDS, and stores one key per
+// 32 columns with shuffles and over the four waves through LDS, and stores one key per
 // (row, workgroup).
 // Pass 2 (lm_head_reduce_kernel): one workgroup per row folds its keys into one.
 // Pass 3: the greedy walk of the chain rule over those keys.
@@ -22,8 +22,9 @@ namespace sv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerWave = 64;                  // four 16-row MFMA blocks
-constexpr int kRing = 6;                          // k-steps of loads (kRing - 1 in flight)
+constexpr int kBlocks = 2;                        // 16-row MFMA blocks per wave
+constexpr int kRowsPerWave = 16 * kBlocks;
+constexpr int kSub = 2;                           // MFMA steps per load step (when Hd allows)
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -41,9 +42,12 @@ __device__ __forceinline__ f32x4v mfma16<TagF16>(u32x4 a, u32x4 b, f32x4v c) {
 }
 
 // MT = row tiles of 16 (M <= 16*MT).  The MFMA contraction pairs element e of lane
-// (i, g) in A with element e of lane (j, g) in B, so loading both operands with the
-// same (g, e) -> column map sums every column of the step exactly once.
-template <class Tag, int MT>
+// (i, g) in A with element e of lane (j, g) in B, so any map of (g, e) to columns that
+// both operands share sums every column exactly once.  One load step covers 32*SUB
+// columns: lane (j, g) reads the 16*SUB contiguous bytes at columns 8*SUB*g .. of the
+// step, and its c-th 16-byte piece feeds MFMA c of the step.  With SUB = 2 the four lanes
+// of a row read one 128-byte line per step.
+template <class Tag, int MT, int SUB, int RING>
 __global__ void __launch_bounds__(kThreads) lm_head_argmax_kernel(const LmHeadParams p) {
   __shared__ uint64_t red[kThreads / kWave][16 * MT];
   const int tid = threadIdx.x;
@@ -53,51 +57,59 @@ __global__ void __launch_bounds__(kThreads) lm_head_argmax_kernel(const LmHeadPa
   const uint16_t* W = static_cast<const uint16_t*>(p.weight);
   const uint16_t* H = static_cast<const uint16_t*>(p.hidden);
   // rows past V or M are clamped in bounds; their keys are never kept
-  const uint16_t* wrow[4];
+  const uint16_t* wrow[kBlocks];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    wrow[nb] = W + static_cast<size_t>(min(v0 + 16 * nb + l16, p.V - 1)) * p.Hd + 8 * g;
+  for (int nb = 0; nb < kBlocks; ++nb)
+    wrow[nb] = W + static_cast<size_t>(min(v0 + 16 * nb + l16, p.V - 1)) * p.Hd + 8 * SUB * g;
   const uint16_t* hrow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    hrow[mt] = H + static_cast<size_t>(min(16 * mt + l16, p.M - 1)) * p.Hd + 8 * g;
+    hrow[mt] = H + static_cast<size_t>(min(16 * mt + l16, p.M - 1)) * p.Hd + 8 * SUB * g;
 
-  const int steps = p.Hd / 32;
-  struct St { u32x4 w[4]; u32x4 h[MT]; };
+  const int steps = p.Hd / (32 * SUB);
+  struct St { u32x4 w[kBlocks][SUB]; u32x4 h[MT][SUB]; };
   auto load = [&](St& s, int st) {
-    const int k = min(st, steps - 1) * 32;        // past the end: re-read the last step
+    const int k = min(st, steps - 1) * 32 * SUB;  // past the end: re-read the last step
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) s.w[nb] = *reinterpret_cast<const u32x4*>(wrow[nb] + k);
+    for (int nb = 0; nb < kBlocks; ++nb)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) s.h[mt] = *reinterpret_cast<const u32x4*>(hrow[mt] + k);
+      for (int c = 0; c < SUB; ++c)
+        s.w[nb][c] = *reinterpret_cast<const u32x4*>(wrow[nb] + k + 8 * c);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int c = 0; c < SUB; ++c)
+        s.h[mt][c] = *reinterpret_cast<const u32x4*>(hrow[mt] + k + 8 * c);
   };
-  f32x4v acc[MT][4];
+  f32x4v acc[MT][kBlocks];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mt][nb] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nb = 0; nb < kBlocks; ++nb) acc[mt][nb] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // The prologue loads are kept in step order and the loop runs whole groups of kRing
+  // The prologue loads are kept in step order and the loop runs whole groups of RING
   // steps (only the MFMAs are skipped past the end): the compiler merges the wait
   // counts of every path into the loop head, and a reordered prologue or an exit from
   // the middle of a group would make it drain the ring once per group.
-  St ring[kRing];
+  St ring[RING];
 #pragma unroll
-  for (int u = 0; u < kRing - 1; ++u) {
+  for (int u = 0; u < RING - 1; ++u) {
     load(ring[u], u);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int s0 = 0; s0 < steps; s0 += kRing) {
+  for (int s0 = 0; s0 < steps; s0 += RING) {
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) {
+    for (int u = 0; u < RING; ++u) {
       const int st = s0 + u;
-      load(ring[(u + kRing - 1) % kRing], st + kRing - 1);
+      load(ring[(u + RING - 1) % RING], st + RING - 1);
       if (st < steps) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int c = 0; c < SUB; ++c)
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            acc[mt][nb] = mfma16<Tag>(ring[u].h[mt], ring[u].w[nb], acc[mt][nb]);
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nb = 0; nb < kBlocks; ++nb)
+              acc[mt][nb] = mfma16<Tag>(ring[u].h[mt][c], ring[u].w[nb][c], acc[mt][nb]);
       }
     }
   }
@@ -109,7 +121,7 @@ __global__ void __launch_bounds__(kThreads) lm_head_argmax_kernel(const LmHeadPa
     for (int r = 0; r < 4; ++r) {
       uint64_t best = 0;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < kBlocks; ++nb) {
         const int v = v0 + 16 * nb + l16;
         const uint64_t key = v < p.V ? argmax_key(acc[mt][nb][r], static_cast<uint32_t>(v)) : 0;
         best = key > best ? key : best;
@@ -147,15 +159,20 @@ __global__ void __launch_bounds__(kThreads) lm_head_reduce_kernel(const LmHeadPa
   }
 }
 
+// Up to 16 rows with a 64-column-multiple width: 128-byte row runs (one cache line per
+// row and step), 4-step ring (128 VGPRs, four waves per SIMD); otherwise single MFMA
+// steps through a 6-step ring.
 template <class Tag>
 hipError_t launch_typed(const LmHeadParams& p, hipStream_t stream) {
   const dim3 grid(p.nwg), block(kThreads);
-  if (p.M <= 16)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1>), grid, block, 0, stream, p);
+  if (p.M <= 16 && p.Hd % (32 * kSub) == 0)
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, kSub, 4>), grid, block, 0, stream, p);
+  else if (p.M <= 16)
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, 1, 6>), grid, block, 0, stream, p);
   else if (p.M <= 32)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 2>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 2, 1, 6>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 4>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 4, 1, 6>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

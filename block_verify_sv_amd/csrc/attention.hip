@@ -408,45 +408,59 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   }
 
   // ---- the row's sum over both lane halves, then (KW == 2) the two key-part waves of
-  // a row group combine through LDS (the tile buffers are free after the last barrier)
+  // a row group combine through LDS (the tile buffers are free after the last barrier).
+  // The pair splits the d blocks: each wave stages the half its partner finishes, then
+  // combines and stores its own half, so both waves share the epilogue's work.  Both
+  // compute the combined (m, l) from the same two pairs (m = max of the two, each side
+  // weighted by exp2 of its distance to m); the kh = 0 wave stores it.
 #pragma unroll
   for (int t = 0; t < NRB; ++t) l_run[t] += __shfl_xor(l_run[t], 32);
+  // Wave kh finishes d blocks kh*HB .. kh*HB+HB-1; its results end up in oacc[t][0..HB)
+  // (registers are picked by value, never by a runtime index).
+  constexpr int HB = KW == 2 ? DB / 2 : DB;
   if constexpr (KW == 2) {
     // staged as [slot][row group][lane] 16-byte slots: every LDS access of a wave is one
-    // contiguous, conflict-free 1 KB run
+    // contiguous, conflict-free 1 KB run; wave kh writes slots kh*4*HB + 4*j + q4 (quad q4
+    // of the j-th d block of the half its partner finishes), and slot 4*DB holds the
+    // (m, l) of key part kh in its 8-byte half kh
     f32x4* stage = reinterpret_cast<f32x4*>(smem);
+    float2* stage_ml = reinterpret_cast<float2*>(smem);
     auto slot = [&](int t, int c) { return ((t * (4 * DB + 1) + c) * RG + rg) * 64 + lane; };
-    if (kh == 1) {
-#pragma unroll
-      for (int t = 0; t < NRB; ++t) {
-        if (!active[t]) continue;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            stage[slot(t, db * 4 + q4)] = f32x4{oacc[t][db][4 * q4], oacc[t][db][4 * q4 + 1],
-                                                oacc[t][db][4 * q4 + 2], oacc[t][db][4 * q4 + 3]};
-        stage[slot(t, 4 * DB)] = f32x4{m_run[t], l_run[t], 0.0f, 0.0f};
-      }
-    }
-    __syncthreads();
-    if (kh == 1) return;
+    const bool lo_half = kh == 0;
 #pragma unroll
     for (int t = 0; t < NRB; ++t) {
       if (!active[t]) continue;
-      const f32x4 ml2 = stage[slot(t, 4 * DB)];
-      const float m = fmaxf(m_run[t], ml2[0]);
-      const float a1 = fast_exp2((m_run[t] - m) * c2), a2 = fast_exp2((ml2[0] - m) * c2);
-      m_run[t] = m;
-      l_run[t] = l_run[t] * a1 + ml2[1] * a2;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int j = 0; j < HB; ++j)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 o2 = stage[slot(t, db * 4 + q4)];
+          const f32x4 lo = {oacc[t][j][4 * q4], oacc[t][j][4 * q4 + 1], oacc[t][j][4 * q4 + 2],
+                            oacc[t][j][4 * q4 + 3]};
+          const f32x4 hi = {oacc[t][j + HB][4 * q4], oacc[t][j + HB][4 * q4 + 1],
+                            oacc[t][j + HB][4 * q4 + 2], oacc[t][j + HB][4 * q4 + 3]};
+          stage[slot(t, kh * 4 * HB + 4 * j + q4)] = lo_half ? hi : lo;
+        }
+      stage_ml[2 * slot(t, 4 * DB) + kh] = make_float2(m_run[t], l_run[t]);
+    }
+    __syncthreads();
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            oacc[t][db][4 * q4 + e] = oacc[t][db][4 * q4 + e] * a1 + o2[e] * a2;
+    for (int t = 0; t < NRB; ++t) {
+      if (!active[t]) continue;
+      const float2 ml2 = stage_ml[2 * slot(t, 4 * DB) + 1 - kh];
+      const float m = fmaxf(m_run[t], ml2.x);
+      const float a1 = fast_exp2((m_run[t] - m) * c2), a2 = fast_exp2((ml2.x - m) * c2);
+      m_run[t] = m;
+      l_run[t] = l_run[t] * a1 + ml2.y * a2;
+#pragma unroll
+      for (int j = 0; j < HB; ++j)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 o2 = stage[slot(t, (1 - kh) * 4 * HB + 4 * j + q4)];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float own = lo_half ? oacc[t][j][4 * q4 + e] : oacc[t][j + HB][4 * q4 + e];
+            oacc[t][j][4 * q4 + e] = own * a1 + o2[e] * a2;
+          }
         }
     }
   }
@@ -466,11 +480,12 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
     if (r < p.R) {
       const float inv = l_run[t] > 0.0f ? 1.0f / l_run[t] : 0.0f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int j = 0; j < HB; ++j) {
+        const int db = (KW == 2 ? kh * HB : 0) + j;     // runtime only in the address
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float o[4] = {oacc[t][db][4 * q4], oacc[t][db][4 * q4 + 1],
-                              oacc[t][db][4 * q4 + 2], oacc[t][db][4 * q4 + 3]};
+          const float o[4] = {oacc[t][j][4 * q4], oacc[t][j][4 * q4 + 1],
+                              oacc[t][j][4 * q4 + 2], oacc[t][j][4 * q4 + 3]};
           S* dst = static_cast<S*>(p.part_o) +
                    ((((bg * RBT + rb) * DB + db) * 4 + q4) * p.nsplit + s) * 256 + lane * 4;
           if constexpr (SZ == 2) {
@@ -480,7 +495,8 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
             *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
           }
         }
-      if (h == 0) {
+      }
+      if (h == 0 && kh == 0) {
         const size_t rowid = (bg * p.nsplit + s) * p.R + r;
         p.part_ml[rowid] = make_float2(m_run[t] * c2, l_run[t]);   // m in log2 units
       }

@@ -110,6 +110,9 @@ ROWS = {
                       "(36, 324)", 4),
     "attn_tree60": ("qwen7b_tree60", "verify attention with the Tree-60 mask (61 nodes, 427 "
                     "rows per KV head), 7B layer, ctx 25,119", 12),
+    "attn_drafter": ("vflash_drafter", "drafter block attention (one of its layers): anchor + "
+                     "15 masks, bidirectional within the block, over ctx 25,119, 28q/4kv d128",
+                     12),
     "tree60_accept": ("qwen7b_tree60", "greedy tree acceptance, 61 nodes over 152,064", 28),
     "lm_head": ("qwen7b_lmhead", "LM head fused with greedy acceptance: 16 x 3584 hidden "
                 "states against the 152,064 x 3584 bf16 output embedding (1.09 GB, more than "
@@ -172,7 +175,8 @@ def run_row(args):
         shape = {"B": inp.B, "K": inp.K, "Hq": inp.Hq, "Hkv": inp.Hkv, "d": inp.D,
                  "ctx_sum": int(inp.ctx_lens.sum())}
 
-        mask = sv.mask_array(inp.mask) if wl == "qwen7b_tree60" else None
+        causal = np.array_equal(inp.mask, W.causal_mask(inp.K))
+        mask = None if causal else sv.mask_array(inp.mask)
 
         def call(i, st):
             sv.verify_attention_into(desc, q, ks[i], vs[i], pt, cl, out, lse, mask, ws, st)

@@ -21,7 +21,8 @@ def run(sv, inp, split_keys=0, max_ctx=None, hint=True):
     return out, lse
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "qwen7b_25k", "batched_paged", "qwen72b_sampling"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "qwen7b_25k", "batched_paged", "qwen72b_sampling",
+                                  "vflash_drafter"])
 def test_named_workloads_full_size(gpu_lib, name):
     """The workloads at their full sizes, in the launch configuration the bench uses."""
     inp = W.make_workload_verify(name)

@@ -27,6 +27,11 @@ Workloads (shapes taken from the pages' measurement setups):
 * ``qwen7b_tree60`` -- the 7B layer verifying a static draft tree of 60 nodes
   below the anchor (the "Tree-60" variant of the VFlash-FM results table): 61
   block rows with ancestor masks, planted greedy path through the tree.
+* ``vflash_drafter`` -- one layer of the VFlash-FM drafter's block attention: the
+  anchor and 15 masks attend bidirectionally to each other and to keys/values over
+  the whole 25,119-token context (VFlash-FM page, cycle figure: 4 drafter layers
+  reading projected keys and values of the target's cached hidden states), in the
+  7B layer's head geometry.
 * ``qwen7b_lmhead`` -- the 7B target's LM head over the block: 16 hidden states of
   width 3584 against a 152,064 x 3584 bf16 output embedding ~ N(0, 0.02), each
   hidden state steered to a planted token, drafts with a planted prefix.
@@ -528,6 +533,9 @@ WORKLOADS = {
                                    dtype="bf16", levels=TREE60_LEVELS)),
     "qwen7b_lmhead": Workload("qwen7b_lmhead", "7B LM head: 16 rows x hidden 3584 x V 152064",
                               dict(B=1, K=16, hidden=3584, V=152064, dtype="bf16")),
+    "vflash_drafter": Workload("vflash_drafter", "drafter layer: anchor + 15 masks, bidirectional "
+                               "block over ctx 25119, 28q/4kv d128",
+                               dict(B=1, K=16, Hq=28, Hkv=4, D=128, ctx=25119, dtype="bf16")),
 }
 
 
@@ -544,6 +552,10 @@ def make_workload_verify(name: str, cycle: int = 0) -> VerifyInputs:
         return make_verify(rng, B=p["B"], K=p["K"], Hq=p["Hq"], Hkv=p["Hkv"], D=p["D"],
                            ctx_lens=[p["ctx"]] * p["B"], P=16, dtype=p["dtype"],
                            mask=tree_mask(workload_tree(name)))
+    if name == "vflash_drafter":
+        return make_verify(rng, B=p["B"], K=p["K"], Hq=p["Hq"], Hkv=p["Hkv"], D=p["D"],
+                           ctx_lens=[p["ctx"]] * p["B"], P=16, dtype=p["dtype"],
+                           mask=all_ones_mask(p["K"]))
     if name == "batched_paged":
         ctx = log_uniform_contexts(rng, p["B"])
         return make_verify(rng, B=p["B"], K=p["K"], Hq=p["Hq"], Hkv=p["Hkv"], D=p["D"],

@@ -535,10 +535,20 @@ __global__ void __launch_bounds__(kMergeWaves * 64) attn_merge_kernel(const Attn
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int h = lane >> 5;
-  const int db = blockIdx.x >> 2;
-  const int q = blockIdx.x & 3;
-  const int rb = blockIdx.y;
-  const int bg = blockIdx.z;                     // b * Hkv + g
+  // Workgroups go to the 8 XCDs round-robin by linear id.  The NX workgroups of one
+  // (row block, b * Hkv + g) pair -- one per (d block, register quad) -- get ids of one
+  // residue mod 8, so that pair's (m, l) rows are fetched into one XCD's L2 instead of
+  // into all eight.  Ids past the last pair (the pair count rounded up to 8) exit.
+  constexpr int NX = 4 * DB;
+  const int RBT = (p.R + 31) >> 5;
+  const int slot = blockIdx.x >> 3;
+  const int pair = (slot / NX) * 8 + (blockIdx.x & 7);
+  if (pair >= RBT * p.B * p.Hkv) return;
+  const int x = slot - (slot / NX) * NX;
+  const int db = x >> 2;
+  const int q = x & 3;
+  const int rb = pair % RBT;
+  const int bg = pair / RBT;                     // b * Hkv + g
   const int b = bg / p.Hkv;
   const int g = bg - b * p.Hkv;
   const int r = rb * 32 + (lane & 31);
@@ -546,7 +556,6 @@ __global__ void __launch_bounds__(kMergeWaves * 64) attn_merge_kernel(const Attn
   int ctx = p.ctx_lens[b];
   ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
   const int ns = (ctx + p.K + p.chunk - 1) / p.chunk;
-  const int RBT = (p.R + 31) >> 5;
   const S* const po = static_cast<const S*>(p.part_o) +
                       ((((static_cast<size_t>(bg) * RBT + rb) * DB + db) * 4 + q) * p.nsplit) * 256 + lane * 4;
   const float2* const pml = p.part_ml + static_cast<size_t>(bg) * p.nsplit * p.R + min(r, p.R - 1);
@@ -614,7 +623,7 @@ __global__ void __launch_bounds__(kMergeWaves * 64) attn_merge_kernel(const Attn
   } else {
     *reinterpret_cast<f32x4*>(out) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
   }
-  if (p.lse && blockIdx.x == 0 && h == 0)
+  if (p.lse && x == 0 && h == 0)                 // the (d block 0, quad 0) workgroup
     p.lse[(static_cast<size_t>(b) * p.K + i) * p.Hq + hq] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
@@ -622,7 +631,7 @@ template <class Tag, int D>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   // 4 row-group waves x 2 key halves, one row block each (512 threads, two waves per
   // SIMD), a deep register ring for 16-bit data.  More than 4 row blocks (K*G > 128)
-  // run as two row halves of the same split.
+  // run as up to four row groups of 128 rows of the same split.
   const dim3 grid(p.nsplit_pad * p.row_halves, p.Hkv, p.B);
   if constexpr (Tag::kBytes == 2)
     hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, kRingDeep>), grid, dim3(512), 0, stream, p);
@@ -630,7 +639,8 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, 2>), grid, dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 mgrid(D / 32 * 4, (p.R + 31) / 32, p.B * p.Hkv);
+  const int pairs = (p.R + 31) / 32 * p.B * p.Hkv;
+  const dim3 mgrid(D / 32 * 4 * ((pairs + 7) / 8 * 8));
   hipLaunchKernelGGL((attn_merge_kernel<Tag, D>), mgrid, dim3(kMergeWaves * 64), 0, stream, p);
   return hipGetLastError();
 }

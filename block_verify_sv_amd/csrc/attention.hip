@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   S* const v_lds = reinterpret_cast<S*>(smem + K_LDS);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int l32 = lane & 31;
@@ -105,11 +105,16 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   // blockIdx.x = rgroup * nsplit_pad + s: the row groups of 128 rows of one split are
   // nsplit_pad (a multiple of 8) workgroups apart, so round-robin dispatch puts them on
   // one XCD and the later reads of each KV tile come from that XCD's L2
+  // No branch comes before the tile loads are issued: an exit taken on a loaded value
+  // (the split padding, the context length) would make the compiler wait for that value
+  // first and sink every load behind the branch.  A padding workgroup runs as the last
+  // real split with no tiles and stores nothing.
   const int rgroup = blockIdx.x / p.nsplit_pad;
-  const int s = blockIdx.x - rgroup * p.nsplit_pad;
+  const int s_raw = blockIdx.x - rgroup * p.nsplit_pad;
+  const bool pad = s_raw >= p.nsplit;
+  const int s = pad ? p.nsplit - 1 : s_raw;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
-  if (s >= p.nsplit) return;                     // padding of the split index
   const int rb0 = rgroup * RG * NRB;               // first row block of this row group
 
   // ---- start-up.  Nothing below needs the context length until the early-exit test,
@@ -129,6 +134,9 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   const int run = tid / TPR;
   const int li = tid - run * TPR;
   const int ntmax = (p.chunk + kTK - 1) / kTK;   // tiles of a full split
+  // the context length is read first, as a scalar load that overlaps the page-table
+  // reads; nothing waits on it until every tile load of the prologue is issued
+  const int ctx_raw = p.ctx_lens[b];
   int pg_pro[RING - 1];
 #pragma unroll
   for (int u = 0; u < RING - 1; ++u) {
@@ -139,8 +147,7 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   const int npg = min(((k0 + p.chunk - 1) >> p.P_log2) - pg0 + 1, p.max_pages - pg0);
   int pg_all[NPT];
 #pragma unroll
-  for (int u = 0; u < NPT; ++u)
-    pg_all[u] = u * T < npg ? table[min(pg0 + tid + u * T, last_page)] : -1;   // uniform test
+  for (int u = 0; u < NPT; ++u) pg_all[u] = table[min(pg0 + tid + u * T, last_page)];
   // query operand (B of S^T = K . Q^T): lane owns query row 32*rb + l32 (padding rows
   // past R read row R-1; their results are never stored)
   Op qop[NRB][KSTEPS];
@@ -219,13 +226,16 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   Tile r[RING];
 #pragma unroll
   for (int u = 0; u < RING - 1; ++u) load_tile(r[u], k0 + min(u, ntmax - 1) * kTK, pg_pro[u]);
+  // every load above is issued before anything waits on the context length: nothing
+  // may be moved across this point
+  asm volatile("" ::: "memory");
 
-  // ---- the context length: the first wait of the kernel
-  int ctx = p.ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
+  // ---- the context length: the first value the kernel branches on.  A split past this
+  // sequence's keys (or a padding workgroup) keeps k1 = k0: no tiles, no stores.
+  const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > p.max_ctx ? p.max_ctx : ctx_raw);
   const int n_keys = ctx + p.K;
-  if (k0 >= n_keys) return;                      // this sequence has fewer splits
-  const int k1 = min(k0 + p.chunk, n_keys);
+  const bool dead = pad || k0 >= n_keys;
+  const int k1 = dead ? k0 : min(k0 + p.chunk, n_keys);
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
     const int i = tid + u * T;
@@ -282,10 +292,30 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   // into the exp unit.
   const float c2 = p.scale_log2;
   const float resc = kRescale / c2;              // rescale threshold in raw units
+  // O^T += V^T . P^T for row block t over this wave's keys of the tile at vbase
+  auto pv = [&](int t, const Op (&pb)[PSW], const S* vbase) {
+#pragma unroll
+    for (int psi = 0; psi < PSW; ++psi) {
+      Op vop[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int ps = kh * PSW + psi;           // MFMA step within the tile
+        const S* vrow = vbase + (db * 32 + l32) * VROW;
+        if constexpr (KPL == 8) {
+          vop[db] = *reinterpret_cast<const u32x4*>(vrow + ps * 16 + h * 8);
+        } else {
+          vop[db] = static_cast<float>(vrow[32 * (ps >> 4) + key_of_reg(ps & 15, h)]);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[t][db] = Mfma<Tag>::step(vop[db], pb[psi], oacc[t][db]);
+    }
+  };
+  // One step of a wave: S^T for its keys of the tile in LDS buffer buf, mask, online
+  // softmax, then P.V.
   auto compute = [&](int buf, int kt) {
     const bool need_mask = (kt + kTK > ctx) || (kt + kTK > k1);
     const S* kbase = k_lds + buf * kTK * KROW;
-    const S* vbase = v_lds + buf * D * VROW;
     f32x16 sacc[NRB][KBW];
     auto scores = [&](int t) {
 #pragma unroll
@@ -353,30 +383,18 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
         psum += sv[e];
       }
       l_run[t] += psum;
+      Op pb[PSW];                                // P^T operands (16-bit: 8 keys a lane)
 #pragma unroll
       for (int psi = 0; psi < PSW; ++psi) {
-        Op bop;
         if constexpr (KPL == 8) {
-          const float* pv = &sv[psi * 8];
-          bop = u32x4{Tag::pack2(pv[0], pv[1]), Tag::pack2(pv[2], pv[3]),
-                      Tag::pack2(pv[4], pv[5]), Tag::pack2(pv[6], pv[7])};
+          const float* pv8 = &sv[psi * 8];
+          pb[psi] = u32x4{Tag::pack2(pv8[0], pv8[1]), Tag::pack2(pv8[2], pv8[3]),
+                          Tag::pack2(pv8[4], pv8[5]), Tag::pack2(pv8[6], pv8[7])};
         } else {
-          bop = sv[psi];
+          pb[psi] = sv[psi];
         }
-        Op vop[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int ps = kh * PSW + psi;         // MFMA step within the tile
-          const S* vrow = vbase + (db * 32 + l32) * VROW;
-          if constexpr (KPL == 8) {
-            vop[db] = *reinterpret_cast<const u32x4*>(vrow + ps * 16 + h * 8);
-          } else {
-            vop[db] = static_cast<float>(vrow[32 * (ps >> 4) + key_of_reg(ps & 15, h)]);
-          }
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[t][db] = Mfma<Tag>::step(vop[db], bop, oacc[t][db]);
       }
+      pv(t, pb, v_lds + buf * D * VROW);
     }
   };
 
@@ -389,15 +407,28 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   __syncthreads();                               // page ids visible
   const int nt = (k1 - k0 + kTK - 1) / kTK;
   auto tile_at = [&](int j) { return k0 + min(j, nt - 1) * kTK; };
+  // The page id of each ring load is read from LDS one step ahead, so its LDS round
+  // trip overlaps a step's math instead of delaying the load issue.
+  int pg_next = page_of(tile_at(RING - 1));
   auto step = [&](int j, Tile& rl, const Tile& rs, int buf) {
-    const int kt = tile_at(j + RING - 1);
-    load_tile(rl, kt, page_of(kt));
+    load_tile(rl, tile_at(j + RING - 1), pg_next);
+    pg_next = page_of(tile_at(j + RING));
     compute(buf, k0 + j * kTK);
     if (j + 1 < nt) store_tile(rs, buf ^ 1, k0 + (j + 1) * kTK);
     __syncthreads();
   };
   store_tile(r[0], 0, k0);
   __syncthreads();
+  if (dead) {                                    // workgroup-uniform, after the last barrier use
+    // a real split past this sequence's keys leaves an empty (m, l) pair for each row,
+    // which is all the merge reads of it (its O rows keep whatever the workspace held)
+    if (!pad) {
+      for (int r = tid; r < p.R; r += T)
+        p.part_ml[((static_cast<size_t>(b) * p.Hkv + g) * p.nsplit + s) * p.R + r] =
+            make_float2(kNegBig, 0.0f);
+    }
+    return;
+  }
   for (int j0 = 0; j0 < nt; j0 += RING) {
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
@@ -526,24 +557,32 @@ constexpr int kMergeWaves = 4;
 constexpr int kMergeBatch = 16;
 
 template <class Tag, int D>
-__global__ void __launch_bounds__(kMergeWaves * 64) attn_merge_kernel(const AttnParams p) {
+// (one workgroup per CU: registers are spent on loads in flight, not on occupancy)
+__global__ void __launch_bounds__(kMergeWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+attn_merge_kernel(const AttnParams p) {
   using S = typename Tag::store_t;
   constexpr int DB = D / 32;
   __shared__ f32x4 st[2][kMergeWaves][64];       // accumulator quad, (m, l) per lane
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int lane = tid & 63;
   const int h = lane >> 5;
   // Workgroups go to the 8 XCDs round-robin by linear id.  The NX workgroups of one
   // (row block, b * Hkv + g) pair -- one per (d block, register quad) -- get ids of one
   // residue mod 8, so that pair's (m, l) rows are fetched into one XCD's L2 instead of
   // into all eight.  Ids past the last pair (the pair count rounded up to 8) exit.
+  // The merge reads no context length: every real split leaves an (m, l) pair for each
+  // row, an empty one (l = 0) when it lies past its sequence's keys, so no load waits on
+  // another and no branch comes before the loads (ids past the last pair read the last
+  // pair and leave after the loads).
   constexpr int NX = 4 * DB;
   const int RBT = (p.R + 31) >> 5;
   const int slot = blockIdx.x >> 3;
-  const int pair = (slot / NX) * 8 + (blockIdx.x & 7);
-  if (pair >= RBT * p.B * p.Hkv) return;
+  const int npairs = RBT * p.B * p.Hkv;
+  const int pair_raw = (slot / NX) * 8 + (blockIdx.x & 7);
+  const bool live = pair_raw < npairs;
+  const int pair = live ? pair_raw : npairs - 1;
   const int x = slot - (slot / NX) * NX;
   const int db = x >> 2;
   const int q = x & 3;
@@ -553,20 +592,16 @@ __global__ void __launch_bounds__(kMergeWaves * 64) attn_merge_kernel(const Attn
   const int g = bg - b * p.Hkv;
   const int r = rb * 32 + (lane & 31);
   const bool valid = r < p.R;                    // padding rows of the last row block
-  int ctx = p.ctx_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > p.max_ctx ? p.max_ctx : ctx);
-  const int ns = (ctx + p.K + p.chunk - 1) / p.chunk;
   const S* const po = static_cast<const S*>(p.part_o) +
                       ((((static_cast<size_t>(bg) * RBT + rb) * DB + db) * 4 + q) * p.nsplit) * 256 + lane * 4;
   const float2* const pml = p.part_ml + static_cast<size_t>(bg) * p.nsplit * p.R + min(r, p.R - 1);
 
   float m_w = kNegBig, l_w = 0.0f;
   f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // Loads cover every allocated split and are issued together with the context-length
-  // read (no dependent round trip).  They are unconditional, at clamped in-bounds
-  // indices -- a load under a branch would be waited for before the next one -- and
-  // splits past this sequence's end (stale workspace: may hold anything) are replaced
-  // by empty ones afterwards.
+  // Loads cover every allocated split.  They are unconditional, at clamped in-bounds
+  // indices -- a load under a branch would be waited for before the next one.  A split
+  // with l = 0 (past its sequence's end; its O rows are stale workspace and may hold
+  // anything) adds nothing: its O is replaced by zeros before it is weighted.
   for (int s0 = wave; s0 < p.nsplit; s0 += kMergeWaves * kMergeBatch) {
     float2 ml[kMergeBatch];
     f32x4 o[kMergeBatch];
@@ -576,9 +611,10 @@ __global__ void __launch_bounds__(kMergeWaves * 64) attn_merge_kernel(const Attn
       ml[u] = pml[sp * p.R];
       o[u] = load4<Tag>(po + sp * 256);
     }
+    asm volatile("" ::: "memory");               // the whole batch is in flight before any use
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u)
-      if (!valid || s0 + u * kMergeWaves >= ns) {
+      if (s0 + u * kMergeWaves >= p.nsplit || !(ml[u].y > 0.0f)) {
         ml[u] = make_float2(kNegBig, 0.0f);
         o[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
@@ -599,7 +635,7 @@ __global__ void __launch_bounds__(kMergeWaves * 64) attn_merge_kernel(const Attn
   st[0][wave][lane] = acc;
   st[1][wave][lane] = f32x4{m_w, l_w, 0.0f, 0.0f};
   __syncthreads();
-  if (wave != 0 || !valid) return;
+  if (!live || wave != 0 || !valid) return;
 
   float M = kNegBig;
 #pragma unroll

@@ -67,7 +67,11 @@ __device__ __forceinline__ u32x4 keep32(u32x4 v, int keep) {
 
 // Split kernel.  RG row-group waves x KW key-part waves; wave (rg, kh) owns row blocks
 // rg, rg + RG, ... (NRB of them) and keys [32 kh*KBW, 32 (kh+1)*KBW) of every tile.
-template <class Tag, int D, int RG, int NRB, int KW, int RING>
+// LOADS_FIRST: the start-up tile loads go out before the context length is known (one
+// sequence: every split is live).  Otherwise (a batch, where the splits past a shorter
+// sequence's end are a large part of the grid) the context length is read first and
+// those splits leave before loading anything.
+template <class Tag, int D, int RG, int NRB, int KW, int RING, bool LOADS_FIRST>
 __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnParams p) {
   using S = typename Tag::store_t;
   using Op = typename Mfma<Tag>::op_t;
@@ -105,10 +109,10 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   // blockIdx.x = rgroup * nsplit_pad + s: the row groups of 128 rows of one split are
   // nsplit_pad (a multiple of 8) workgroups apart, so round-robin dispatch puts them on
   // one XCD and the later reads of each KV tile come from that XCD's L2
-  // No branch comes before the tile loads are issued: an exit taken on a loaded value
-  // (the split padding, the context length) would make the compiler wait for that value
-  // first and sink every load behind the branch.  A padding workgroup runs as the last
-  // real split with no tiles and stores nothing.
+  // With LOADS_FIRST no branch comes before the tile loads are issued: an exit taken on
+  // a loaded value (the split padding, the context length) would make the compiler wait
+  // for that value first and sink every load behind the branch.  A padding workgroup
+  // then runs as the last real split with no tiles and stores nothing.
   const int rgroup = blockIdx.x / p.nsplit_pad;
   const int s_raw = blockIdx.x - rgroup * p.nsplit_pad;
   const bool pad = s_raw >= p.nsplit;
@@ -135,8 +139,20 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   const int li = tid - run * TPR;
   const int ntmax = (p.chunk + kTK - 1) / kTK;   // tiles of a full split
   // the context length is read first, as a scalar load that overlaps the page-table
-  // reads; nothing waits on it until every tile load of the prologue is issued
+  // reads; with LOADS_FIRST nothing waits on it until every tile load of the prologue
+  // is issued
   const int ctx_raw = p.ctx_lens[b];
+  if constexpr (!LOADS_FIRST) {
+    const int ctx0 = ctx_raw < 0 ? 0 : (ctx_raw > p.max_ctx ? p.max_ctx : ctx_raw);
+    if (pad || k0 >= ctx0 + p.K) {               // no tiles: an empty (m, l) pair per row
+      if (!pad) {
+        for (int r = tid; r < p.R; r += T)
+          p.part_ml[((static_cast<size_t>(b) * p.Hkv + g) * p.nsplit + s) * p.R + r] =
+              make_float2(kNegBig, 0.0f);
+      }
+      return;
+    }
+  }
   int pg_pro[RING - 1];
 #pragma unroll
   for (int u = 0; u < RING - 1; ++u) {
@@ -550,14 +566,14 @@ __device__ __forceinline__ f32x4 load4(const typename Tag::store_t* src) {
 // Merge: one workgroup per (d block of 32 x register quad, row block of 32, sequence b x
 // KV head g).  Lane l owns row 32*rb + l%32 and the 4 d values 8q + 4(l/32) .. +3 of the
 // d block -- the partial layout's own order, so a wave's load of one split is one
-// contiguous 512-byte run.  Wave w folds splits w, w+4, ... in batches of kMergeBatch
-// (all loads of a batch in flight) with a running maximum; the four wave states are
-// combined in wave order through LDS.
+// contiguous 512-byte run.  Wave w folds splits w, w+4, ... in batches of BATCH (all
+// loads of a batch in flight; 16 when a pair has more than 32 splits, else 8, so few
+// loads go to clamped repeats) with a running maximum; the four wave states are
+// combined in wave order through LDS.  Registers are given to the loads in flight
+// rather than to occupancy.
 constexpr int kMergeWaves = 4;
-constexpr int kMergeBatch = 16;
 
-template <class Tag, int D>
-// (one workgroup per CU: registers are spent on loads in flight, not on occupancy)
+template <class Tag, int D, int BATCH>
 __global__ void __launch_bounds__(kMergeWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
 attn_merge_kernel(const AttnParams p) {
   using S = typename Tag::store_t;
@@ -602,31 +618,31 @@ attn_merge_kernel(const AttnParams p) {
   // indices -- a load under a branch would be waited for before the next one.  A split
   // with l = 0 (past its sequence's end; its O rows are stale workspace and may hold
   // anything) adds nothing: its O is replaced by zeros before it is weighted.
-  for (int s0 = wave; s0 < p.nsplit; s0 += kMergeWaves * kMergeBatch) {
-    float2 ml[kMergeBatch];
-    f32x4 o[kMergeBatch];
+  for (int s0 = wave; s0 < p.nsplit; s0 += kMergeWaves * BATCH) {
+    float2 ml[BATCH];
+    f32x4 o[BATCH];
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
+    for (int u = 0; u < BATCH; ++u) {
       const size_t sp = static_cast<size_t>(min(s0 + u * kMergeWaves, p.nsplit - 1));
       ml[u] = pml[sp * p.R];
       o[u] = load4<Tag>(po + sp * 256);
     }
     asm volatile("" ::: "memory");               // the whole batch is in flight before any use
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
+    for (int u = 0; u < BATCH; ++u)
       if (s0 + u * kMergeWaves >= p.nsplit || !(ml[u].y > 0.0f)) {
         ml[u] = make_float2(kNegBig, 0.0f);
         o[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
     float bm = m_w;
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) bm = fmaxf(bm, ml[u].x);
+    for (int u = 0; u < BATCH; ++u) bm = fmaxf(bm, ml[u].x);
     const float a = fast_exp2(m_w - bm);
     m_w = bm;
     l_w *= a;
     acc *= a;
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
+    for (int u = 0; u < BATCH; ++u) {
       const float w = ml[u].y * fast_exp2(ml[u].x - bm);   // 0 for absent / empty splits
       l_w += w;
       acc += w * o[u];
@@ -667,17 +683,23 @@ template <class Tag, int D>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   // 4 row-group waves x 2 key halves, one row block each (512 threads, two waves per
   // SIMD), a deep register ring for 16-bit data.  More than 4 row blocks (K*G > 128)
-  // run as up to four row groups of 128 rows of the same split.
+  // run as up to four row groups of 128 rows of the same split.  One sequence issues its
+  // start-up loads before reading its context length; a batch reads it first.
   const dim3 grid(p.nsplit_pad * p.row_halves, p.Hkv, p.B);
-  if constexpr (Tag::kBytes == 2)
-    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, kRingDeep>), grid, dim3(512), 0, stream, p);
-  else
-    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, 2>), grid, dim3(512), 0, stream, p);
+  constexpr int RING = Tag::kBytes == 2 ? kRingDeep : 2;
+  if (p.B == 1) {
+    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, true>), grid, dim3(512), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, false>), grid, dim3(512), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int pairs = (p.R + 31) / 32 * p.B * p.Hkv;
   const dim3 mgrid(D / 32 * 4 * ((pairs + 7) / 8 * 8));
-  hipLaunchKernelGGL((attn_merge_kernel<Tag, D>), mgrid, dim3(kMergeWaves * 64), 0, stream, p);
+  if (p.nsplit > 32)
+    hipLaunchKernelGGL((attn_merge_kernel<Tag, D, 16>), mgrid, dim3(kMergeWaves * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<Tag, D, 8>), mgrid, dim3(kMergeWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -75,8 +75,23 @@ def test_shapes_and_edges(gpu_lib, case):
     check_attention(out, lse, ref_out, ref_lse, dtype, str(case))
 
 
+def run_poisoned(sv, inp, split_keys, max_ctx):
+    """Like run(), into a workspace filled with 0xFF bytes (NaN as floats): any partial
+    of an absent split that the merge failed to ignore would surface in the output."""
+    d = upload_verify(inp)
+    desc = sv.make_desc(d["q"], d["k_cache"], d["page_table"], max_ctx, 0.0, split_keys, 0)
+    ws = torch.full((sv.attention_workspace_bytes(desc),), 255, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(d["q"].shape[:3], dtype=torch.float32, device="cuda")
+    sv.verify_attention_into(desc, d["q"], d["k_cache"], d["v_cache"], d["page_table"],
+                             d["ctx_lens"], out, lse, sv.mask_array(inp.mask), ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
 def test_max_ctx_above_actual_and_no_hint(gpu_lib):
-    """Grid sized for a larger max_ctx than any sequence has: surplus splits exit early."""
+    """Grid sized for a larger max_ctx than any sequence has (a batch: the context length
+    is read first): surplus splits exit early, leaving only empty (m, l) pairs."""
     rng = np.random.default_rng(7)
     inp = W.make_verify(rng, B=3, K=16, Hq=28, Hkv=4, D=128, ctx_lens=[100, 2000, 37], P=16,
                         dtype="bf16", shuffle=True)
@@ -85,10 +100,39 @@ def test_max_ctx_above_actual_and_no_hint(gpu_lib):
     pt = np.zeros((3, need), dtype=np.int32)
     pt[:, :inp.page_table.shape[1]] = np.where(inp.page_table >= 0, inp.page_table, 0)
     inp.page_table = pt
-    say("[attention] max_ctx=4000 over ctx [100, 2000, 37]")
-    out, lse = run(gpu_lib, inp, max_ctx=4000, hint=False)
+    say("[attention] max_ctx=4000 over ctx [100, 2000, 37], poisoned workspace")
+    out, lse = run_poisoned(gpu_lib, inp, split_keys=0, max_ctx=4000)
     ref_out, ref_lse = oracle.verify_attention_ref(inp)
     check_attention(out, lse, ref_out, ref_lse, "bf16", "max_ctx")
+
+
+def test_single_sequence_surplus_splits(gpu_lib):
+    """One sequence (start-up loads issued before the context length is known) with a
+    grid sized for max_ctx = 2000 over ctx 300: the surplus splits load, then leave an
+    empty (m, l) pair per row; the merge must treat them as absent."""
+    rng = np.random.default_rng(8)
+    inp = W.make_verify(rng, B=1, K=16, Hq=28, Hkv=4, D=128, ctx_lens=[300], P=16,
+                        dtype="bf16", shuffle=True)
+    need = (2000 + 16 + 15) // 16
+    pt = np.zeros((1, need), dtype=np.int32)
+    pt[:, :inp.page_table.shape[1]] = np.where(inp.page_table >= 0, inp.page_table, 0)
+    inp.page_table = pt
+    say("[attention] B=1 max_ctx=2000 over ctx [300], 64-key splits, poisoned workspace")
+    out, lse = run_poisoned(gpu_lib, inp, split_keys=64, max_ctx=2000)
+    ref_out, ref_lse = oracle.verify_attention_ref(inp)
+    check_attention(out, lse, ref_out, ref_lse, "bf16", "surplus")
+
+
+def test_more_splits_than_one_merge_round(gpu_lib):
+    """126 splits of 16 keys: each merge wave folds two rounds of 16 splits; the last
+    split holds only block keys 7..15, which rows 0..6 cannot see (l = 0 there)."""
+    rng = np.random.default_rng(9)
+    inp = W.make_verify(rng, B=1, K=16, Hq=28, Hkv=4, D=128, ctx_lens=[1993], P=16,
+                        dtype="bf16", shuffle=True)
+    say("[attention] ctx 1993, 16-key splits (126 splits), poisoned workspace")
+    out, lse = run_poisoned(gpu_lib, inp, split_keys=16, max_ctx=1993)
+    ref_out, ref_lse = oracle.verify_attention_ref(inp)
+    check_attention(out, lse, ref_out, ref_lse, "bf16", "two merge rounds")
 
 
 def test_deterministic_repeats(gpu_lib):

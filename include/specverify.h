@@ -172,7 +172,7 @@ sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
  *   out[b] = softmax(scale * queries . feats[b]^T) . feats[b], softmax over the N rows.
  * The printed formula has no 1/sqrt(D); pass scale = 1 for it (0 is read as 1).
  * Layouts: queries [C][D], feats [B][N][D], out [B][C][D], all SV_F16 (fp32 accumulate).
- * Limits: 1 <= C <= 64, 1 <= N <= 4096, D a multiple of 128.
+ * Limits: 1 <= C <= 64, 1 <= N <= 1024, D a multiple of 128 (invalid: SV_ERR_INVALID_ARG).
  * ------------------------------------------------------------------------------------ */
 sv_status sv_latent_compress_workspace(int32_t B, int32_t C, int32_t N, int32_t D,
                                        size_t* bytes);

@@ -23,7 +23,6 @@ constexpr int kMaxC = 64;
 constexpr int kSK = 64;                 // pass-1 contraction step (d per LDS tile)
 constexpr int kSRing = 4;               // pass-1 register ring (kSRing - 1 steps in flight)
 constexpr int kNT = 32;                 // feature rows per pass-3 tile
-constexpr int kDT = 128;                // output columns per pass-3 workgroup
 constexpr int kRing = 3;                // pass-3 register ring (kRing - 1 tiles in flight)
 
 __host__ __device__ __forceinline__ int pad_n(int N) { return (N + kNT - 1) / kNT * kNT; }
@@ -170,23 +169,31 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// DT: output columns per workgroup, 256 for long feature streams when D allows (each
+// wave then owns 4 column blocks of 32), else 128 (2 blocks).  The weight operand is read once per feature tile
+// for all DT columns, so the wider tile halves the weight re-reads per feature byte.
+template <int DT>
 __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
-  // feature tile row: kDT columns padded to 160 halves (80 banks), so the four rows one
-  // half-wave's transpose read touches start 16 banks apart
-  constexpr int FROW = 160;
-  static_assert(FROW >= kDT, "feature tile row");
+  // feature tile row: DT columns padded by 32 halves (DT + 32 halves = 16 banks mod 64),
+  // so the four rows one half-wave's transpose read touches start 16 banks apart
+  constexpr int FROW = DT + 32;
+  constexpr int NB = DT / 64;                      // 32-column blocks per wave
+  constexpr int CPR = DT / 8;                      // 16-byte chunks per tile row
+  constexpr int CPT = kNT * CPR / kThreads;        // chunks per thread per tile
+  static_assert(CPT * kThreads == kNT * CPR, "tile chunks per thread");
   __shared__ __align__(16) uint16_t f_lds[2][kNT * FROW];
   __shared__ float rsum[kMaxC];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int b = blockIdx.y;
-  const int dbase = blockIdx.x * kDT;
+  const int dbase = blockIdx.x * DT;
   const int N = p.N;
   const int Nw = pad_n(N);
   if (tid < kMaxC) rsum[tid] = p.rowsum[b * kMaxC + tid];
 
-  // ---- out tile: wave (wc, wd) owns query rows 32*wc.. and columns 64*wd.. (2 blocks).
+  // ---- out tile: wave (wc, wd) owns query rows 32*wc.. and columns (DT/2)*wd.. (NB
+  // blocks).
   // The weight operand (8 consecutive feature rows of one query row per lane) comes
   // straight from the workspace (cache-resident: every d tile of the image reads it).
   const int wc = wave >> 1, wd = wave & 1;
@@ -197,25 +204,25 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
   const int grp = lane >> 4, i16 = lane & 15;
   const int tr_off = (h * 8 + (i16 >> 2)) * FROW + (grp & 1) * 16 + 4 * (i16 & 3);
   const uint16_t* wsrc = p.weights + (static_cast<size_t>(b) * kMaxC + wc * 32 + l32) * Nw + h * 8;
-  f32x16 acc[2];
+  f32x16 acc[NB];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < NB; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
 
-  // feature tiles: kNT rows x kDT columns = 512 chunks of 16 B, 2 per thread, held in a
+  // feature tiles: kNT rows x DT columns in chunks of 16 B, CPT per thread, held in a
   // register ring with the tile's weight operands; tile rows past N (the last tile)
   // re-read row N-1 and meet weights that are zero
   const uint16_t* fb = static_cast<const uint16_t*>(p.feats) + static_cast<size_t>(b) * N * p.D;
   const int nt_count = Nw / kNT;
-  struct FT { u32x4 v[2]; u32x4 a[kNT / 16]; };
+  struct FT { u32x4 v[CPT]; u32x4 a[kNT / 16]; };
   auto load = [&](FT& f, int t) {
     const int nt = min(t, nt_count - 1) * kNT;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < CPT; ++u) {
       const int ch = tid + kThreads * u;
-      const int r = min(nt + (ch >> 4), N - 1);
-      f.v[u] = *reinterpret_cast<const u32x4*>(fb + static_cast<size_t>(r) * p.D + dbase + (ch & 15) * 8);
+      const int r = min(nt + ch / CPR, N - 1);
+      f.v[u] = *reinterpret_cast<const u32x4*>(fb + static_cast<size_t>(r) * p.D + dbase + (ch % CPR) * 8);
     }
 #pragma unroll
     for (int ks = 0; ks < kNT / 16; ++ks) f.a[ks] = *reinterpret_cast<const u32x4*>(wsrc + nt + ks * 16);
@@ -223,19 +230,19 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
   auto tile = [&](const FT& f, int t) {
     uint16_t* fl = f_lds[t & 1];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {                  // row-major, as loaded
+    for (int u = 0; u < CPT; ++u) {                // row-major, as loaded
       const int ch = tid + kThreads * u;
-      *reinterpret_cast<u32x4*>(&fl[(ch >> 4) * FROW + (ch & 15) * 8]) = f.v[u];
+      *reinterpret_cast<u32x4*>(&fl[(ch / CPR) * FROW + (ch % CPR) * 8]) = f.v[u];
     }
     __syncthreads();                               // tile t in LDS; tile t-1's buffer free
     if (active && t < nt_count) {
 #pragma unroll
       for (int ks = 0; ks < kNT / 16; ++ks) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < NB; ++tt) {
           // the operand (feature rows 16ks + 8h .. +7 of one column) as two transpose
           // reads of 4 rows each
-          const uint16_t* src = &fl[ks * 16 * FROW + wd * 64 + tt * 32 + tr_off];
+          const uint16_t* src = &fl[ks * 16 * FROW + wd * (DT / 2) + tt * 32 + tr_off];
           const uint2 lo = lds_read_tr16(src);
           const uint2 hi = lds_read_tr16(src + 4 * FROW);
           const u32x4 bo = {lo.x, lo.y, hi.x, hi.y};
@@ -261,12 +268,13 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
   if (!active) return;
   uint16_t* ob = static_cast<uint16_t*>(p.out) + static_cast<size_t>(b) * p.C * p.D;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < NB; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int c = wc * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
       if (c < p.C)
-        ob[static_cast<size_t>(c) * p.D + dbase + wd * 64 + t * 32 + l32] = f32_to_f16(acc[t][r] / rsum[c]);
+        ob[static_cast<size_t>(c) * p.D + dbase + wd * (DT / 2) + t * 32 + l32] =
+            f32_to_f16(acc[t][r] / rsum[c]);
     }
 }
 
@@ -294,7 +302,11 @@ hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(softmax_kernel, dim3(kMaxC / (kThreads / 64), p.B), dim3(kThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(out_kernel, dim3(p.D / kDT, p.B), dim3(kThreads), 0, stream, p);
+  // the wide tile pays off on long feature streams (measured: N = 576 -6%, N = 324 +1%)
+  if (p.D % 256 == 0 && p.N > 384)
+    hipLaunchKernelGGL(out_kernel<256>, dim3(p.D / 256, p.B), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(out_kernel<128>, dim3(p.D / 128, p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -42,6 +42,8 @@ def test_compressor_workload(gpu_lib, C, N):
 
 @pytest.mark.parametrize("B,C,N,D,scale", [
     (3, 1, 1, 128, 1.0), (2, 33, 100, 256, 1.0), (5, 64, 1024, 384, 0.5), (1, 17, 70, 4096, 1.0),
+    # 256-column out tiles (N > 384, D % 256 == 0): partial query block, ragged last tile
+    (2, 40, 500, 512, 1.0), (1, 64, 1024, 768, 1.0),
 ])
 def test_compressor_shapes(gpu_lib, B, C, N, D, scale):
     rng = np.random.default_rng(B * 7 + C)

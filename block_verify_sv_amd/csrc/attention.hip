@@ -5,12 +5,16 @@
 // of its head group form one dense (K*G) x d tile, so the scores S = Q_g K^T and the
 // update O += P V are matrix products and run on MFMA (32x32x16 bf16/f16, 32x32x2 fp32).
 //
-// Split pass: one workgroup per (sequence b, KV head g, key split s), sized so the
-// grid is about one workgroup per compute unit.  Four waves; wave w owns query-row
-// blocks w, w+4 (32 rows each).  The split's page ids are staged in LDS once, then keys
-// stream in tiles of 64: a ring of four register tiles keeps three tiles (96 KB at bf16,
-// d = 128) of global loads in flight while the fourth is written to one of two LDS
-// buffers, so the HBM latency is covered without a dependent page-table load per tile.
+// Split pass: one workgroup per (sequence b, KV head g, key split s, group of 128 query
+// rows), sized so the grid is about one workgroup per compute unit.  Eight waves: wave
+// (rg, kh) owns query-row block rg (32 rows) and key half kh of every 64-key tile; the
+// two key halves of a row block combine through LDS at the end.  The split's page ids
+// are staged in LDS once, then keys stream in tiles of 64: a ring of four register tiles
+// keeps three tiles (96 KB at bf16, d = 128) of global loads in flight while the fourth
+// is written to one of two LDS buffers, so the HBM latency is covered without a
+// dependent page-table load per tile.  One sequence issues its start-up loads before the
+// context length arrives; a batch reads the context length first and lets the splits
+// past a shorter sequence's end leave at once.
 // Per tile and row block the wave computes S^T = K_tile . Q^T (keys on the MFMA M axis,
 // query rows on N, so each lane owns one query row), applies the block mask, runs the
 // online softmax in registers, and accumulates O^T = V^T . P^T.
@@ -20,7 +24,8 @@
 //
 // Merge pass: one workgroup per (32-wide d block, 32-row block, sequence x KV head); its
 // waves read the partial tiles in the same register order (contiguous runs) and combine
-// the splits in a fixed order:
+// the splits in a fixed order (a split with l = 0, past its sequence's keys or with no
+// visible key for the row, is absent; no context length is read):
 //   m = max_s m_s, w_s = l_s 2^(m_s - m), out = sum_s w_s O_s / sum_s w_s,
 //   lse = (m + log2 sum_s w_s) * ln 2      (O_s: split s's output, already divided by l_s).
 #include "common.hpp"

@@ -42,9 +42,10 @@ def parse():
                     help="attention-only launches timed for the roofline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--row", choices=["cycle"] + sorted(ROWS), default="cycle",
+    ap.add_argument("--row", choices=["cycle", "hbm_probe"] + sorted(ROWS), default="cycle",
                     help="'cycle' (default) is the verify-cycle line; the others time one "
-                         "further entry point on its own workload and print its own line")
+                         "further entry point on its own workload and print its own line; "
+                         "'hbm_probe' times plain HBM traffic with torch's own kernels")
     ap.add_argument("--pmc-workload", choices=["attn", "copy"], default=None,
                     help="run a fixed loop for rocprofv3 --pmc counter passes and exit: "
                          "'attn' = --steps attention passes (rotating copies), 'copy' = "
@@ -269,8 +270,55 @@ def run_row(args):
     print(json.dumps(line), flush=True)
 
 
+def run_hbm_probe(args):
+    """Reference points for the rooflines, with torch's own kernels (not this library):
+    a read-only reduction over 2 GiB, a 1 GiB device copy (read + write), and the cost of
+    one tiny kernel launched back to back from a HIP graph."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = 1 << 30                                   # bf16 elements: 2 GiB
+    x = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(n // 2, dtype=torch.bfloat16, device=dev)
+    z = torch.zeros(1, dtype=torch.float32, device=dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / reps   # us per call
+
+    read_us = timed(lambda: torch.sum(x, dtype=torch.float32), 20)
+    copy_us = timed(lambda: y.copy_(x[: n // 2]), 20)
+    gr = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        z.add_(1.0)
+        st.synchronize()
+        with torch.cuda.graph(gr, stream=st):
+            for _ in range(200):
+                z.add_(1.0)
+    launch_us = timed(gr.replay, 10) / 200
+    print(json.dumps({"row": "hbm_probe",
+                      "read_2GiB_us": read_us, "read_GBps": 2 * n / (read_us * 1e-6) / 1e9,
+                      "copy_1GiB_us": copy_us,
+                      "copy_GBps_read_plus_write": 2 * n / (copy_us * 1e-6) / 1e9,
+                      "tiny_kernel_back_to_back_us": launch_us,
+                      "note": "torch kernels; reference points, not this library"}), flush=True)
+
+
 def main():
     args = parse()
+    if args.row == "hbm_probe":
+        run_hbm_probe(args)
+        return
     if args.row != "cycle":
         if args.gpus != 1:
             print(json.dumps({"error": "one GPU only"}))

@@ -111,7 +111,9 @@ AttnPlan plan_attention(const sv_attn_desc& d) {
     const int64_t work =
         (ctx_sum + static_cast<int64_t>(d.batch) * d.block) * d.num_kv_heads * pl.row_halves;
     chunk = (work + kNumCUs - 1) / kNumCUs;
-    chunk = (chunk + gran - 1) / gran * gran;
+    // whole 64-key tiles: a split's last tile costs a full step however few keys it
+    // holds, so rounding up to the tile keeps the step count and needs fewer splits
+    chunk = (chunk + 63) / 64 * 64;
     if (chunk < 64) chunk = 64;
     const int64_t cap = (n_max + gran - 1) / gran * gran;
     if (chunk > cap) chunk = cap;

@@ -25,6 +25,9 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"), "-I", SRC,
     # packed fp32 arithmetic stays off: plain fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar and pointer kernel arguments arrive preloaded in SGPRs, so a kernel's
+    # first loads need no kernel-argument round trip (an aggregate argument ends the run)
+    "-Xarch_device", "-mllvm=-amdgpu-kernarg-preload-count=16",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -77,7 +77,11 @@ __device__ __forceinline__ u32x4 keep32(u32x4 v, int keep) {
 // sequence's end are a large part of the grid) the context length is read first and
 // those splits leave before loading anything.
 template <class Tag, int D, int RG, int NRB, int KW, int RING, bool LOADS_FIRST>
-__global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(64 * RG * KW, 1)
+attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_cache,
+                  const int32_t* ctx_lens,
+                  int32_t chunk, int32_t nsplit_pad, int32_t P_log2, int32_t max_pages,
+                  int32_t num_pages, int32_t Hkv, const AttnParams p) {
   using S = typename Tag::store_t;
   using Op = typename Mfma<Tag>::op_t;
   constexpr int T = 64 * RG * KW;                // threads
@@ -117,11 +121,11 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   // With LOADS_FIRST no branch comes before the tile loads are issued: an exit taken on
   // a loaded value (the split padding, the context length) would make the compiler wait
   // for that value first and sink every load behind the branch.  A padding workgroup
-  // then runs as the last real split with no tiles and stores nothing.
-  const int rgroup = blockIdx.x / p.nsplit_pad;
-  const int s_raw = blockIdx.x - rgroup * p.nsplit_pad;
+  // reads pages at its own (clamped) positions, then has no tiles and stores nothing.
+  const int rgroup = blockIdx.x / nsplit_pad;
+  const int s_raw = blockIdx.x - rgroup * nsplit_pad;
   const bool pad = s_raw >= p.nsplit;
-  const int s = pad ? p.nsplit - 1 : s_raw;
+  const int s = s_raw;                           // a padding id only reads (clamped) pages
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int rb0 = rgroup * RG * NRB;               // first row block of this row group
@@ -133,26 +137,26 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   // (staged in LDS for the later tiles), the query rows and the block mask.  All of them
   // are unconditional loads at clamped, in-bounds indices: a load under a branch would
   // make the compiler wait for it before the next one.
-  const int k0 = s * p.chunk;
-  const int pg0 = k0 >> p.P_log2;
-  const int Pm1 = (1 << p.P_log2) - 1;
-  const int32_t* table = p.page_table + static_cast<size_t>(b) * p.max_pages;
-  const int last_page = p.max_pages - 1;
+  const int k0 = s * chunk;
+  const int pg0 = k0 >> P_log2;
+  const int Pm1 = (1 << P_log2) - 1;
+  const int32_t* table = page_table + static_cast<size_t>(b) * max_pages;
+  const int last_page = max_pages - 1;
   const int KR = min(Pm1 + 1, kTK);              // keys of one run (see tile staging)
   const int TPR = T * KR / kTK;                  // threads per run
   const int run = tid / TPR;
   const int li = tid - run * TPR;
-  const int ntmax = (p.chunk + kTK - 1) / kTK;   // tiles of a full split
+  const int ntmax = (chunk + kTK - 1) / kTK;     // tiles of a full split
   // the context length is read first, as a scalar load that overlaps the page-table
   // reads; with LOADS_FIRST nothing waits on it until every tile load of the prologue
   // is issued
-  const int ctx_raw = p.ctx_lens[b];
+  const int ctx_raw = ctx_lens[b];
   if constexpr (!LOADS_FIRST) {
     const int ctx0 = ctx_raw < 0 ? 0 : (ctx_raw > p.max_ctx ? p.max_ctx : ctx_raw);
     if (pad || k0 >= ctx0 + p.K) {               // no tiles: an empty (m, l) pair per row
       if (!pad) {
         for (int r = tid; r < p.R; r += T)
-          p.part_ml[((static_cast<size_t>(b) * p.Hkv + g) * p.nsplit + s) * p.R + r] =
+          p.part_ml[((static_cast<size_t>(b) * Hkv + g) * p.nsplit + s) * p.R + r] =
               make_float2(kNegBig, 0.0f);
       }
       return;
@@ -162,10 +166,10 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
 #pragma unroll
   for (int u = 0; u < RING - 1; ++u) {
     const int pos0 = k0 + min(u, ntmax - 1) * kTK + run * KR;
-    pg_pro[u] = table[min(pos0 >> p.P_log2, last_page)];
+    pg_pro[u] = table[min(pos0 >> P_log2, last_page)];
   }
   constexpr int NPT = (kMaxSplitPages + T - 1) / T;
-  const int npg = min(((k0 + p.chunk - 1) >> p.P_log2) - pg0 + 1, p.max_pages - pg0);
+  const int npg = min(((k0 + chunk - 1) >> P_log2) - pg0 + 1, max_pages - pg0);
   int pg_all[NPT];
 #pragma unroll
   for (int u = 0; u < NPT; ++u) pg_all[u] = table[min(pg0 + tid + u * T, last_page)];
@@ -192,8 +196,8 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
       }
     }
   }
-  const S* kc = static_cast<const S*>(p.k_cache);
-  const S* vc = static_cast<const S*>(p.v_cache);
+  const S* kc = static_cast<const S*>(k_cache);
+  const S* vc = static_cast<const S*>(v_cache);
 
   // ---- tile staging: global -> register ring -> LDS.  A 64-key tile is split into
   // runs of KR = min(P, 64) keys that lie in one page; each thread owns a fixed set of
@@ -221,19 +225,19 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   for (int u = 0; u < V_PER_T; ++u) {
     const int ci = li + TPR * u;
     const int d = ci / KGR, kp = ci - (ci / KGR) * KGR;
-    v_goff[u] = (d << p.P_log2) + kp * EPC;
+    v_goff[u] = (d << P_log2) + kp * EPC;
     v_loff[u] = d * VROW + run * KR + kp * EPC;
     v_key[u] = run * KR + kp * EPC;              // first key of the chunk in the tile
   }
 
   // a page holds Hkv heads of P keys x D for K (token-major) and of D x P for V
   // (dim-major): the same element stride per page for both caches
-  const uint32_t pstride = static_cast<uint32_t>(p.Hkv * D) << p.P_log2;
-  const S* const kc_h = kc + (static_cast<size_t>(g * D) << p.P_log2);
-  const S* const vc_h = vc + (static_cast<size_t>(g * D) << p.P_log2);
+  const uint32_t pstride = static_cast<uint32_t>(Hkv * D) << P_log2;
+  const S* const kc_h = kc + (static_cast<size_t>(g * D) << P_log2);
+  const S* const vc_h = vc + (static_cast<size_t>(g * D) << P_log2);
   auto load_tile = [&](Tile& r, int kt, int pg) {
     r.pos0 = kt + run * KR;
-    r.page_ok = static_cast<unsigned>(pg) < static_cast<unsigned>(p.num_pages);
+    r.page_ok = static_cast<unsigned>(pg) < static_cast<unsigned>(num_pages);
     const uint32_t page = r.page_ok ? static_cast<uint32_t>(pg) : 0u;
     const uint32_t slot = static_cast<uint32_t>(r.pos0 & Pm1);
     const size_t poff = static_cast<size_t>(page) * pstride;   // one 32x32 -> 64-bit multiply
@@ -256,16 +260,16 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   const int ctx = ctx_raw < 0 ? 0 : (ctx_raw > p.max_ctx ? p.max_ctx : ctx_raw);
   const int n_keys = ctx + p.K;
   const bool dead = pad || k0 >= n_keys;
-  const int k1 = dead ? k0 : min(k0 + p.chunk, n_keys);
+  const int k1 = dead ? k0 : min(k0 + chunk, n_keys);
 #pragma unroll
   for (int u = 0; u < NPT; ++u) {
     const int i = tid + u * T;
     if (i < npg)
-      pg_lds[i] = static_cast<unsigned>(pg_all[u]) < static_cast<unsigned>(p.num_pages) ? pg_all[u] : -1;
+      pg_lds[i] = static_cast<unsigned>(pg_all[u]) < static_cast<unsigned>(num_pages) ? pg_all[u] : -1;
   }
   auto page_of = [&](int kt) {                   // page id of this thread's run of tile kt
     const int pos0 = kt + run * KR;
-    return pos0 < k1 ? pg_lds[(pos0 >> p.P_log2) - pg0] : -1;
+    return pos0 < k1 ? pg_lds[(pos0 >> P_log2) - pg0] : -1;
   };
 
   auto store_tile = [&](const Tile& r, int buf, int kt) {
@@ -445,7 +449,7 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
     // which is all the merge reads of it (its O rows keep whatever the workspace held)
     if (!pad) {
       for (int r = tid; r < p.R; r += T)
-        p.part_ml[((static_cast<size_t>(b) * p.Hkv + g) * p.nsplit + s) * p.R + r] =
+        p.part_ml[((static_cast<size_t>(b) * Hkv + g) * p.nsplit + s) * p.R + r] =
             make_float2(kNegBig, 0.0f);
     }
     return;
@@ -523,7 +527,7 @@ __global__ void __launch_bounds__(64 * RG * KW, 1) attn_split_kernel(const AttnP
   // (512 bytes for 16-bit data), and the merge reads every split of one (row block,
   // d block, quad) as a single contiguous stretch.
   const int RBT = (p.R + 31) >> 5;
-  const size_t bg = static_cast<size_t>(b) * p.Hkv + g;
+  const size_t bg = static_cast<size_t>(b) * Hkv + g;
 #pragma unroll
   for (int t = 0; t < NRB; ++t) {
     if (!active[t]) continue;
@@ -580,7 +584,8 @@ constexpr int kMergeWaves = 4;
 
 template <class Tag, int D, int BATCH>
 __global__ void __launch_bounds__(kMergeWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
-attn_merge_kernel(const AttnParams p) {
+attn_merge_kernel(const void* part_o, const float2* part_ml, int32_t R, int32_t B, int32_t Hkv,
+                  int32_t nsplit, const AttnParams p) {
   using S = typename Tag::store_t;
   constexpr int DB = D / 32;
   __shared__ f32x4 st[2][kMergeWaves][64];       // accumulator quad, (m, l) per lane
@@ -598,9 +603,9 @@ attn_merge_kernel(const AttnParams p) {
   // another and no branch comes before the loads (ids past the last pair read the last
   // pair and leave after the loads).
   constexpr int NX = 4 * DB;
-  const int RBT = (p.R + 31) >> 5;
+  const int RBT = (R + 31) >> 5;
   const int slot = blockIdx.x >> 3;
-  const int npairs = RBT * p.B * p.Hkv;
+  const int npairs = RBT * B * Hkv;
   const int pair_raw = (slot / NX) * 8 + (blockIdx.x & 7);
   const bool live = pair_raw < npairs;
   const int pair = live ? pair_raw : npairs - 1;
@@ -609,13 +614,13 @@ attn_merge_kernel(const AttnParams p) {
   const int q = x & 3;
   const int rb = pair % RBT;
   const int bg = pair / RBT;                     // b * Hkv + g
-  const int b = bg / p.Hkv;
-  const int g = bg - b * p.Hkv;
+  const int b = bg / Hkv;
+  const int g = bg - b * Hkv;
   const int r = rb * 32 + (lane & 31);
-  const bool valid = r < p.R;                    // padding rows of the last row block
-  const S* const po = static_cast<const S*>(p.part_o) +
-                      ((((static_cast<size_t>(bg) * RBT + rb) * DB + db) * 4 + q) * p.nsplit) * 256 + lane * 4;
-  const float2* const pml = p.part_ml + static_cast<size_t>(bg) * p.nsplit * p.R + min(r, p.R - 1);
+  const bool valid = r < R;                      // padding rows of the last row block
+  const S* const po = static_cast<const S*>(part_o) +
+                      ((((static_cast<size_t>(bg) * RBT + rb) * DB + db) * 4 + q) * nsplit) * 256 + lane * 4;
+  const float2* const pml = part_ml + static_cast<size_t>(bg) * nsplit * R + min(r, R - 1);
 
   float m_w = kNegBig, l_w = 0.0f;
   f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -623,19 +628,19 @@ attn_merge_kernel(const AttnParams p) {
   // indices -- a load under a branch would be waited for before the next one.  A split
   // with l = 0 (past its sequence's end; its O rows are stale workspace and may hold
   // anything) adds nothing: its O is replaced by zeros before it is weighted.
-  for (int s0 = wave; s0 < p.nsplit; s0 += kMergeWaves * BATCH) {
+  for (int s0 = wave; s0 < nsplit; s0 += kMergeWaves * BATCH) {
     float2 ml[BATCH];
     f32x4 o[BATCH];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const size_t sp = static_cast<size_t>(min(s0 + u * kMergeWaves, p.nsplit - 1));
-      ml[u] = pml[sp * p.R];
+      const size_t sp = static_cast<size_t>(min(s0 + u * kMergeWaves, nsplit - 1));
+      ml[u] = pml[sp * R];
       o[u] = load4<Tag>(po + sp * 256);
     }
     asm volatile("" ::: "memory");               // the whole batch is in flight before any use
 #pragma unroll
     for (int u = 0; u < BATCH; ++u)
-      if (s0 + u * kMergeWaves >= p.nsplit || !(ml[u].y > 0.0f)) {
+      if (s0 + u * kMergeWaves >= nsplit || !(ml[u].y > 0.0f)) {
         ml[u] = make_float2(kNegBig, 0.0f);
         o[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
@@ -691,20 +696,25 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   // run as up to four row groups of 128 rows of the same split.  One sequence issues its
   // start-up loads before reading its context length; a batch reads it first.
   const dim3 grid(p.nsplit_pad * p.row_halves, p.Hkv, p.B);
+#define SPLIT_ARGS p.page_table, p.k_cache, p.v_cache, p.ctx_lens, p.chunk, p.nsplit_pad, \
+                   p.P_log2, p.max_pages, p.num_pages, p.Hkv, p
+#define MERGE_ARGS p.part_o, p.part_ml, p.R, p.B, p.Hkv, p.nsplit, p
   constexpr int RING = Tag::kBytes == 2 ? kRingDeep : 2;
   if (p.B == 1) {
-    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, true>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, true>), grid, dim3(512), 0, stream, SPLIT_ARGS);
   } else {
-    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, false>), grid, dim3(512), 0, stream, p);
+    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, false>), grid, dim3(512), 0, stream, SPLIT_ARGS);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int pairs = (p.R + 31) / 32 * p.B * p.Hkv;
   const dim3 mgrid(D / 32 * 4 * ((pairs + 7) / 8 * 8));
   if (p.nsplit > 32)
-    hipLaunchKernelGGL((attn_merge_kernel<Tag, D, 16>), mgrid, dim3(kMergeWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_merge_kernel<Tag, D, 16>), mgrid, dim3(kMergeWaves * 64), 0, stream, MERGE_ARGS);
   else
-    hipLaunchKernelGGL((attn_merge_kernel<Tag, D, 8>), mgrid, dim3(kMergeWaves * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_merge_kernel<Tag, D, 8>), mgrid, dim3(kMergeWaves * 64), 0, stream, MERGE_ARGS);
+#undef SPLIT_ARGS
+#undef MERGE_ARGS
   return hipGetLastError();
 }
 

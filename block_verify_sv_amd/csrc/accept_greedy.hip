@@ -27,27 +27,29 @@ __device__ __forceinline__ float load_logit(const void* base, size_t i) {
   else return static_cast<const float*>(base)[i];
 }
 
+// The fields the first loads need come first as plain arguments (preloaded into SGPRs).
 template <bool kBF16>
-__global__ void __launch_bounds__(kThreads) greedy_argmax_kernel(const GreedyParams p) {
+__global__ void __launch_bounds__(kThreads)
+greedy_argmax_kernel(const void* logits, int32_t V, int32_t chunk, const GreedyParams p) {
   __shared__ uint64_t red[kThreads / kWave];
 
   const int tid = threadIdx.x;
   const int row = blockIdx.y;                     // b * K + i
-  const int j0 = blockIdx.x * p.chunk;
-  const int j1 = min(j0 + p.chunk, p.V);
-  const size_t rbase = static_cast<size_t>(row) * p.V;
+  const int j0 = blockIdx.x * chunk;
+  const int j1 = min(j0 + chunk, V);
+  const size_t rbase = static_cast<size_t>(row) * V;
 
   uint64_t best = 0;
   constexpr int EPV = kBF16 ? 8 : 4;              // elements per 16-byte load
-  if ((p.V % EPV) == 0) {
+  if ((V % EPV) == 0) {
     // per round every load is issued before any is consumed; indices past the row end
     // are clamped to its last 16 bytes (in bounds) and ignored below
     for (int jr = j0; jr < j1; jr += kLoadsPerThread * kThreads * EPV) {
       u32x4 v[kLoadsPerThread];
 #pragma unroll
       for (int u = 0; u < kLoadsPerThread; ++u) {
-        const int j = min(jr + (tid + u * kThreads) * EPV, p.V - EPV);
-        v[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.logits) +
+        const int j = min(jr + (tid + u * kThreads) * EPV, V - EPV);
+        v[u] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(logits) +
                                                (rbase + j) * (kBF16 ? 2 : 4));
       }
 #pragma unroll
@@ -66,7 +68,7 @@ __global__ void __launch_bounds__(kThreads) greedy_argmax_kernel(const GreedyPar
     }
   } else {
     for (int j = j0 + tid; j < j1; j += kThreads) {
-      const uint64_t key = argmax_key(load_logit<kBF16>(p.logits, rbase + j), static_cast<uint32_t>(j));
+      const uint64_t key = argmax_key(load_logit<kBF16>(logits, rbase + j), static_cast<uint32_t>(j));
       best = key > best ? key : best;
     }
   }
@@ -83,21 +85,22 @@ __global__ void __launch_bounds__(kThreads) greedy_argmax_kernel(const GreedyPar
 
 constexpr int kWalkSeqs = kThreads / kWave;       // sequences per walk workgroup
 
-__global__ void __launch_bounds__(kThreads) greedy_walk_kernel(const GreedyParams p) {
+__global__ void __launch_bounds__(kThreads)
+greedy_walk_kernel(const unsigned long long* chunk_keys, const int32_t* drafts, int32_t B, int32_t K,
+                   int32_t nchunk, const GreedyParams p) {
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.x * kWalkSeqs + (threadIdx.x >> 6);
-  if (b >= p.B) return;                           // whole waves
-  const int K = p.K;
+  if (b >= B) return;                             // whole waves
   const bool in = lane < K;
   // lane i reduces row i's chunk keys (at most kMaxChunks; plain data written by the
   // argmax pass; all loads in flight, clamped index)
-  const unsigned long long* keys = p.keys + static_cast<size_t>(b) * K * p.nchunk;
+  const unsigned long long* keys = chunk_keys + static_cast<size_t>(b) * K * nchunk;
   uint64_t best = 0;
   if (in) {
     uint64_t k[kMaxChunks];
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c)
-      k[c] = keys[static_cast<size_t>(lane) * p.nchunk + min(c, p.nchunk - 1)];
+      k[c] = keys[static_cast<size_t>(lane) * nchunk + min(c, nchunk - 1)];
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) best = k[c] > best ? k[c] : best;
   }
@@ -107,7 +110,7 @@ __global__ void __launch_bounds__(kThreads) greedy_walk_kernel(const GreedyParam
     if (p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
   }
   // draft k+1 (drafts[b][k]) is checked against row k's choice, k = 0 .. K-2
-  const int32_t d = lane < K - 1 ? p.drafts[static_cast<size_t>(b) * (K - 1) + lane] : 0;
+  const int32_t d = lane < K - 1 ? drafts[static_cast<size_t>(b) * (K - 1) + lane] : 0;
   const uint64_t miss = __ballot(lane < K - 1 && d != t);
   const int a = miss ? __builtin_ctzll(miss) : K - 1;   // accepted drafts
   const int32_t corr = __shfl(t, a);
@@ -121,19 +124,21 @@ __global__ void __launch_bounds__(kThreads) greedy_walk_kernel(const GreedyParam
 // numbered above it and hold its greedy token picks the lowest such lane as the next
 // node.  Each step raises the node number, so the walk ends within K-1 steps whatever
 // the parent array holds.
-__global__ void __launch_bounds__(kThreads) greedy_tree_walk_kernel(const GreedyParams p) {
+__global__ void __launch_bounds__(kThreads)
+greedy_tree_walk_kernel(const unsigned long long* chunk_keys, const int32_t* drafts,
+                        const int32_t* parents, int32_t B, int32_t K, int32_t nchunk,
+                        const GreedyParams p) {
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.x * kWalkSeqs + (threadIdx.x >> 6);
-  if (b >= p.B) return;                           // whole waves
-  const int K = p.K;
+  if (b >= B) return;                             // whole waves
   const bool in = lane < K;
-  const unsigned long long* keys = p.keys + static_cast<size_t>(b) * K * p.nchunk;
+  const unsigned long long* keys = chunk_keys + static_cast<size_t>(b) * K * nchunk;
   uint64_t best = 0;
   if (in) {
     uint64_t k[kMaxChunks];
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c)
-      k[c] = keys[static_cast<size_t>(lane) * p.nchunk + min(c, p.nchunk - 1)];
+      k[c] = keys[static_cast<size_t>(lane) * nchunk + min(c, nchunk - 1)];
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) best = k[c] > best ? k[c] : best;
   }
@@ -144,8 +149,8 @@ __global__ void __launch_bounds__(kThreads) greedy_tree_walk_kernel(const Greedy
   }
   const bool node = lane >= 1 && lane < K;        // a draft node
   const size_t nb = static_cast<size_t>(b) * (K - 1) + (lane - 1);
-  const int32_t par = node ? p.parents[nb] : -1;
-  const int32_t tok = node ? p.drafts[nb] : 0;
+  const int32_t par = node ? parents[nb] : -1;
+  const int32_t tok = node ? drafts[nb] : 0;
   int cur = 0, a = 0;
   int32_t my_path = lane == 0 ? 0 : -1;           // lane j ends up holding path[j]
   for (int step = 1; step < K; ++step) {
@@ -184,9 +189,11 @@ int greedy_chunk(int V, sv_dtype dtype) {
 hipError_t launch_greedy(const GreedyParams& p, sv_dtype dtype, hipStream_t stream) {
   const dim3 grid(p.nchunk, p.B * p.K);
   if (dtype == SV_BF16)
-    hipLaunchKernelGGL(greedy_argmax_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(greedy_argmax_kernel<true>, grid, dim3(kThreads), 0, stream, p.logits, p.V,
+                       p.chunk, p);
   else
-    hipLaunchKernelGGL(greedy_argmax_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(greedy_argmax_kernel<false>, grid, dim3(kThreads), 0, stream, p.logits, p.V,
+                       p.chunk, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_greedy_walk(p, stream);
@@ -195,10 +202,10 @@ hipError_t launch_greedy(const GreedyParams& p, sv_dtype dtype, hipStream_t stre
 hipError_t launch_greedy_walk(const GreedyParams& p, hipStream_t stream) {
   if (p.tree)
     hipLaunchKernelGGL(greedy_tree_walk_kernel, dim3((p.B + kWalkSeqs - 1) / kWalkSeqs),
-                       dim3(kThreads), 0, stream, p);
+                       dim3(kThreads), 0, stream, p.keys, p.drafts, p.parents, p.B, p.K, p.nchunk, p);
   else
     hipLaunchKernelGGL(greedy_walk_kernel, dim3((p.B + kWalkSeqs - 1) / kWalkSeqs),
-                       dim3(kThreads), 0, stream, p);
+                       dim3(kThreads), 0, stream, p.keys, p.drafts, p.B, p.K, p.nchunk, p);
   return hipGetLastError();
 }
 

@@ -73,35 +73,39 @@ __device__ __forceinline__ float logit_at(const void* base, size_t i) {
   else return static_cast<const float*>(base)[i];
 }
 
-// Row rho < B*K is target row rho; otherwise draft row rho - B*K.
+// Row rho < nt = B*K is target row rho; otherwise draft row rho - B*K.
 template <bool kBF16>
-__device__ __forceinline__ const void* row_ptr(const SampleParams& p, int rho) {
-  const int nt = p.B * p.K;
+__device__ __forceinline__ const void* row_ptr(const void* target, const void* draft, int nt, int V,
+                                               int rho) {
   const size_t esz = kBF16 ? 2 : 4;
-  if (rho < nt) return static_cast<const char*>(p.target) + static_cast<size_t>(rho) * p.V * esz;
-  return static_cast<const char*>(p.draft) + static_cast<size_t>(rho - nt) * p.V * esz;
+  if (rho < nt) return static_cast<const char*>(target) + static_cast<size_t>(rho) * V * esz;
+  return static_cast<const char*>(draft) + static_cast<size_t>(rho - nt) * V * esz;
 }
 
+// Each kernel takes the fields its first loads need as leading plain arguments
+// (preloaded into SGPRs), then the whole parameter block.
 template <bool kBF16>
-__global__ void __launch_bounds__(kLseThreads) row_lse_kernel(const SampleParams p) {
+__global__ void __launch_bounds__(kLseThreads)
+row_lse_kernel(const void* target, const void* draft, int32_t B, int32_t K, int32_t V,
+               int32_t chunk, const SampleParams p) {
   __shared__ float redf[kLseThreads / kWave];
   __shared__ double redd[kLseThreads / kWave];
   const int tid = threadIdx.x;
   const int c = blockIdx.x;
   const int rho = blockIdx.y;
-  const void* x = row_ptr<kBF16>(p, rho);
-  const int j0 = c * p.chunk;
-  const int j1 = min(j0 + p.chunk, p.V);
+  const void* x = row_ptr<kBF16>(target, draft, B * K, V, rho);
+  const int j0 = c * chunk;
+  const int j1 = min(j0 + chunk, V);
   constexpr int EPL = kBF16 ? 8 : 4;               // elements per 16-byte load
   constexpr int kLoads = kLseChunk / (kLseThreads * EPL);
   constexpr int kMaxPer = kLoads * EPL;
   float v[kMaxPer];
-  if ((p.V % EPL) == 0) {
+  if ((V % EPL) == 0) {
     // every load issued before any is consumed; clamped (in-bounds) indices past the
     // row end are masked afterwards
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
-      const int j = min(j0 + (tid + u * kLseThreads) * EPL, p.V - EPL);
+      const int j = min(j0 + (tid + u * kLseThreads) * EPL, V - EPL);
       const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const char*>(x) +
                                                        static_cast<size_t>(j) * (kBF16 ? 2 : 4));
 #pragma unroll
@@ -119,7 +123,7 @@ __global__ void __launch_bounds__(kLseThreads) row_lse_kernel(const SampleParams
 #pragma unroll
     for (int e = 0; e < kMaxPer; ++e) {
       const int j = j0 + tid + e * kLseThreads;
-      v[e] = logit_at<kBF16>(x, min(j, p.V - 1));
+      v[e] = logit_at<kBF16>(x, min(j, V - 1));
     }
 #pragma unroll
     for (int e = 0; e < kMaxPer; ++e)
@@ -185,7 +189,10 @@ __device__ __forceinline__ void block_best(double& bk_r, int32_t& bi_r, double& 
 }
 
 template <bool kBF16>
-__global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParams p) {
+__global__ void __launch_bounds__(kThreads)
+sample_race_kernel(const void* target, const void* draft, const int32_t* drafts, const float* part_m,
+                   const double* part_s, int32_t B, int32_t K, int32_t V, int32_t nchunk,
+                   const SampleParams p) {
   __shared__ double Lrow[2 * kMaxBlock];
   __shared__ int32_t a_sh;
   __shared__ double rk[2][kThreads / kWave];
@@ -194,20 +201,19 @@ __global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParam
   const int tid = threadIdx.x;
   const int c = blockIdx.x;
   const int b = blockIdx.y;
-  const int K = p.K;
   const double it = p.inv_t;
-  const int32_t* dr = p.drafts + static_cast<size_t>(b) * (K - 1);
+  const int32_t* dr = drafts + static_cast<size_t>(b) * (K - 1);
 
   // ---- loads that need nothing computed here, issued together: the drafted tokens'
   // logits for the ratio tests (lane k-1 of wave 0 tests draft k) ...
   const bool tester = tid < K - 1;
   int32_t d = tester ? dr[tid] : 0;
-  const bool in_vocab = d >= 0 && d < p.V;
+  const bool in_vocab = d >= 0 && d < V;
   const int dc = in_vocab ? d : 0;
   const double lp = tester ? static_cast<double>(logit_at<kBF16>(
-      p.target, (static_cast<size_t>(b) * K + tid) * p.V + dc)) : 0.0;
+      target, (static_cast<size_t>(b) * K + tid) * V + dc)) : 0.0;
   const double lq = tester ? static_cast<double>(logit_at<kBF16>(
-      p.draft, (static_cast<size_t>(b) * (K - 1) + tid) * p.V + dc)) : 0.0;
+      draft, (static_cast<size_t>(b) * (K - 1) + tid) * V + dc)) : 0.0;
   // ... and the log-normalisers of the K target rows, then the K-1 draft rows: lpr
   // lanes (a power of two, aligned in the wave) share a row, each folding every lpr-th
   // chunk partial, then combine by shuffles
@@ -218,14 +224,14 @@ __global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParam
     const int row = tid / lpr, sub = tid - row * lpr;
     const bool has = row < nrows;
     const int rr = has ? row : 0;
-    const int rho = rr < K ? b * K + rr : p.B * K + b * (K - 1) + (rr - K);
-    const float* pm = p.part_m + static_cast<size_t>(rho) * p.nchunk;
-    const double* ps = p.part_s + static_cast<size_t>(rho) * p.nchunk;
+    const int rho = rr < K ? b * K + rr : B * K + b * (K - 1) + (rr - K);
+    const float* pm = part_m + static_cast<size_t>(rho) * nchunk;
+    const double* ps = part_s + static_cast<size_t>(rho) * nchunk;
     float m = -INFINITY;
-    for (int q = sub; q < p.nchunk; q += lpr) m = fmaxf(m, pm[q]);
+    for (int q = sub; q < nchunk; q += lpr) m = fmaxf(m, pm[q]);
     for (int o = 1; o < lpr; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
     double s = 0.0;
-    for (int q = sub; q < p.nchunk; q += lpr)
+    for (int q = sub; q < nchunk; q += lpr)
       s += ps[q] * exp((static_cast<double>(pm[q]) - static_cast<double>(m)) * it);
     for (int o = 1; o < lpr; o <<= 1) s += __shfl_xor(s, o);
     if (has && sub == 0) Lrow[row] = static_cast<double>(m) * it + log(s);
@@ -258,20 +264,20 @@ __global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParam
   const bool resid = a < K - 1;
   const double Lp = Lrow[a];
   const double Lq = resid ? Lrow[K + a] : 0.0;
-  const size_t prow = (static_cast<size_t>(b) * K + a) * p.V;
-  const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (resid ? a : 0)) * p.V;
+  const size_t prow = (static_cast<size_t>(b) * K + a) * V;
+  const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (resid ? a : 0)) * V;
 
   // ---- exponential race over this chunk: one Philox block of 4 tokens per thread
   const int jb = c * p.race_chunk + 4 * tid;
   double bk_r = INFINITY, bk_p = INFINITY;
   int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
-  if (jb < p.V) {
+  if (jb < V) {
     float xp[4], xq[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {                 // clamped, in bounds; masked below
-      const int j = min(jb + e, p.V - 1);
-      xp[e] = logit_at<kBF16>(p.target, prow + j);
-      xq[e] = logit_at<kBF16>(p.draft, qrow + j);
+      const int j = min(jb + e, V - 1);
+      xp[e] = logit_at<kBF16>(target, prow + j);
+      xq[e] = logit_at<kBF16>(draft, qrow + j);
     }
     const uint64_t c2 = (1ull << 32) | static_cast<uint64_t>(a);
     const U64x4 w = philox(p.offset, static_cast<uint64_t>(b), c2, static_cast<uint64_t>(jb >> 2),
@@ -279,7 +285,7 @@ __global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParam
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = jb + e;
-      if (j >= p.V) break;
+      if (j >= V) break;
       const double pj = exp(static_cast<double>(xp[e]) * it - Lp);
       double rj = pj;
       if (resid) rj = fmax(0.0, pj - exp(static_cast<double>(xq[e]) * it - Lq));
@@ -306,26 +312,27 @@ __global__ void __launch_bounds__(kThreads) sample_race_kernel(const SampleParam
 
 // One workgroup per sequence: the race winner over every chunk (the (key, index) minimum
 // is order-independent), then the outputs.
-__global__ void __launch_bounds__(kThreads) sample_finish_kernel(const SampleParams p) {
+__global__ void __launch_bounds__(kThreads)
+sample_finish_kernel(const double* race_key, const int32_t* race_idx, const int32_t* decision,
+                     const int32_t* drafts, int32_t K, int32_t race_nchunk, const SampleParams p) {
   __shared__ double rk[2][kThreads / kWave];
   __shared__ int32_t ri[2][kThreads / kWave];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const int K = p.K;
   double bk_r = INFINITY, bk_p = INFINITY;
   int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
-  for (int q = tid; q < p.race_nchunk; q += kThreads) {
-    const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + q) * 2;
-    const double k0 = p.race_key[slot], k1 = p.race_key[slot + 1];
-    const int32_t i0 = p.race_idx[slot], i1 = p.race_idx[slot + 1];
+  for (int q = tid; q < race_nchunk; q += kThreads) {
+    const size_t slot = (static_cast<size_t>(b) * race_nchunk + q) * 2;
+    const double k0 = race_key[slot], k1 = race_key[slot + 1];
+    const int32_t i0 = race_idx[slot], i1 = race_idx[slot + 1];
     if (better(k0, i0, bk_r, bi_r)) { bk_r = k0; bi_r = i0; }
     if (better(k1, i1, bk_p, bi_p)) { bk_p = k1; bi_p = i1; }
   }
   block_best(bk_r, bi_r, bk_p, bi_p, rk, ri);
-  const int a = p.decision[b];
+  const int a = decision[b];
   const int32_t token = (bk_r < INFINITY) ? bi_r : bi_p;
   if (tid < K) {
-    const int32_t* dr = p.drafts + static_cast<size_t>(b) * (K - 1);
+    const int32_t* dr = drafts + static_cast<size_t>(b) * (K - 1);
     p.out_tokens[static_cast<size_t>(b) * K + tid] = tid < a ? dr[tid] : (tid == a ? token : -1);
   }
   if (tid == 0) p.accept_len[b] = a;
@@ -359,20 +366,25 @@ size_t sample_workspace_bytes(int B, int K, int V) {
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stream) {
   const dim3 g1(p.nchunk, p.B * (2 * p.K - 1));
   const dim3 g2(p.race_nchunk, p.B);
+#define LSE_ARGS p.target, p.draft, p.B, p.K, p.V, p.chunk, p
+#define RACE_ARGS p.target, p.draft, p.drafts, p.part_m, p.part_s, p.B, p.K, p.V, p.nchunk, p
   if (dtype == SV_BF16) {
-    hipLaunchKernelGGL(row_lse_kernel<true>, g1, dim3(kLseThreads), 0, stream, p);
+    hipLaunchKernelGGL(row_lse_kernel<true>, g1, dim3(kLseThreads), 0, stream, LSE_ARGS);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sample_race_kernel<true>, g2, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(sample_race_kernel<true>, g2, dim3(kThreads), 0, stream, RACE_ARGS);
   } else {
-    hipLaunchKernelGGL(row_lse_kernel<false>, g1, dim3(kLseThreads), 0, stream, p);
+    hipLaunchKernelGGL(row_lse_kernel<false>, g1, dim3(kLseThreads), 0, stream, LSE_ARGS);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sample_race_kernel<false>, g2, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(sample_race_kernel<false>, g2, dim3(kThreads), 0, stream, RACE_ARGS);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sample_finish_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(sample_finish_kernel, dim3(p.B), dim3(kThreads), 0, stream, p.race_key,
+                     p.race_idx, p.decision, p.drafts, p.K, p.race_nchunk, p);
+#undef LSE_ARGS
+#undef RACE_ARGS
   return hipGetLastError();
 }
 

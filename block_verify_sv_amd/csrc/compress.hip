@@ -32,7 +32,11 @@ __host__ __device__ __forceinline__ int pad_n(int N) { return (N + kNT - 1) / kN
 // pass adds them in order).  Both operands are staged in 64-d steps: coalesced 16-byte
 // loads (8 lanes per 128-byte row segment) into a register ring kSRing-1 steps ahead,
 // then padded LDS tiles that the four 32x32 MFMA blocks read.
-__global__ void __launch_bounds__(kThreads) scores_kernel(const CompressParams p) {
+// Kernels take the fields their first loads need as leading plain arguments (preloaded
+// into SGPRs), then the whole parameter block.
+__global__ void __launch_bounds__(kThreads)
+scores_kernel(const void* queries, const void* feats, float* scores, int32_t B, int32_t C,
+              int32_t N, int32_t D, const CompressParams p) {
   constexpr int ROW = kSK + 8;                     // LDS row: 64 d + 16 bytes of padding
   __shared__ __align__(16) uint16_t q_lds[2][64 * ROW];
   __shared__ __align__(16) uint16_t f_lds[2][64 * ROW];
@@ -42,9 +46,9 @@ __global__ void __launch_bounds__(kThreads) scores_kernel(const CompressParams p
   const int n0 = blockIdx.x * 64;
   const int b = blockIdx.y;
   const int kh = blockIdx.z;
-  const bool active = wc * 32 < p.C;
-  const int steps = (p.D >> 1) / kSK;
-  const int dbeg = kh * (p.D >> 1);
+  const bool active = wc * 32 < C;
+  const int steps = (D >> 1) / kSK;
+  const int dbeg = kh * (D >> 1);
   // load mapping: chunk ch = tid + 256u covers row ch/8, 8 halves at column 8*(ch%8);
   // rows past C (queries) or N (features) are clamped in bounds and never stored
   const uint16_t* qsrc[2];
@@ -54,9 +58,9 @@ __global__ void __launch_bounds__(kThreads) scores_kernel(const CompressParams p
   for (int u = 0; u < 2; ++u) {
     const int ch = tid + kThreads * u;
     const int r = ch >> 3, col = (ch & 7) * 8;
-    qsrc[u] = static_cast<const uint16_t*>(p.queries) + static_cast<size_t>(min(r, p.C - 1)) * p.D + dbeg + col;
-    fsrc[u] = static_cast<const uint16_t*>(p.feats) +
-              (static_cast<size_t>(b) * p.N + min(n0 + r, p.N - 1)) * p.D + dbeg + col;
+    qsrc[u] = static_cast<const uint16_t*>(queries) + static_cast<size_t>(min(r, C - 1)) * D + dbeg + col;
+    fsrc[u] = static_cast<const uint16_t*>(feats) +
+              (static_cast<size_t>(b) * N + min(n0 + r, N - 1)) * D + dbeg + col;
     loff[u] = r * ROW + col;
   }
   struct ST { u32x4 q[2], f[2]; };
@@ -108,40 +112,42 @@ __global__ void __launch_bounds__(kThreads) scores_kernel(const CompressParams p
     }
   }
   const int n = n0 + wn * 32 + l32;
-  if (!active || n >= p.N) return;
-  float* srow = p.scores + (static_cast<size_t>(kh) * p.B + b) * p.C * p.N + n;
+  if (!active || n >= N) return;
+  float* srow = scores + (static_cast<size_t>(kh) * B + b) * C * N + n;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int cc = wc * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-    if (cc < p.C) srow[static_cast<size_t>(cc) * p.N] = acc[r];
+    if (cc < C) srow[static_cast<size_t>(cc) * N] = acc[r];
   }
 }
 
 // One wave per query row (rows C..63 get zero weights and sum 1).
-__global__ void __launch_bounds__(kThreads) softmax_kernel(const CompressParams p) {
+__global__ void __launch_bounds__(kThreads)
+softmax_kernel(const float* scores, uint16_t* weights, float* rowsum, int32_t B, int32_t C,
+               int32_t N, float scale, const CompressParams p) {
   constexpr int kPer = 1024 / 64;                  // scores per lane (N <= 1024)
   const int lane = threadIdx.x & 63;
   const int c = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int b = blockIdx.y;
-  const int Nw = pad_n(p.N);
-  uint16_t* wr = p.weights + (static_cast<size_t>(b) * kMaxC + c) * Nw;
-  if (c >= p.C) {
+  const int Nw = pad_n(N);
+  uint16_t* wr = weights + (static_cast<size_t>(b) * kMaxC + c) * Nw;
+  if (c >= C) {
     for (int n = lane; n < Nw; n += 64) wr[n] = 0;
-    if (lane == 0) p.rowsum[b * kMaxC + c] = 1.0f;
+    if (lane == 0) rowsum[b * kMaxC + c] = 1.0f;
     return;
   }
-  const float* s0 = p.scores + (static_cast<size_t>(b) * p.C + c) * p.N;
-  const float* s1 = s0 + static_cast<size_t>(p.B) * p.C * p.N;   // second contraction half
+  const float* s0 = scores + (static_cast<size_t>(b) * C + c) * N;
+  const float* s1 = s0 + static_cast<size_t>(B) * C * N;   // second contraction half
   float s[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {                 // all loads in flight
-    const int n = min(lane + 64 * i, p.N - 1);
-    s[i] = (s0[n] + s1[n]) * p.scale;
+    const int n = min(lane + 64 * i, N - 1);
+    s[i] = (s0[n] + s1[n]) * scale;
   }
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if (lane + 64 * i < p.N) m = fmaxf(m, s[i]);
+    if (lane + 64 * i < N) m = fmaxf(m, s[i]);
   m = wave_max(m);
   float sum = 0.0f;
 #pragma unroll
@@ -149,7 +155,7 @@ __global__ void __launch_bounds__(kThreads) softmax_kernel(const CompressParams 
     const int n = lane + 64 * i;
     if (n >= Nw) break;
     uint16_t wv = 0;
-    if (n < p.N) {
+    if (n < N) {
       wv = f32_to_f16(__expf(s[i] - m));
       sum += f16_to_f32(wv);
     }
@@ -157,7 +163,7 @@ __global__ void __launch_bounds__(kThreads) softmax_kernel(const CompressParams 
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
-  if (lane == 0) p.rowsum[b * kMaxC + c] = sum;
+  if (lane == 0) rowsum[b * kMaxC + c] = sum;
 }
 
 // LDS transpose read (gfx950): within each 16-lane group, lane i receives 16-bit element
@@ -173,7 +179,9 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 // wave then owns 4 column blocks of 32), else 128 (2 blocks).  The weight operand is read once per feature tile
 // for all DT columns, so the wider tile halves the weight re-reads per feature byte.
 template <int DT>
-__global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
+__global__ void __launch_bounds__(kThreads)
+out_kernel(const void* feats, const uint16_t* weights, const float* rowsum, const float* scores,
+           void* out, int32_t B, int32_t C, int32_t N, int32_t D, const CompressParams p) {
   // feature tile row: DT columns padded by 32 halves (DT + 32 halves = 16 banks mod 64),
   // so the four rows one half-wave's transpose read touches start 16 banks apart
   constexpr int FROW = DT + 32;
@@ -188,22 +196,21 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
   const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int b = blockIdx.y;
   const int dbase = blockIdx.x * DT;
-  const int N = p.N;
   const int Nw = pad_n(N);
-  if (tid < kMaxC) rsum[tid] = p.rowsum[b * kMaxC + tid];
+  if (tid < kMaxC) rsum[tid] = rowsum[b * kMaxC + tid];
 
   // ---- out tile: wave (wc, wd) owns query rows 32*wc.. and columns (DT/2)*wd.. (NB
   // blocks).
   // The weight operand (8 consecutive feature rows of one query row per lane) comes
   // straight from the workspace (cache-resident: every d tile of the image reads it).
   const int wc = wave >> 1, wd = wave & 1;
-  const bool active = wc * 32 < p.C;
+  const bool active = wc * 32 < C;
   // transpose-read address of this lane: lane 4j + q of a 16-lane group points at row
   // 8h + j, columns 16*(group & 1) + 4q .. +3, so lane i of the group receives rows
   // 8h .. 8h+3 of column 16*(group & 1) + i: the MFMA B operand's layout
   const int grp = lane >> 4, i16 = lane & 15;
   const int tr_off = (h * 8 + (i16 >> 2)) * FROW + (grp & 1) * 16 + 4 * (i16 & 3);
-  const uint16_t* wsrc = p.weights + (static_cast<size_t>(b) * kMaxC + wc * 32 + l32) * Nw + h * 8;
+  const uint16_t* wsrc = weights + (static_cast<size_t>(b) * kMaxC + wc * 32 + l32) * Nw + h * 8;
   f32x16 acc[NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t)
@@ -213,7 +220,7 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
   // feature tiles: kNT rows x DT columns in chunks of 16 B, CPT per thread, held in a
   // register ring with the tile's weight operands; tile rows past N (the last tile)
   // re-read row N-1 and meet weights that are zero
-  const uint16_t* fb = static_cast<const uint16_t*>(p.feats) + static_cast<size_t>(b) * N * p.D;
+  const uint16_t* fb = static_cast<const uint16_t*>(feats) + static_cast<size_t>(b) * N * D;
   const int nt_count = Nw / kNT;
   struct FT { u32x4 v[CPT]; u32x4 a[kNT / 16]; };
   auto load = [&](FT& f, int t) {
@@ -222,7 +229,7 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
     for (int u = 0; u < CPT; ++u) {
       const int ch = tid + kThreads * u;
       const int r = min(nt + ch / CPR, N - 1);
-      f.v[u] = *reinterpret_cast<const u32x4*>(fb + static_cast<size_t>(r) * p.D + dbase + (ch % CPR) * 8);
+      f.v[u] = *reinterpret_cast<const u32x4*>(fb + static_cast<size_t>(r) * D + dbase + (ch % CPR) * 8);
     }
 #pragma unroll
     for (int ks = 0; ks < kNT / 16; ++ks) f.a[ks] = *reinterpret_cast<const u32x4*>(wsrc + nt + ks * 16);
@@ -266,14 +273,14 @@ __global__ void __launch_bounds__(kThreads) out_kernel(const CompressParams p) {
     }
   }
   if (!active) return;
-  uint16_t* ob = static_cast<uint16_t*>(p.out) + static_cast<size_t>(b) * p.C * p.D;
+  uint16_t* ob = static_cast<uint16_t*>(out) + static_cast<size_t>(b) * C * D;
 #pragma unroll
   for (int t = 0; t < NB; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int c = wc * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (c < p.C)
-        ob[static_cast<size_t>(c) * p.D + dbase + wd * (DT / 2) + t * 32 + l32] =
+      if (c < C)
+        ob[static_cast<size_t>(c) * D + dbase + wd * (DT / 2) + t * 32 + l32] =
             f32_to_f16(acc[t][r] / rsum[c]);
     }
 }
@@ -296,17 +303,21 @@ void compress_bind_workspace(CompressParams& p, void* workspace) {
 }
 
 hipError_t launch_compress(const CompressParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(scores_kernel, dim3((p.N + 63) / 64, p.B, 2), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(scores_kernel, dim3((p.N + 63) / 64, p.B, 2), dim3(kThreads), 0, stream,
+                     p.queries, p.feats, p.scores, p.B, p.C, p.N, p.D, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(softmax_kernel, dim3(kMaxC / (kThreads / 64), p.B), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(softmax_kernel, dim3(kMaxC / (kThreads / 64), p.B), dim3(kThreads), 0, stream,
+                     p.scores, p.weights, p.rowsum, p.B, p.C, p.N, p.scale, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the wide tile pays off on long feature streams (measured: N = 576 -6%, N = 324 +1%)
   if (p.D % 256 == 0 && p.N > 384)
-    hipLaunchKernelGGL(out_kernel<256>, dim3(p.D / 256, p.B), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(out_kernel<256>, dim3(p.D / 256, p.B), dim3(kThreads), 0, stream,
+                       p.feats, p.weights, p.rowsum, p.scores, p.out, p.B, p.C, p.N, p.D, p);
   else
-    hipLaunchKernelGGL(out_kernel<128>, dim3(p.D / 128, p.B), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(out_kernel<128>, dim3(p.D / 128, p.B), dim3(kThreads), 0, stream,
+                       p.feats, p.weights, p.rowsum, p.scores, p.out, p.B, p.C, p.N, p.D, p);
   return hipGetLastError();
 }
 

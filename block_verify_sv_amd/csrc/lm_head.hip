@@ -47,26 +47,30 @@ __device__ __forceinline__ f32x4v mfma16<TagF16>(u32x4 a, u32x4 b, f32x4v c) {
 // columns: lane (j, g) reads the 16*SUB contiguous bytes at columns 8*SUB*g .. of the
 // step, and its c-th 16-byte piece feeds MFMA c of the step.  With SUB = 2 the four lanes
 // of a row read one 128-byte line per step.
+// Kernels take the fields their first loads need as leading plain arguments (preloaded
+// into SGPRs), then the whole parameter block.
 template <class Tag, int MT, int SUB, int RING>
-__global__ void __launch_bounds__(kThreads) lm_head_argmax_kernel(const LmHeadParams p) {
+__global__ void __launch_bounds__(kThreads)
+lm_head_argmax_kernel(const void* hidden, const void* weight, int32_t M, int32_t V, int32_t Hd,
+                      const LmHeadParams p) {
   __shared__ uint64_t red[kThreads / kWave][16 * MT];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int v0 = blockIdx.x * (kThreads / kWave) * kRowsPerWave + wave * kRowsPerWave;
-  const uint16_t* W = static_cast<const uint16_t*>(p.weight);
-  const uint16_t* H = static_cast<const uint16_t*>(p.hidden);
+  const uint16_t* W = static_cast<const uint16_t*>(weight);
+  const uint16_t* H = static_cast<const uint16_t*>(hidden);
   // rows past V or M are clamped in bounds; their keys are never kept
   const uint16_t* wrow[kBlocks];
 #pragma unroll
   for (int nb = 0; nb < kBlocks; ++nb)
-    wrow[nb] = W + static_cast<size_t>(min(v0 + 16 * nb + l16, p.V - 1)) * p.Hd + 8 * SUB * g;
+    wrow[nb] = W + static_cast<size_t>(min(v0 + 16 * nb + l16, V - 1)) * Hd + 8 * SUB * g;
   const uint16_t* hrow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    hrow[mt] = H + static_cast<size_t>(min(16 * mt + l16, p.M - 1)) * p.Hd + 8 * SUB * g;
+    hrow[mt] = H + static_cast<size_t>(min(16 * mt + l16, M - 1)) * Hd + 8 * SUB * g;
 
-  const int steps = p.Hd / (32 * SUB);
+  const int steps = Hd / (32 * SUB);
   struct St { u32x4 w[kBlocks][SUB]; u32x4 h[MT][SUB]; };
   auto load = [&](St& s, int st) {
     const int k = min(st, steps - 1) * 32 * SUB;  // past the end: re-read the last step
@@ -123,7 +127,7 @@ __global__ void __launch_bounds__(kThreads) lm_head_argmax_kernel(const LmHeadPa
 #pragma unroll
       for (int nb = 0; nb < kBlocks; ++nb) {
         const int v = v0 + 16 * nb + l16;
-        const uint64_t key = v < p.V ? argmax_key(acc[mt][nb][r], static_cast<uint32_t>(v)) : 0;
+        const uint64_t key = v < V ? argmax_key(acc[mt][nb][r], static_cast<uint32_t>(v)) : 0;
         best = key > best ? key : best;
       }
 #pragma unroll
@@ -135,7 +139,7 @@ __global__ void __launch_bounds__(kThreads) lm_head_argmax_kernel(const LmHeadPa
     }
   }
   __syncthreads();
-  if (tid < p.M) {
+  if (tid < M) {
     uint64_t best = red[0][tid];
 #pragma unroll
     for (int w = 1; w < kThreads / kWave; ++w) best = red[w][tid] > best ? red[w][tid] : best;
@@ -144,12 +148,14 @@ __global__ void __launch_bounds__(kThreads) lm_head_argmax_kernel(const LmHeadPa
 }
 
 // One workgroup per row: the maximum of the row's per-workgroup keys.
-__global__ void __launch_bounds__(kThreads) lm_head_reduce_kernel(const LmHeadParams p) {
+__global__ void __launch_bounds__(kThreads)
+lm_head_reduce_kernel(const unsigned long long* part, int32_t M, int32_t nwg,
+                      const LmHeadParams p) {
   __shared__ uint64_t red[kThreads / kWave];
   const int row = blockIdx.x, tid = threadIdx.x;
-  const unsigned long long* src = p.part + static_cast<size_t>(row) * p.nwg;
+  const unsigned long long* src = part + static_cast<size_t>(row) * nwg;
   uint64_t best = 0;
-  for (int i = tid; i < p.nwg; i += kThreads) best = src[i] > best ? static_cast<uint64_t>(src[i]) : best;
+  for (int i = tid; i < nwg; i += kThreads) best = src[i] > best ? static_cast<uint64_t>(src[i]) : best;
   best = wave_max_u64(best);
   if ((tid & 63) == 0) red[tid >> 6] = best;
   __syncthreads();
@@ -166,13 +172,17 @@ template <class Tag>
 hipError_t launch_typed(const LmHeadParams& p, hipStream_t stream) {
   const dim3 grid(p.nwg), block(kThreads);
   if (p.M <= 16 && p.Hd % (32 * kSub) == 0)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, kSub, 4>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, kSub, 4>), grid, block, 0, stream,
+                       p.hidden, p.weight, p.M, p.V, p.Hd, p);
   else if (p.M <= 16)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, 1, 6>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, 1, 6>), grid, block, 0, stream,
+                       p.hidden, p.weight, p.M, p.V, p.Hd, p);
   else if (p.M <= 32)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 2, 1, 6>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 2, 1, 6>), grid, block, 0, stream,
+                       p.hidden, p.weight, p.M, p.V, p.Hd, p);
   else
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 4, 1, 6>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 4, 1, 6>), grid, block, 0, stream,
+                       p.hidden, p.weight, p.M, p.V, p.Hd, p);
   return hipGetLastError();
 }
 
@@ -191,7 +201,8 @@ hipError_t launch_lm_head(const LmHeadParams& p, const GreedyParams& walk, sv_dt
                           hipStream_t stream) {
   hipError_t e = dtype == SV_F16 ? launch_typed<TagF16>(p, stream) : launch_typed<TagBF16>(p, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lm_head_reduce_kernel, dim3(p.M), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(lm_head_reduce_kernel, dim3(p.M), dim3(kThreads), 0, stream,
+                     p.part, p.M, p.nwg, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_greedy_walk(walk, stream);

@@ -98,7 +98,7 @@ def cpu_baseline(seconds):
 
 
 # ------------------------------------------------------------------ further rows
-# name -> (workload, description, rotated copies)
+# name -> (workload, description, rotated copies = calls held by one graph)
 ROWS = {
     "attn_batched": ("batched_paged", "verify attention, 8 sequences, log-uniform 4k-32k "
                      "contexts, shuffled 16-token pages", 3),
@@ -115,6 +115,9 @@ ROWS = {
                      "15 masks, bidirectional within the block, over ctx 25,119, 28q/4kv d128",
                      12),
     "tree60_accept": ("qwen7b_tree60", "greedy tree acceptance, 61 nodes over 152,064", 28),
+    "commit_7b": ("qwen7b_25k", "cycle commit, 7B layer: the block's 16 K/V rows appended to "
+                  "the paged cache (sv_kv_append), then the context-length and anchor update "
+                  "(sv_commit); 32 calls per graph, inputs not rotated (64 KB)", 32),
     "lm_head": ("qwen7b_lmhead", "LM head fused with greedy acceptance: 16 x 3584 hidden "
                 "states against the 152,064 x 3584 bf16 output embedding (1.09 GB, more than "
                 "twice the Infinity Cache, so no rotation)", 1),
@@ -181,6 +184,25 @@ def run_row(args):
 
         def call(i, st):
             sv.verify_attention_into(desc, q, ks[i], vs[i], pt, cl, out, lse, mask, ws, st)
+    elif args.row == "commit_7b":
+        inp = W.make_workload_verify(wl)
+        kc, vc = dev_t(inp.k_cache, inp.dtype), dev_t(inp.v_cache, inp.dtype)
+        pt = i32(inp.page_table)
+        start = i32(inp.ctx_lens)                 # the block goes to [ctx, ctx + K)
+        rng = np.random.default_rng(0)
+        new_rows = [dev_t(W.bf16_bits(rng.standard_normal((inp.B, inp.K, inp.Hkv, inp.D),
+                                                          dtype=np.float32)), inp.dtype)
+                    for _ in range(2)]
+        acc = i32(np.full(inp.B, inp.K - 1))
+        toks = i32(np.zeros((inp.B, inp.K)))
+        ctx = i32(inp.ctx_lens)                   # grows by K per call; only commit reads it
+        anchor = torch.empty(inp.B, dtype=torch.int32, device=dev)
+        nbytes = 4 * new_rows[0].numel() * new_rows[0].element_size() + 16 * inp.B
+        shape = {"B": inp.B, "K": inp.K, "Hkv": inp.Hkv, "d": inp.D}
+
+        def call(i, st):
+            sv.kv_append(new_rows[0], new_rows[1], start, pt, kc, vc, stream=st)
+            sv.commit(acc, toks, ctx, anchor, stream=st)
     elif args.row == "tree60_accept":
         ti = W.make_workload_tree(wl)
         lg = [dev_t(ti.logits, ti.dtype)]
@@ -263,7 +285,8 @@ def run_row(args):
     line = {"row": args.row, "workload": wl, "what": desc_txt, "config": shape,
             "us_per_call": us, "calls_per_s": 1e6 / us, "algorithmic_bytes": int(nbytes),
             "GBps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS, "steps": args.steps,
-            "warmup": args.warmup, "rotated_copies": R}
+            "warmup": args.warmup, "calls_per_graph": R,
+            "rotated_copies": 1 if args.row == "commit_7b" else R}
     if flops is not None:
         line["TFLOPs"] = flops / (us * 1e-6) / 1e12
         line["flops_per_call"] = flops

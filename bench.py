@@ -114,6 +114,12 @@ ROWS = {
     "attn_drafter": ("vflash_drafter", "drafter block attention (one of its layers): anchor + "
                      "15 masks, bidirectional within the block, over ctx 25,119, 28q/4kv d128",
                      12),
+    "attn_sar": ("compressor_sar", "semi-autoregressive block attention: 32 images x 5 slot "
+                 "queries x 64 heads (d 64, fp16) over 64 compressed rows + the 5 slots, "
+                 "bidirectional within the block", 15),
+    "attn_sar_qwen": ("compressor_sar", "semi-autoregressive block attention: 32 images x 5 "
+                      "slot queries x 64 heads (d 64, fp16) over 36 compressed rows + the 5 "
+                      "slots, bidirectional within the block", 24),
     "tree60_accept": ("qwen7b_tree60", "greedy tree acceptance, 61 nodes over 152,064", 28),
     "commit_7b": ("qwen7b_25k", "cycle commit, 7B layer: the block's 16 K/V rows appended to "
                   "the paged cache (sv_kv_append), then the context-length and anchor update "
@@ -162,7 +168,14 @@ def run_row(args):
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
     flops = None
     if args.row.startswith("attn"):
-        inp = W.make_workload_verify(wl)
+        if args.row.startswith("attn_sar"):
+            p = W.WORKLOADS[wl].params
+            C = p["shapes"][0][0] if args.row == "attn_sar" else p["shapes"][1][0]
+            inp = W.make_verify(W.rng_for(wl, 2000 + C), B=p["B"], K=p["S"], Hq=p["H"],
+                                Hkv=p["H"], D=p["HD"], ctx_lens=[C] * p["B"], P=16,
+                                dtype="f16", shuffle=True, mask=W.all_ones_mask(p["S"]))
+        else:
+            inp = W.make_workload_verify(wl)
         q = dev_t(inp.q, inp.dtype)
         ks = [dev_t(inp.k_cache, inp.dtype)]
         vs = [dev_t(inp.v_cache, inp.dtype)]

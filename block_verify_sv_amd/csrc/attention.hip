@@ -15,12 +15,16 @@
 // dependent page-table load per tile.  One sequence issues its start-up loads before the
 // context length arrives; a batch reads the context length first and lets the splits
 // past a shorter sequence's end leave at once.
+// With at most 32 query rows per KV head and d = 64 (16-bit), the workgroup is one
+// row-block wave pair (128 threads, two-tile ring) so that several share a CU.
 // Per tile and row block the wave computes S^T = K_tile . Q^T (keys on the MFMA M axis,
 // query rows on N, so each lane owns one query row), applies the block mask, runs the
 // online softmax in registers, and accumulates O^T = V^T . P^T.
 // Output per row: the partial output divided by its own sum, in the input dtype (half the
 // bytes of fp32 for 16-bit inputs) and in the accumulator's register order, its
-// reference maximum m (log2 units) and sum l.
+// reference maximum m (log2 units) and sum l.  When every (b, g) has a single split
+// those values are the result: the split pass writes the output rows and the lse itself
+// and the merge pass is not launched.
 //
 // Merge pass: one workgroup per (32-wide d block, 32-row block, sequence x KV head); its
 // waves read the partial tiles in the same register order (contiguous runs) and combine
@@ -116,8 +120,8 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
   const int rg = wave % RG;                      // row group: row blocks rg + RG*t
   const int kh = wave / RG;                      // key part of each tile
   // blockIdx.x = rgroup * nsplit_pad + s: the row groups of 128 rows of one split are
-  // nsplit_pad (a multiple of 8) workgroups apart, so round-robin dispatch puts them on
-  // one XCD and the later reads of each KV tile come from that XCD's L2
+  // nsplit_pad (then a multiple of 8) workgroups apart, so round-robin dispatch puts them
+  // on one XCD and the later reads of each KV tile come from that XCD's L2
   // With LOADS_FIRST no branch comes before the tile loads are issued: an exit taken on
   // a loaded value (the split padding, the context length) would make the compiler wait
   // for that value first and sink every load behind the branch.  A padding workgroup
@@ -526,6 +530,8 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
   // consecutive d values: each store instruction of a wave writes one contiguous run
   // (512 bytes for 16-bit data), and the merge reads every split of one (row block,
   // d block, quad) as a single contiguous stretch.
+  // With a single split per (b, g) (p.direct) the same values are the result: they go
+  // straight to the output rows [b][i][head][d] and the lse, and no merge runs.
   const int RBT = (p.R + 31) >> 5;
   const size_t bg = static_cast<size_t>(b) * Hkv + g;
 #pragma unroll
@@ -533,7 +539,29 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
     if (!active[t]) continue;
     const int rb = rb0 + rg + RG * t;
     const int r = rb * 32 + l32;
-    if (r < p.R) {
+    if (r < p.R && p.direct) {
+      const float inv = l_run[t] > 0.0f ? 1.0f / l_run[t] : 0.0f;
+      const int i = r / p.G;
+      const size_t orow = (static_cast<size_t>(b) * p.K + i) * p.Hq + g * p.G + (r - i * p.G);
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        const int db = (KW == 2 ? kh * HB : 0) + j;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float o[4] = {oacc[t][j][4 * q4], oacc[t][j][4 * q4 + 1],
+                              oacc[t][j][4 * q4 + 2], oacc[t][j][4 * q4 + 3]};
+          S* dst = static_cast<S*>(p.out) + orow * D + db * 32 + 8 * q4 + 4 * h;
+          if constexpr (SZ == 2) {
+            const uint2 v = {Tag::pack2(o[0] * inv, o[1] * inv), Tag::pack2(o[2] * inv, o[3] * inv)};
+            *reinterpret_cast<uint2*>(dst) = v;
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+          }
+        }
+      }
+      if (p.lse && h == 0 && kh == 0)
+        p.lse[orow] = (m_run[t] * c2 + log2f(l_run[t])) * 0.69314718055994531f;
+    } else if (r < p.R) {
       const float inv = l_run[t] > 0.0f ? 1.0f / l_run[t] : 0.0f;
 #pragma unroll
       for (int j = 0; j < HB; ++j) {
@@ -700,13 +728,23 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
                    p.P_log2, p.max_pages, p.num_pages, p.Hkv, p
 #define MERGE_ARGS p.part_o, p.part_ml, p.R, p.B, p.Hkv, p.nsplit, p
   constexpr int RING = Tag::kBytes == 2 ? kRingDeep : 2;
-  if (p.B == 1) {
+  bool small = false;
+  if constexpr (D == 64 && Tag::kBytes == 2) {
+    // at most one row block per KV head (the semi-autoregressive block: 5 rows, G = 1):
+    // one row-block wave pair of 128 threads, three workgroups per CU
+    if (p.R <= 32) {
+      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 1, 1, 2, 2, false>), grid, dim3(128), 0, stream, SPLIT_ARGS);
+      small = true;
+    }
+  }
+  if (small) {
+  } else if (p.B == 1) {
     hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, true>), grid, dim3(512), 0, stream, SPLIT_ARGS);
   } else {
     hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, false>), grid, dim3(512), 0, stream, SPLIT_ARGS);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.direct) return e;
   const int pairs = (p.R + 31) / 32 * p.B * p.Hkv;
   const dim3 mgrid(D / 32 * 4 * ((pairs + 7) / 8 * 8));
   if (p.nsplit > 32)

@@ -30,7 +30,9 @@ struct AttnParams {
   int32_t P_log2, max_pages, num_pages, max_ctx;
   int32_t chunk;        // keys per split
   int32_t nsplit;       // splits allocated per (b, g)
-  int32_t nsplit_pad;   // nsplit rounded up to a multiple of 8 (grid spacing of halves)
+  int32_t nsplit_pad;   // grid spacing of row groups: nsplit, rounded up to a multiple of 8
+                        // from 8 splits up or when there are several row groups
+  int32_t direct;       // 1: one split per (b, g); the split kernel writes out and lse
   int32_t row_halves;   // row groups of 128 rows (4 row blocks each): ceil(K*G / 128)
   float scale_log2;     // scale * log2(e)
   uint64_t mask[kMaxBlock];

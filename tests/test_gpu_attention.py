@@ -51,6 +51,10 @@ CASES = [
     ("f32", 64, 16, 2, 1, 4, [512], 0, "causal", False),
     ("f32", 128, 16, 8, 2, 6, [250, 999], 0, "random", True),
     ("f32", 64, 64, 6, 2, 16, [77], 64, "ones", True),
+    # one split per (b, g): the split pass writes the output and lse itself (no merge)
+    ("bf16", 128, 16, 28, 4, 16, [40], 0, "causal", True),       # 112 rows, 512 threads
+    ("f16", 64, 16, 64, 64, 5, [64, 64, 17], 0, "ones", True),   # 5 rows: 128-thread pair
+    ("f32", 64, 16, 4, 2, 4, [30, 0], 0, "random", False),
 ]
 
 

@@ -46,6 +46,9 @@ constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
 #endif
 constexpr int kRingDeep = SV_RING_DEEP;
 constexpr int kMaxSplitPages = kMaxSplitKeys / 16 + 2;
+// the 128-thread workgroup takes splits of at most this many keys: its page-id stage
+// then fits four workgroups' LDS in a CU
+constexpr int kMaxSplitKeysSmall = 8192;
 
 // LDS row of key k within a tile: bits 2 and 3 swapped.  With this order the MFMA
 // accumulator register r of lane-half h in a 32-key block holds key
@@ -108,7 +111,8 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
   static_assert(K_PER_T >= 1 && V_PER_T >= 1, "tile chunks per thread");
 
   __shared__ __align__(16) char smem[K_LDS + V_LDS];
-  __shared__ int32_t pg_lds[kMaxSplitPages];
+  constexpr int MSP = (RG == 1 ? kMaxSplitKeysSmall : kMaxSplitKeys) / 16 + 2;  // page ids
+  __shared__ int32_t pg_lds[MSP];
   S* const k_lds = reinterpret_cast<S*>(smem);
   S* const v_lds = reinterpret_cast<S*>(smem + K_LDS);
 
@@ -172,7 +176,7 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
     const int pos0 = k0 + min(u, ntmax - 1) * kTK + run * KR;
     pg_pro[u] = table[min(pos0 >> P_log2, last_page)];
   }
-  constexpr int NPT = (kMaxSplitPages + T - 1) / T;
+  constexpr int NPT = (MSP + T - 1) / T;
   const int npg = min(((k0 + chunk - 1) >> P_log2) - pg0 + 1, max_pages - pg0);
   int pg_all[NPT];
 #pragma unroll
@@ -731,8 +735,8 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   bool small = false;
   if constexpr (D == 64 && Tag::kBytes == 2) {
     // at most one row block per KV head (the semi-autoregressive block: 5 rows, G = 1):
-    // one row-block wave pair of 128 threads, three workgroups per CU
-    if (p.R <= 32) {
+    // one row-block wave pair of 128 threads, four workgroups per CU
+    if (p.R <= 32 && p.chunk <= kMaxSplitKeysSmall) {
       hipLaunchKernelGGL((attn_split_kernel<Tag, D, 1, 1, 2, 2, false>), grid, dim3(128), 0, stream, SPLIT_ARGS);
       small = true;
     }

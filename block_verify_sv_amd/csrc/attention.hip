@@ -607,12 +607,12 @@ __device__ __forceinline__ f32x4 load4(const typename Tag::store_t* src) {
 // Merge: one workgroup per (d block of 32 x register quad, row block of 32, sequence b x
 // KV head g).  Lane l owns row 32*rb + l%32 and the 4 d values 8q + 4(l/32) .. +3 of the
 // d block -- the partial layout's own order, so a wave's load of one split is one
-// contiguous 512-byte run.  Wave w folds splits w, w+4, ... in batches of BATCH (all
-// loads of a batch in flight; 16 when a pair has more than 32 splits, else 8, so few
-// loads go to clamped repeats) with a running maximum; the four wave states are
+// contiguous 512-byte run.  Wave w folds splits w, w+8, ... in batches of BATCH (all
+// loads of a batch in flight; 8 when a pair has more than 32 splits, else 4, so few
+// loads go to clamped repeats) with a running maximum; the eight wave states are
 // combined in wave order through LDS.  Registers are given to the loads in flight
 // rather than to occupancy.
-constexpr int kMergeWaves = 4;
+constexpr int kMergeWaves = 8;
 
 template <class Tag, int D, int BATCH>
 __global__ void __launch_bounds__(kMergeWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
@@ -752,9 +752,9 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   const int pairs = (p.R + 31) / 32 * p.B * p.Hkv;
   const dim3 mgrid(D / 32 * 4 * ((pairs + 7) / 8 * 8));
   if (p.nsplit > 32)
-    hipLaunchKernelGGL((attn_merge_kernel<Tag, D, 16>), mgrid, dim3(kMergeWaves * 64), 0, stream, MERGE_ARGS);
-  else
     hipLaunchKernelGGL((attn_merge_kernel<Tag, D, 8>), mgrid, dim3(kMergeWaves * 64), 0, stream, MERGE_ARGS);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<Tag, D, 4>), mgrid, dim3(kMergeWaves * 64), 0, stream, MERGE_ARGS);
 #undef SPLIT_ARGS
 #undef MERGE_ARGS
   return hipGetLastError();

@@ -132,7 +132,7 @@ def test_single_sequence_surplus_splits(gpu_lib):
 
 
 def test_more_splits_than_one_merge_round(gpu_lib):
-    """126 splits of 16 keys: each merge wave folds two rounds of 16 splits; the last
+    """126 splits of 16 keys: each merge wave folds two rounds of 8 splits; the last
     split holds only block keys 7..15, which rows 0..6 cannot see (l = 0 there)."""
     rng = np.random.default_rng(9)
     inp = W.make_verify(rng, B=1, K=16, Hq=28, Hkv=4, D=128, ctx_lens=[1993], P=16,

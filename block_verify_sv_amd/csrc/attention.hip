@@ -736,16 +736,15 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   if constexpr (D == 64 && Tag::kBytes == 2) {
     // at most one row block per KV head (the semi-autoregressive block: 5 rows, G = 1):
     // one row-block wave pair of 128 threads, four workgroups per CU
-    if (p.R <= 32 && p.chunk <= kMaxSplitKeysSmall) {
+    small = p.R <= 32 && p.chunk <= kMaxSplitKeysSmall;
+    if (small)
       hipLaunchKernelGGL((attn_split_kernel<Tag, D, 1, 1, 2, 2, false>), grid, dim3(128), 0, stream, SPLIT_ARGS);
-      small = true;
-    }
   }
-  if (small) {
-  } else if (p.B == 1) {
-    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, true>), grid, dim3(512), 0, stream, SPLIT_ARGS);
-  } else {
-    hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, false>), grid, dim3(512), 0, stream, SPLIT_ARGS);
+  if (!small) {
+    if (p.B == 1)
+      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, true>), grid, dim3(512), 0, stream, SPLIT_ARGS);
+    else
+      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, false>), grid, dim3(512), 0, stream, SPLIT_ARGS);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.direct) return e;

@@ -166,13 +166,13 @@ lm_head_reduce_kernel(const unsigned long long* part, int32_t M, int32_t nwg,
 }
 
 // Up to 16 rows with a 64-column-multiple width: 128-byte row runs (one cache line per
-// row and step), 4-step ring (128 VGPRs, four waves per SIMD); otherwise single MFMA
+// row and step), 3-step ring (104 VGPRs, four waves per SIMD); otherwise single MFMA
 // steps through a 6-step ring.
 template <class Tag>
 hipError_t launch_typed(const LmHeadParams& p, hipStream_t stream) {
   const dim3 grid(p.nwg), block(kThreads);
   if (p.M <= 16 && p.Hd % (32 * kSub) == 0)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, kSub, 4>), grid, block, 0, stream,
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, kSub, 3>), grid, block, 0, stream,
                        p.hidden, p.weight, p.M, p.V, p.Hd, p);
   else if (p.M <= 16)
     hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, 1, 6>), grid, block, 0, stream,

@@ -65,6 +65,8 @@ def sample_rule(p_rows, q_rows, drafts):
     residual distribution used on a first rejection at k,
     norm(max(0, p_{k-1} - q_k)) (p_{k-1} itself if that residual is all zero),
     and the bonus distribution p_{K-1} used when every draft is accepted.
+    A draft the target gives no probability is never accepted (0/0 counts as 0); one
+    the draft distribution gives none but the target does has ratio +inf (accepted).
     """
     K = len(p_rows)
     acc = []
@@ -72,7 +74,10 @@ def sample_rule(p_rows, q_rows, drafts):
     for k in range(1, K):
         d = int(drafts[k - 1])
         p, q = p_rows[k - 1], q_rows[k - 1]
-        acc.append(min(1.0, p[d] / q[d]) if q[d] > 0 else 1.0)
+        if p[d] == 0:
+            acc.append(0.0)
+        else:
+            acc.append(min(1.0, p[d] / q[d]) if q[d] > 0 else 1.0)
         r = np.maximum(0.0, p - q)
         resid.append(r / r.sum() if r.sum() > 0 else p / p.sum())
     return acc, resid, p_rows[K - 1]
@@ -85,7 +90,8 @@ def race_ref(r, seed, offset, b, row):
     (b, row, j); the winner is argmin_j E_j / r_j, ties to the lowest j.  Since
     E_j / r_j is exponential with rate r_j, independently over j, the winner is
     j with probability r_j / sum(r).  Returns (winner, key of the winner,
-    smallest relative gap between the two smallest keys).
+    smallest relative gap between the two smallest keys).  With no positive weight
+    there is nothing to draw: the winner is -1 (never a token id).
     """
     V = len(r)
     j = np.arange(V)
@@ -93,6 +99,8 @@ def race_ref(r, seed, offset, b, row):
     e = -np.log1p(-u)
     key = np.full(V, np.inf)
     pos = r > 0
+    if not pos.any():
+        return -1, float("inf"), float("inf")
     key[pos] = e[pos] / r[pos]
     w = int(np.argmin(key))
     srt = np.sort(key[pos])
@@ -101,7 +109,8 @@ def race_ref(r, seed, offset, b, row):
 
 
 def accept_sample_ref(target_logits, draft_logits, drafts, dtype: str, temperature: float,
-                      seed: int, offset: int, return_diag: bool = False):
+                      seed: int, offset: int, return_diag: bool = False,
+                      return_steps: bool = False):
     """Sampling verification with Philox uniforms and an exponential-race resample.
 
     For each sequence b and k = 1 .. K-1 in order:
@@ -113,7 +122,9 @@ def accept_sample_ref(target_logits, draft_logits, drafts, dtype: str, temperatu
     p_{K-1} on target row K-1 for the bonus token.
     Returns (accept_len [B], out_tokens [B][K]) and, with ``return_diag``, the
     per-sequence minimum |u_k - exp(min(0, lambda_k))| over the tests taken and
-    the race's relative top-2 gap.
+    the race's relative top-2 gap; with ``return_steps``, per sequence the thresholds
+    exp(min(0, lambda_k)) of the tests taken, the target row raced over and the race
+    weights (unnormalised), in place of the diagnostics.
     """
     lp = decode(target_logits, dtype)
     lq = decode(draft_logits, dtype)
@@ -122,20 +133,26 @@ def accept_sample_ref(target_logits, draft_logits, drafts, dtype: str, temperatu
     acc = np.zeros(B, dtype=np.int32)
     out = np.full((B, K), -1, dtype=np.int32)
     diag = []
+    steps = []
     for b in range(B):
         logp = _log_softmax_rows(lp[b], T)      # [K][V]
         logq = _log_softmax_rows(lq[b], T)      # [K-1][V]
         a = K - 1
         margin = np.inf
+        thresholds = []
         for k in range(1, K):
             d = int(drafts[b][k - 1])
             if not 0 <= d < V:                     # a token outside the vocabulary is rejected
                 a = k - 1
                 break
-            lam = logp[k - 1, d] - logq[k - 1, d]
             u = float(uniforms(seed, offset, b, ACCEPT, k, np.array([0]))[0])
-            thr = np.exp(min(0.0, lam))
+            if logp[k - 1, d] == -np.inf:           # p_{k-1}(d_k) = 0: never accepted
+                thr = 0.0
+            else:                                    # q_k(d_k) = 0 gives lam = +inf
+                lam = logp[k - 1, d] - logq[k - 1, d]
+                thr = np.exp(min(0.0, lam))
             margin = min(margin, abs(u - thr))
+            thresholds.append(float(thr))
             if not u < thr:
                 a = k - 1
                 break
@@ -154,6 +171,9 @@ def accept_sample_ref(target_logits, draft_logits, drafts, dtype: str, temperatu
         out[b, :a] = drafts[b][:a]
         out[b, a] = tok
         diag.append((margin, gap))
+        steps.append({"thresholds": thresholds, "row": row, "weights": r})
+    if return_steps:
+        return acc, out, steps
     if return_diag:
         return acc, out, diag
     return acc, out

@@ -110,6 +110,19 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
+def _on_stream(stream, *tensors):
+    """Tell the caching allocator that tensors made on the current stream are used by
+    a launch on another stream, so their memory is not reused before that stream gets
+    past the launch."""
+    if stream is None:
+        return
+    if stream.cuda_stream == torch.cuda.current_stream(stream.device).cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _require(t: torch.Tensor, name: str, dtype=None):
     if not t.is_cuda:
         raise SvError(f"{name} must be a device tensor")
@@ -123,14 +136,19 @@ def _require(t: torch.Tensor, name: str, dtype=None):
 _WS: dict = {}
 
 
-def _workspace(kind: str, nbytes: int, device, zero: bool) -> torch.Tensor:
-    """A per-(kind, device) workspace grown on demand (the library needs no initial
-    contents; ``zero`` only picks a zero-filled first allocation)."""
-    key = (kind, str(device))
+def _workspace(kind: str, nbytes: int, device, zero: bool, stream=None) -> torch.Tensor:
+    """A per-(kind, device, stream) workspace grown on demand (the library needs no
+    initial contents; ``zero`` only picks a zero-filled first allocation).  Calls on
+    different streams get different buffers, since two calls sharing one must not
+    overlap in time; a buffer replaced by a larger one is released only after the work
+    its stream has queued (record_stream)."""
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (kind, str(device), s.cuda_stream)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
         n = max(nbytes, 256)
-        ws = (torch.zeros if zero else torch.empty)(n, dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = (torch.zeros if zero else torch.empty)(n, dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws
 
@@ -161,7 +179,8 @@ def verify_attention_into(desc: AttnDesc, q, k_cache, v_cache, page_table, ctx_l
     (or None for causal); ``workspace`` a device uint8 tensor (or None: cached)."""
     nbytes = attention_workspace_bytes(desc)
     if workspace is None:
-        workspace = _workspace("attn", nbytes, q.device, zero=False)
+        workspace = _workspace("attn", nbytes, q.device, zero=False, stream=stream)
+    _on_stream(stream, out, lse)
     _check(load().sv_verify_attention(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                       _ptr(page_table), _ptr(ctx_lens), block_mask, _ptr(out),
                                       _ptr(lse), _ptr(workspace), workspace.numel(),
@@ -213,11 +232,12 @@ def accept_greedy(logits: torch.Tensor, drafts: torch.Tensor, want_argmax: bool 
     n = c_sz()
     _check(lib.sv_accept_greedy_workspace(B, K, V, ctypes.byref(n)), "sv_accept_greedy_workspace")
     if workspace is None:
-        workspace = _workspace("greedy", n.value, logits.device, zero=True)
+        workspace = _workspace("greedy", n.value, logits.device, zero=True, stream=stream)
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=logits.device)
         toks = torch.empty(B, K, dtype=torch.int32, device=logits.device)
         am = torch.empty(B, K, dtype=torch.int32, device=logits.device) if want_argmax else None
+        _on_stream(stream, acc, toks, am)
     else:
         acc, toks, am = out
     _check(lib.sv_accept_greedy(B, K, V, _DTYPES[logits.dtype], _ptr(logits), _ptr(drafts),
@@ -244,12 +264,13 @@ def accept_greedy_tree(logits: torch.Tensor, parents: torch.Tensor, tokens: torc
     n = c_sz()
     _check(lib.sv_accept_greedy_workspace(B, K, V, ctypes.byref(n)), "sv_accept_greedy_workspace")
     if workspace is None:
-        workspace = _workspace("greedy", n.value, logits.device, zero=True)
+        workspace = _workspace("greedy", n.value, logits.device, zero=True, stream=stream)
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=logits.device)
         toks = torch.empty(B, K, dtype=torch.int32, device=logits.device)
         path = torch.empty(B, K, dtype=torch.int32, device=logits.device)
         am = torch.empty(B, K, dtype=torch.int32, device=logits.device) if want_argmax else None
+        _on_stream(stream, acc, toks, path, am)
     else:
         acc, toks, path, am = out
     _check(lib.sv_accept_greedy_tree(B, K, V, _DTYPES[logits.dtype], _ptr(logits),
@@ -278,11 +299,12 @@ def lm_head_greedy(hidden_states: torch.Tensor, weight: torch.Tensor, drafts: to
     _check(lib.sv_lm_head_greedy_workspace(B, K, V, Hd, ctypes.byref(n)),
            "sv_lm_head_greedy_workspace")
     if workspace is None:
-        workspace = _workspace("lm_head", n.value, weight.device, zero=False)
+        workspace = _workspace("lm_head", n.value, weight.device, zero=False, stream=stream)
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=weight.device)
         toks = torch.empty(B, K, dtype=torch.int32, device=weight.device)
         am = torch.empty(B, K, dtype=torch.int32, device=weight.device) if want_argmax else None
+        _on_stream(stream, acc, toks, am)
     else:
         acc, toks, am = out
     _check(lib.sv_lm_head_greedy(B, K, V, Hd, _DTYPES[hidden_states.dtype], _ptr(hidden_states),
@@ -308,10 +330,12 @@ def accept_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
     n = c_sz()
     _check(lib.sv_accept_sample_workspace(B, K, V, ctypes.byref(n)), "sv_accept_sample_workspace")
     if workspace is None:
-        workspace = _workspace("sample", n.value, target_logits.device, zero=False)
+        workspace = _workspace("sample", n.value, target_logits.device, zero=False,
+                               stream=stream)
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=target_logits.device)
         toks = torch.empty(B, K, dtype=torch.int32, device=target_logits.device)
+        _on_stream(stream, acc, toks)
     else:
         acc, toks = out
     _check(lib.sv_accept_sample(B, K, V, _DTYPES[target_logits.dtype], _ptr(target_logits),
@@ -337,9 +361,10 @@ def latent_compress(queries: torch.Tensor, feats: torch.Tensor, scale: float = 1
     _check(lib.sv_latent_compress_workspace(B, C, N, D, ctypes.byref(n)),
            "sv_latent_compress_workspace")
     if workspace is None:
-        workspace = _workspace("compress", n.value, feats.device, zero=False)
+        workspace = _workspace("compress", n.value, feats.device, zero=False, stream=stream)
     if out is None:
         out = torch.empty(B, C, D, dtype=torch.float16, device=feats.device)
+        _on_stream(stream, out)
     _check(lib.sv_latent_compress(B, C, N, D, SV_F16, _ptr(queries), _ptr(feats), _ptr(out),
                                   float(scale), _ptr(workspace), workspace.numel(),
                                   _stream(stream)),
@@ -381,6 +406,7 @@ def commit(accept_len: torch.Tensor, out_tokens: torch.Tensor, ctx_lens: torch.T
         raise SvError("commit shape mismatch")
     if next_anchor is None:
         next_anchor = torch.empty(B, dtype=torch.int32, device=out_tokens.device)
+        _on_stream(stream, next_anchor)
     _require(next_anchor, "next_anchor", torch.int32)
     _check(load().sv_commit(B, K, _ptr(accept_len), _ptr(out_tokens), _ptr(ctx_lens),
                             _ptr(next_anchor), _stream(stream)),
@@ -407,6 +433,7 @@ def commit_tree(accept_len: torch.Tensor, out_tokens: torch.Tensor, accept_path:
         raise SvError("commit_tree shape mismatch")
     if next_anchor is None:
         next_anchor = torch.empty(B, dtype=torch.int32, device=out_tokens.device)
+        _on_stream(stream, next_anchor)
     _require(next_anchor, "next_anchor", torch.int32)
     desc = AttnDesc(B, K, Hkv, Hkv, D, P, page_table.shape[1], num_pages, 0, 0, 0.0,
                     _DTYPES[k_cache.dtype], 0)

@@ -1,9 +1,11 @@
 """Build libspecverify.so in-tree with hipcc for gfx950.
 
-    python -m block_verify_sv_amd.build          # compile every source, link the library
+    python -m block_verify_sv_amd.build          # compile every source, link the libraries
 
 Objects go to ``block_verify_sv_amd/_build/``; the library to
-``block_verify_sv_amd/libspecverify.so``.  Every call recompiles.
+``block_verify_sv_amd/libspecverify.so``.  The streaming-read probe the benchmark uses
+for its bandwidth ceiling is linked on its own into ``libsvprobe.so`` (measurement only;
+the verification library does not contain it).  Every call recompiles.
 """
 import os
 import subprocess
@@ -15,10 +17,12 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
+PROBE_LIB = os.path.join(PKG, "libsvprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "attention.hip", "accept_greedy.hip", "accept_sample.hip",
            "compress.hip", "kv_append.hip", "commit.hip", "lm_head.hip"]
+PROBE_SOURCES = ["hbm_probe.hip"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -42,18 +46,24 @@ def _compile(src):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OUT, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -4,7 +4,8 @@
 // Launch 1 (row_lse_kernel), grid (8192-entry vocabulary chunk, row) over the B*K
 // target rows and the B*(K-1) draft rows: per chunk the maximum m_c of the raw logits
 // and s_c = sum exp((x - m_c) / T), fp32 exponentials (the hardware exp2 unit)
-// accumulated in fp64.
+// accumulated in fp64.  Logits may be -inf (probability 0, e.g. a masked vocabulary);
+// a chunk of nothing but -inf contributes s_c = 0.
 //
 // Launch 2 (sample_race_kernel), grid (1024-entry vocabulary chunk, sequence).  Every
 // workgroup combines the chunk partials into the row log-normalisers
@@ -138,11 +139,15 @@ row_lse_kernel(const void* target, const void* draft, int32_t B, int32_t K, int3
   m = redf[0];
 #pragma unroll
   for (int w = 1; w < kLseThreads / kWave; ++w) m = fmaxf(m, redf[w]);
-  // e^((x - m)/T) = 2^((x - m) * log2(e)/T) on the hardware exp unit
+  // e^((x - m)/T) = 2^((x - m) * log2(e)/T) on the hardware exp unit.  A chunk whose
+  // logits are all -inf (a masked stretch of the vocabulary) has m = -inf: subtracting 0
+  // instead gives exp2(-inf) = 0 for every entry, so s = 0 and the chunk drops out of
+  // the row's normaliser.
   const float it2 = static_cast<float>(p.inv_t * 1.4426950408889634);
+  const float mref = m == -INFINITY ? 0.0f : m;
   double s = 0.0;
 #pragma unroll
-  for (int e = 0; e < kMaxPer; ++e) s += static_cast<double>(fast_exp2((v[e] - m) * it2));
+  for (int e = 0; e < kMaxPer; ++e) s += static_cast<double>(fast_exp2((v[e] - mref) * it2));
   s = wave_sum_f64(s);
   if ((tid & 63) == 0) redd[tid >> 6] = s;
   __syncthreads();
@@ -242,9 +247,9 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
   if (tid < 64) {
     bool fail = false;
     if (tester) {
-      if (!in_vocab) {
-        fail = true;                              // a token outside the vocabulary is rejected
-      } else {
+      if (!in_vocab || lp == -INFINITY) {
+        fail = true;     // a token outside the vocabulary, or one the target gives p = 0
+      } else {           // q_k(d_k) = 0 < p: lambda = +inf, accepted
         const int k = tid + 1;
         const double lam = (lp - lq) * it - (Lrow[k - 1] - Lrow[K + k - 1]);
         const U64x4 w = philox(p.offset, static_cast<uint64_t>(b), static_cast<uint64_t>(k), 0,
@@ -330,7 +335,8 @@ sample_finish_kernel(const double* race_key, const int32_t* race_idx, const int3
   }
   block_best(bk_r, bi_r, bk_p, bi_p, rk, ri);
   const int a = decision[b];
-  const int32_t token = (bk_r < INFINITY) ? bi_r : bi_p;
+  // a race with no positive weight (a row with no finite logit) draws nothing: -1
+  const int32_t token = (bk_r < INFINITY) ? bi_r : (bk_p < INFINITY ? bi_p : -1);
   if (tid < K) {
     const int32_t* dr = drafts + static_cast<size_t>(b) * (K - 1);
     p.out_tokens[static_cast<size_t>(b) * K + tid] = tid < a ? dr[tid] : (tid == a ? token : -1);

@@ -388,6 +388,8 @@ sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
     return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0 (use sv_accept_greedy for 0)");
   if (!target_logits || !draft_logits || !drafts || !accept_len || !out_tokens)
     return fail(SV_ERR_INVALID_ARG, "logits, drafts and outputs are required");
+  if (!aligned16(target_logits) || !aligned16(draft_logits))
+    return fail(SV_ERR_INVALID_ARG, "target_logits and draft_logits must be 16-byte aligned");
   const int chunk = sv::sample_chunk(V);
   const int nchunk = (V + chunk - 1) / chunk;
   const int race_chunk = sv::sample_race_chunk(V);
@@ -458,6 +460,7 @@ sv_status sv_latent_compress(int32_t B, int32_t C, int32_t N, int32_t D, sv_dtyp
   const size_t need = sv::compress_workspace_bytes(B, C, N);
   if (!workspace || workspace_bytes < need)
     return fail(SV_ERR_WORKSPACE, "compressor needs %zu workspace bytes", need);
+  if (!aligned16(workspace)) return fail(SV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   sv::CompressParams p;
   p.queries = queries;
   p.feats = feats;

@@ -29,8 +29,8 @@
  *   - Arguments are validated on the host before anything is launched; a
  *     nonzero status launches nothing and leaves outputs untouched.  A short
  *     message for the last failure on the calling thread is in sv_last_error().
- *   - Inputs must be finite.  Results are bitwise reproducible for identical
- *     inputs, shapes and workspace contents.
+ *   - Inputs must be finite (sv_accept_sample also takes -inf logits, see there).
+ *     Results are bitwise reproducible for identical inputs and shapes.
  *   - Workspaces carry no state between calls and need no initialisation; two
  *     calls that share one workspace must not overlap in time.
  */
@@ -154,11 +154,16 @@ sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
  * argmin_j E_j / r_j with E_j = -ln(1 - u_j) over r_j > 0 (an exponential race, exact
  * in distribution), ties to the lowest j.  The ratio test and the race run in fp64; the
  * row log-normalisers use fp32 exponentials summed in fp64.
- * Layouts: target_logits [B][K][V], draft_logits [B][K-1][V] (SV_F32 or SV_BF16),
- * drafts [B][K-1] int32; outputs as for sv_accept_greedy.  A draft outside [0, V) counts
- * as rejected (its logits are never read).
+ * Layouts: target_logits [B][K][V], draft_logits [B][K-1][V] (SV_F32 or SV_BF16), both
+ * 16-byte aligned; drafts [B][K-1] int32; outputs as for sv_accept_greedy.  A draft
+ * outside [0, V) counts as rejected (its logits are never read).
+ * Logits may be -inf: such an entry has probability 0 (a masked vocabulary).  A draft
+ * whose target probability is 0 is always rejected; one whose draft probability is 0
+ * (but target probability is not) is always accepted.  Every row must hold at least
+ * one finite logit; +inf and NaN are not supported.  A draw over a row without any
+ * finite logit has nothing to draw from and is reported as token -1.
  * Limits: 2 <= K <= 64, 1 <= V < 2^31, B * (2K - 1) <= 65535, temperature > 0 (greedy is
- * its own call).  The workspace needs no initial contents.
+ * its own call).  The workspace (16-byte aligned) needs no initial contents.
  * ------------------------------------------------------------------------------------ */
 sv_status sv_accept_sample_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes);
 sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
@@ -171,7 +176,8 @@ sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
  * Latent visual compressor (SpecFLASH README, "components", compressor equation):
  *   out[b] = softmax(scale * queries . feats[b]^T) . feats[b], softmax over the N rows.
  * The printed formula has no 1/sqrt(D); pass scale = 1 for it (0 is read as 1).
- * Layouts: queries [C][D], feats [B][N][D], out [B][C][D], all SV_F16 (fp32 accumulate).
+ * Layouts: queries [C][D], feats [B][N][D], out [B][C][D], all SV_F16 (fp32 accumulate),
+ * each 16-byte aligned, as is the workspace (no initial contents).
  * Limits: 1 <= C <= 64, 1 <= N <= 1024, D a multiple of 128 (invalid: SV_ERR_INVALID_ARG).
  * ------------------------------------------------------------------------------------ */
 sv_status sv_latent_compress_workspace(int32_t B, int32_t C, int32_t N, int32_t D,

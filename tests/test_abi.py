@@ -132,6 +132,11 @@ def test_sample_validation(lib):
     assert call(float("inf")) == INVALID
     assert call(1.0, dt=sv.SV_F16) == UNSUPPORTED
     assert call(1.0, ws=None) == WORKSPACE
+    assert call(1.0, ws=ctypes.c_void_p(0x1008)) == INVALID         # misaligned workspace
+    odd = ctypes.c_void_p(0x1008)                                   # 8- but not 16-byte aligned
+    for tl, dl in ((odd, FAKE), (FAKE, odd)):
+        assert lib.sv_accept_sample(1, 4, 100, sv.SV_BF16, tl, dl, FAKE, 1.0, 1, 0, FAKE, FAKE,
+                                    FAKE, 1 << 30, None) == INVALID
 
 
 def test_compress_validation(lib):
@@ -146,6 +151,7 @@ def test_compress_validation(lib):
                                                  1 << 20, None)
     assert call(sv.SV_BF16, FAKE) == UNSUPPORTED
     assert call(sv.SV_F16, None) == WORKSPACE
+    assert call(sv.SV_F16, ctypes.c_void_p(0x1008)) == INVALID      # misaligned workspace
 
 
 def test_kv_append_validation(lib):

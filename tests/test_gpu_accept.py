@@ -1,4 +1,8 @@
 """GPU parity of sv_accept_greedy / sv_accept_sample against the oracle: bit-exact."""
+import json
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -6,6 +10,8 @@ import torch
 import oracle
 import workloads as W
 from gpu_helpers import i32, say, to_dev
+
+sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden"))
 
 pytestmark = pytest.mark.gpu
 
@@ -220,3 +226,141 @@ def test_sample_a_thousand_sequence_cycles(gpu_lib):
     say(f"  accepted drafts {accepted} over 1024 sequence-cycles; smallest margin "
         f"{min(margins):.2e}, smallest race gap {min(gaps):.2e}")
     assert accepted > 0
+
+
+# ------------------------------------------------------------------ un-planted inputs
+def _drafts_following(rng, t, V):
+    """Drafts that copy the oracle's greedy tokens t [B][K] for a Geometric(0.25) prefix,
+    then differ once, then are uniform (test-side; the argmax comes from the oracle)."""
+    B, K = t.shape
+    L = np.minimum(rng.geometric(0.25, size=B) - 1, K - 1)
+    drafts = rng.integers(0, V, size=(B, K - 1)).astype(np.int32)
+    for b in range(B):
+        n = int(L[b])
+        drafts[b, :n] = t[b, :n]
+        if n < K - 1 and V > 1:
+            o = int(rng.integers(0, V - 1))
+            drafts[b, n] = o if o < t[b, n] else o + 1
+    return drafts, L
+
+
+@pytest.mark.parametrize("B,K,sign", [(1, 16, "mixed"), (8, 16, "mixed"), (4, 16, "negative"),
+                                      (2, 32, "negative")])
+def test_greedy_unplanted_full_vocabulary(gpu_lib, B, K, sign):
+    """Plain N(0, 3) bf16 rows over the full 152,064-token vocabulary, nothing planted:
+    the natural bf16 ties (a few percent of rows) and, for "negative", rows whose every
+    logit (and so the maximum) is negative -- the ordering of negative keys."""
+    V = 152064
+    rng = np.random.default_rng([77, B, K, len(sign)])
+    x = rng.standard_normal(size=(B, K, V), dtype=np.float32) * np.float32(3.0)
+    if sign == "negative":
+        x = -np.abs(x) - np.float32(0.25)
+    logits = W.bf16_bits(x)
+    _, _, t = oracle.accept_greedy_ref(logits, np.zeros((B, K - 1), np.int32), "bf16")
+    drafts, L = _drafts_following(rng, t, V)
+    xs = W.bf16_bits_to_f32(logits)
+    ties = int(((xs == xs.max(axis=-1, keepdims=True)).sum(axis=-1) > 1).sum())
+    say(f"[greedy] unplanted B={B} K={K} V={V} {sign}: rows with a tied maximum {ties}/{B * K}")
+    acc = assert_greedy(gpu_lib, logits, drafts, "bf16", f"unplanted {sign}")
+    np.testing.assert_array_equal(acc, L)
+    if sign == "negative":
+        assert (xs.max(axis=-1) < 0).all()
+
+
+def test_greedy_unplanted_ties_are_common(gpu_lib):
+    """Rows built to hold their maximum several times at scattered indices, in f32 and
+    bf16, over the full vocabulary: the lowest index must win."""
+    V, K = 152064, 16
+    rng = np.random.default_rng(4321)
+    x = rng.standard_normal(size=(2, K, V), dtype=np.float32) * np.float32(3.0)
+    for b in range(2):
+        for i in range(K):
+            idx = rng.choice(V, size=4, replace=False)
+            if i % 2:                               # a positive maximum held 4 times
+                x[b, i, idx] = 30.0
+            else:                                   # every logit negative, maximum -0.75
+                x[b, i] = -np.abs(x[b, i]) - 1.0
+                x[b, i, idx] = -0.75
+    for dtype in ("f32", "bf16"):
+        logits = x if dtype == "f32" else W.bf16_bits(x)
+        _, _, t = oracle.accept_greedy_ref(logits, np.zeros((2, K - 1), np.int32), dtype)
+        drafts, L = _drafts_following(rng, t, V)
+        say(f"[greedy] planted multi-ties {dtype}")
+        acc = assert_greedy(gpu_lib, logits, drafts, dtype, f"multi-ties {dtype}")
+        np.testing.assert_array_equal(acc, L)
+
+
+# ------------------------------------------------------------------ 72B sampling at scale
+GOLDEN_72B = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                          "sample_72b_1024.json")
+
+
+def test_sample_72b_thousand_sequence_cycles(gpu_lib):
+    """1,024 sequence-cycles of the 72B sampling shape at the full vocabulary (8 sequences
+    x 128 Philox offsets): every accept length and drawn token bit-exact with the oracle's
+    verdicts, which tests/golden/make_sample_72b.py stored (oracle calls only); the inputs
+    are regenerated and checked against the stored digest, and four offsets are also
+    re-run through the oracle live.  The smallest |u - threshold| and relative race gap
+    over all 1,024 are printed."""
+    import make_sample_72b as G
+    with open(GOLDEN_72B) as fh:
+        gold = json.load(fh)
+    s = G.inputs()
+    assert G.digest(s) == gold["input_digest"], "the input generator changed"
+    tl = to_dev(s.target_logits, s.dtype)
+    dl = to_dev(s.draft_logits, s.dtype)
+    dr = i32(s.drafts)
+    accepted, margins, gaps = 0, [], []
+    for off in range(G.OFFSETS):
+        if off % 32 == 0:
+            say(f"[sample] 72B x 8 sequences, offsets {off}..{off + 31}")
+        acc, toks = gpu_lib.accept_sample(tl, dl, dr, s.temperature, s.seed, off)
+        torch.cuda.synchronize()
+        acc, toks = acc.cpu().numpy(), toks.cpu().numpy()
+        g = gold["offsets"][str(off)]
+        np.testing.assert_array_equal(acc, g["accept_len"], err_msg=f"offset {off}")
+        for b in range(s.B):
+            a = int(acc[b])
+            assert list(toks[b, :a]) == list(s.drafts[b, :a]), (off, b)
+            assert toks[b, a] == g["token"][b], (off, b, toks[b, a], g["token"][b],
+                                                 g["margin"][b], g["race_gap"][b])
+            assert (toks[b, a + 1:] == -1).all()
+        accepted += int(acc.sum())
+        margins += g["margin"]
+        gaps += g["race_gap"]
+        if off % 32 == 5:                          # the oracle live, on the same inputs
+            r_acc, r_toks = oracle.accept_sample_ref(s.target_logits, s.draft_logits,
+                                                     s.drafts, s.dtype, s.temperature,
+                                                     s.seed, off)
+            np.testing.assert_array_equal(acc, r_acc)
+            np.testing.assert_array_equal(toks, r_toks)
+    say(f"  1024 sequence-cycles: accepted drafts {accepted}; smallest |u - threshold| "
+        f"{min(margins):.3e}, smallest relative race gap {min(gaps):.3e}")
+
+
+def test_sample_masked_vocabulary(gpu_lib):
+    """-inf logits: whole 8192-entry chunks of the vocabulary masked in the target and
+    the draft rows (and a stretch not aligned to chunks), a draft the target gives
+    probability 0 (always rejected) and one the draft gives probability 0 (always
+    accepted): bit-exact with the oracle, and nothing masked is ever drawn."""
+    V, K, B = 40000, 8, 6
+    rng = np.random.default_rng(606)
+    for off in range(8):
+        s = W.make_sample(rng, B=B, K=K, V=V, dtype="bf16", seed=9, offset=off)
+        t = W.bf16_bits_to_f32(s.target_logits)
+        d = W.bf16_bits_to_f32(s.draft_logits)
+        t[:, :, 8192:24576] = -np.inf               # two whole normaliser chunks
+        d[:, :, 8192:16384] = -np.inf
+        t[:, :, 30001:31234] = -np.inf              # not chunk-aligned
+        s.drafts[0, 0] = 9000                       # p = 0: rejected at k = 1
+        s.drafts[1, 2] = 12000                      # p = 0 at k = 3
+        t[2, 1, 12000] = 5.0                        # p > 0 while q = 0 at k = 2 ...
+        s.drafts[2, 1] = 12000                      # ... so it is accepted
+        s.target_logits = W.bf16_bits(t)
+        s.draft_logits = W.bf16_bits(d)
+        say(f"[sample] masked vocabulary offset={off}")
+        acc, toks = sample_gpu(gpu_lib, s)
+        assert_sample(gpu_lib, s, f"masked/{off}")
+        assert acc[0] == 0
+        tk = toks[np.arange(B), acc]
+        assert not (((tk >= 8192) & (tk < 24576)) | ((tk >= 30001) & (tk < 31234))).any()

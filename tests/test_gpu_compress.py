@@ -54,12 +54,14 @@ def test_compressor_shapes(gpu_lib, B, C, N, D, scale):
     check(got, ref, f"{B},{C},{N},{D}")
 
 
-def test_sar_block_after_compressor(gpu_lib):
+@pytest.mark.parametrize("C,N", [(64, 576), (36, 324)])
+def test_sar_block_after_compressor(gpu_lib, C, N):
     """Compressor output + 5 slot rows as the K/V of the semi-autoregressive block:
-    5 slot queries, 64 heads x 64, one bidirectional block (all-ones mask)."""
+    5 slot queries, 64 heads x 64, one bidirectional block (all-ones mask), for both
+    compressor shapes at full size."""
     p = W.WORKLOADS["compressor_sar"].params
-    B, C, N, D, S, H, HD = p["B"], 64, 576, p["D"], p["S"], p["H"], p["HD"]
-    rng = W.rng_for("compressor_sar", 1000)
+    B, D, S, H, HD = p["B"], p["D"], p["S"], p["H"], p["HD"]
+    rng = W.rng_for("compressor_sar", 1000 + C)
     c = W.make_compress(rng, B=B, C=C, N=N, D=D)
     sar = W.make_sar(rng, B=B, S=S, H=H, D=HD)
     P = 16
@@ -67,7 +69,7 @@ def test_sar_block_after_compressor(gpu_lib):
     table = np.arange(B * pages_per, dtype=np.int32).reshape(B, pages_per)
     kc = torch.zeros(B * pages_per, H, P, HD, dtype=torch.float16, device="cuda")
     vc = torch.zeros(B * pages_per, H, HD, P, dtype=torch.float16, device="cuda")
-    say("[sar] compressor -> kv_append -> verify attention")
+    say(f"[sar] C={C} N={N}: compressor -> kv_append -> verify attention")
     fhat = gpu_lib.latent_compress(to_dev(c.queries, "f16"), to_dev(c.feats, "f16"))
     rows = fhat.view(B, C, H, HD)
     t_table = i32(table)
@@ -89,4 +91,4 @@ def test_sar_block_after_compressor(gpu_lib):
     inp = W.VerifyInputs(B, S, H, H, HD, P, "f16", sar.q, kc_ref, vc_ref, table,
                          np.full(B, C, dtype=np.int32), W.all_ones_mask(S))
     ref_out, ref_lse = oracle.verify_attention_ref(inp)
-    check_attention(out, lse, ref_out, ref_lse, "f16", "sar")
+    check_attention(out, lse, ref_out, ref_lse, "f16", f"sar C={C}")

@@ -22,6 +22,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "load", "SvError", "AttnDesc", "verify_attention", "verify_attention_into",
+    "verify_attention_noalloc_into",
     "attention_workspace_bytes", "accept_greedy", "accept_sample", "latent_compress",
     "kv_append", "commit", "make_desc", "SV_F32", "SV_BF16", "SV_F16",
 ]
@@ -57,6 +58,8 @@ _SIGNATURES = {
     "sv_verify_attention_workspace": (c_i32, [ctypes.POINTER(AttnDesc), ctypes.POINTER(c_sz)]),
     "sv_verify_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "sv_verify_attention_noalloc": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp,
+                                            c_vp, c_vp, c_vp, c_vp, c_vp]),
     "sv_accept_greedy_workspace": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]),
     "sv_accept_greedy": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                  c_sz, c_vp]),
@@ -186,6 +189,17 @@ def verify_attention_into(desc: AttnDesc, q, k_cache, v_cache, page_table, ctx_l
                                       _ptr(lse), _ptr(workspace), workspace.numel(),
                                       _stream(stream)),
            "sv_verify_attention")
+
+
+def verify_attention_noalloc_into(desc: AttnDesc, q, k_cache, v_cache, page_table, ctx_lens,
+                                  out, lse=None, block_mask=None, stream=None):
+    """The allocation-free call: as verify_attention_into, with the library's own
+    per-GPU scratch array in place of a workspace (calls overlapping on one GPU race)."""
+    _on_stream(stream, out, lse)
+    _check(load().sv_verify_attention_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache),
+                                              _ptr(v_cache), _ptr(page_table), _ptr(ctx_lens),
+                                              block_mask, _ptr(out), _ptr(lse), _stream(stream)),
+           "sv_verify_attention_noalloc")
 
 
 def mask_array(mask):

@@ -163,6 +163,23 @@ sv_status sv_verify_attention(const sv_attn_desc* desc, const void* q, const voi
                               const int32_t* ctx_lens, const uint64_t* block_mask, void* out,
                               float* lse, void* workspace, size_t workspace_bytes,
                               void* stream) {
+  return sv::attention_call(desc, q, k_cache, v_cache, page_table, ctx_lens, block_mask, out, lse,
+                            workspace, workspace_bytes, stream, "sv_verify_attention launch");
+}
+
+}  // extern "C"
+
+namespace sv {
+
+sv_status report(sv_status st, const char* msg) {
+  if (st == SV_OK) return ok();
+  return fail(st, "%s", msg);
+}
+
+sv_status attention_call(const sv_attn_desc* desc, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* page_table, const int32_t* ctx_lens,
+                         const uint64_t* block_mask, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream, const char* what) {
   sv_status st = check_attn_desc(desc);
   if (st != SV_OK) return st;
   if (!q || !k_cache || !v_cache || !page_table || !ctx_lens || !out)
@@ -216,8 +233,12 @@ sv_status sv_verify_attention(const sv_attn_desc* desc, const void* q, const voi
   p.scale_log2 = scale * 1.4426950408889634f;
   return device_status(sv::launch_attention(p, desc->head_dim, desc->dtype,
                                             static_cast<hipStream_t>(stream)),
-                       "sv_verify_attention launch");
+                       what);
 }
+
+}  // namespace sv
+
+extern "C" {
 
 // ---------------------------------------------------------------- greedy
 static sv_status check_accept_shape(int32_t B, int32_t K, int32_t V, int min_k) {

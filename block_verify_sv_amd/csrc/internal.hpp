@@ -50,6 +50,14 @@ struct AttnPlan {
 AttnPlan plan_attention(const sv_attn_desc& d);
 hipError_t launch_attention(const AttnParams& p, int head_dim, sv_dtype dtype,
                             hipStream_t stream);
+// The whole of sv_verify_attention (validation, planning, launches) on a given workspace;
+// `what` names the entry point in launch-failure messages.
+sv_status attention_call(const sv_attn_desc* desc, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* page_table, const int32_t* ctx_lens,
+                         const uint64_t* block_mask, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream, const char* what);
+// Records a status and message for sv_last_error (SV_OK clears it); returns st.
+sv_status report(sv_status st, const char* msg);
 
 // ---------------------------------------------------------------- greedy accept
 struct GreedyParams {

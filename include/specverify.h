@@ -123,6 +123,26 @@ sv_status sv_verify_attention(const sv_attn_desc* desc, const void* q, const voi
                               void* stream);
 
 /* -------------------------------------------------------------------------------------
+ * Allocation-free verify attention, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same operation, arguments, layouts, limits and results as sv_verify_attention, without
+ * the workspace arguments: the split-KV partials go to a scratch array of
+ * SV_NOALLOC_SCRATCH_BYTES held by the library on each GPU it runs on (until the process
+ * ends).  Descriptors whose sv_verify_attention_workspace exceeds that size are rejected
+ * with SV_ERR_WORKSPACE.  The call allocates, frees and clears nothing; it runs on the
+ * current device, and `stream` must belong to it (else SV_ERR_INVALID_ARG).  All calls on
+ * one GPU share its scratch array: calls that overlap in time on one GPU (several streams
+ * or host threads) race and give wrong results.
+ * ------------------------------------------------------------------------------------ */
+#define SV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+sv_status sv_verify_attention_noalloc(const sv_attn_desc* desc, const void* q,
+                                      const void* k_cache, const void* v_cache,
+                                      const int32_t* page_table, const int32_t* ctx_lens,
+                                      const uint64_t* block_mask, void* out, float* lse,
+                                      void* stream);
+
+/* -------------------------------------------------------------------------------------
  * Greedy acceptance (VFlash-FM page, caption of the cycle figure: the prefix matching
  * the target's greedy choice is accepted, the target supplies the token at the first
  * disagreement, the rest is discarded).

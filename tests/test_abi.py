@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert lib.sv_version() == 1
@@ -216,3 +216,17 @@ def test_lm_head_validation(lib):
 def test_status_strings(lib):
     assert lib.sv_status_string(0) == b"ok"
     assert lib.sv_status_string(-3) == b"workspace too small"
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free attention call validates like sv_verify_attention and rejects,
+    before any device call, a descriptor whose partials exceed its scratch array."""
+    A = ctypes.c_void_p
+    args = lambda d: (ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None)
+    assert lib.sv_verify_attention_noalloc(*args(_desc(block=0))) == INVALID
+    assert lib.sv_verify_attention_noalloc(*args(_desc(head_dim=96))) == UNSUPPORTED
+    big = _desc(batch=64, split_keys=64, sum_ctx_hint=0)
+    assert _ws(lib, big)[1] > (32 << 20)
+    assert lib.sv_verify_attention_noalloc(*args(big)) == WORKSPACE
+    assert b"32" in lib.sv_last_error() or b"33554432" in lib.sv_last_error()
+

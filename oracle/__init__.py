@@ -31,6 +31,10 @@ Every function follows a passage of the pages it cites:
   of a draft tree (the "Tree-60" row of the VFlash-FM results table) read as the
   chain rule walked from the anchor, and the commit that moves the accepted path's
   K/V rows into place.
+* ``tree_sample.accept_sample_tree_ref`` / ``tree_sample.sample_tree_rule`` -- sampling
+  verification of a draft tree (the "Tree-60" row of the VFlash-FM results table with the
+  standard acceptance-rejection rule of the SpecFLASH README): recursive rejection over
+  the children of the current node, which reduces to the chain rule on a chain.
 * ``lm_head.lm_head_greedy_ref`` -- the target's LM head (hidden state . W^T) followed
   by greedy acceptance over its logits (VFlash-FM page, caption of the cycle figure).
 
@@ -46,11 +50,13 @@ from .compress import latent_compress_ref
 from .kv import kv_append_ref, commit_ref
 from .tree import accept_greedy_tree_ref, tree_commit_ref
 from .lm_head import lm_head_logits_ref, lm_head_greedy_ref
+from .tree_sample import accept_sample_tree_ref, sample_tree_rule, children_of
 
 __all__ = [
     "decode", "verify_attention_ref", "single_query_ref", "merge_partials_ref",
     "accept_greedy_ref", "sample_rule", "accept_sample_ref", "race_ref",
     "philox4x64_10", "uniforms", "ACCEPT", "RESAMPLE", "latent_compress_ref",
     "kv_append_ref", "commit_ref", "accept_greedy_tree_ref", "tree_commit_ref",
-    "lm_head_logits_ref", "lm_head_greedy_ref",
+    "lm_head_logits_ref", "lm_head_greedy_ref", "accept_sample_tree_ref", "sample_tree_rule",
+    "children_of",
 ]

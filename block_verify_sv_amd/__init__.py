@@ -74,6 +74,9 @@ _SIGNATURES = {
     "sv_commit": (c_i32, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "sv_accept_greedy_tree": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                       c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "sv_accept_sample_tree_workspace": (c_i32, [c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]),
+    "sv_accept_sample_tree": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_f32,
+                                      c_u64, c_u64, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "sv_commit_tree": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                c_vp, c_vp, c_vp]),
     "sv_lm_head_greedy_workspace": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]),
@@ -358,6 +361,48 @@ def accept_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
                                 _ptr(toks), _ptr(workspace), workspace.numel(), _stream(stream)),
            "sv_accept_sample")
     return acc, toks
+
+
+def accept_sample_tree(target_logits: torch.Tensor, draft_logits: torch.Tensor, parents,
+                       tokens: torch.Tensor, temperature: float, seed: int, offset: int,
+                       out=None, workspace=None, stream=None):
+    """Sampling acceptance over a draft tree shared by the batch.  parents: host sequence of
+    K-1 ints (parent of node i at [i-1]); tokens [B][K-1] device int32.  Returns
+    (accept_len [B], out_tokens [B][K], accept_path [B][K])."""
+    _require(target_logits, "target_logits")
+    _require(draft_logits, "draft_logits", target_logits.dtype)
+    _require(tokens, "tokens", torch.int32)
+    B, K, V = target_logits.shape
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise SvError("sampling logits must be float32 or bfloat16")
+    if tuple(draft_logits.shape) != (B, K - 1, V) or tuple(tokens.shape) != (B, K - 1):
+        raise SvError("draft_logits must be [B][K-1][V] and tokens [B][K-1]")
+    par = [int(x) for x in parents]
+    if len(par) != K - 1:
+        raise SvError(f"parents must hold K-1 = {K - 1} entries")
+    par_c = (c_i32 * max(1, len(par)))(*par)
+    lib = load()
+    n = c_sz()
+    _check(lib.sv_accept_sample_tree_workspace(B, K, V, ctypes.byref(n)),
+           "sv_accept_sample_tree_workspace")
+    if workspace is None:
+        workspace = _workspace("sample_tree", n.value, target_logits.device, zero=False,
+                               stream=stream)
+    if out is None:
+        dev = target_logits.device
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(B, K, dtype=torch.int32, device=dev)
+        path = torch.empty(B, K, dtype=torch.int32, device=dev)
+        _on_stream(stream, acc, toks, path)
+    else:
+        acc, toks, path = out
+    _check(lib.sv_accept_sample_tree(B, K, V, _DTYPES[target_logits.dtype], _ptr(target_logits),
+                                     _ptr(draft_logits), ctypes.cast(par_c, c_vp), _ptr(tokens),
+                                     float(temperature), int(seed) & (2**64 - 1),
+                                     int(offset) & (2**64 - 1), _ptr(acc), _ptr(toks), _ptr(path),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)),
+           "sv_accept_sample_tree")
+    return acc, toks, path
 
 
 # ----------------------------------------------------------------------- compressor

@@ -21,7 +21,8 @@ PROBE_LIB = os.path.join(PKG, "libsvprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "attention.hip", "accept_greedy.hip", "accept_sample.hip",
-           "compress.hip", "kv_append.hip", "commit.hip", "lm_head.hip", "noalloc.hip"]
+           "compress.hip", "kv_append.hip", "commit.hip", "lm_head.hip", "noalloc.hip",
+           "accept_sample_tree.hip"]
 PROBE_SOURCES = ["hbm_probe.hip"]
 
 COMMON = [

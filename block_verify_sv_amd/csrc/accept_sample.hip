@@ -25,6 +25,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "sample_device.hpp"
 
 namespace sv {
 namespace {
@@ -33,46 +34,6 @@ constexpr int kThreads = 256;                     // race: 4 tokens per thread
 constexpr int kLseThreads = 256;
 constexpr int kLseChunk = 8192;                   // vocabulary entries per row_lse workgroup
 constexpr int kRaceChunk = 4 * kThreads;          // vocabulary entries per race workgroup
-
-// ---- Philox4x64-10 (Salmon et al., SC'11): multipliers and Weyl key increments of
-// the 4x64 variant; ten rounds.
-constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
-constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
-constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
-constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
-
-struct U64x4 {
-  uint64_t x[4];
-};
-
-__device__ __forceinline__ U64x4 philox(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
-                                        uint64_t k0, uint64_t k1) {
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += kPhiloxW0;
-      k1 += kPhiloxW1;
-    }
-    const uint64_t hi0 = __umul64hi(kPhiloxM0, c0), lo0 = kPhiloxM0 * c0;
-    const uint64_t hi1 = __umul64hi(kPhiloxM1, c2), lo1 = kPhiloxM1 * c2;
-    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0;
-    c1 = lo1;
-    c2 = n2;
-    c3 = lo0;
-  }
-  return U64x4{{c0, c1, c2, c3}};
-}
-
-__device__ __forceinline__ double to_uniform(uint64_t w) {
-  return static_cast<double>(w >> 11) * 0x1.0p-53;
-}
-
-template <bool kBF16>
-__device__ __forceinline__ float logit_at(const void* base, size_t i) {
-  if constexpr (kBF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
-  else return static_cast<const float*>(base)[i];
-}
 
 // Row rho < nt = B*K is target row rho; otherwise draft row rho - B*K.
 template <bool kBF16>
@@ -157,39 +118,6 @@ row_lse_kernel(const void* target, const void* draft, int32_t B, int32_t K, int3
     for (int w = 0; w < kLseThreads / kWave; ++w) t += redd[w];
     p.part_m[static_cast<size_t>(rho) * p.nchunk + c] = m;
     p.part_s[static_cast<size_t>(rho) * p.nchunk + c] = t;
-  }
-}
-
-__device__ __forceinline__ bool better(double k, int32_t i, double bk, int32_t bi) {
-  return k < bk || (k == bk && i < bi);
-}
-
-// Smallest (key, index) of a workgroup, for the residual race and the p race.
-__device__ __forceinline__ void block_best(double& bk_r, int32_t& bi_r, double& bk_p,
-                                           int32_t& bi_p, double (*rk)[kThreads / kWave],
-                                           int32_t (*ri)[kThreads / kWave]) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double kr = __shfl_xor(bk_r, o);
-    const int32_t ir = __shfl_xor(bi_r, o);
-    if (better(kr, ir, bk_r, bi_r)) { bk_r = kr; bi_r = ir; }
-    const double kp = __shfl_xor(bk_p, o);
-    const int32_t ip = __shfl_xor(bi_p, o);
-    if (better(kp, ip, bk_p, bi_p)) { bk_p = kp; bi_p = ip; }
-  }
-  if ((tid & 63) == 0) {
-    rk[0][tid >> 6] = bk_r;
-    ri[0][tid >> 6] = bi_r;
-    rk[1][tid >> 6] = bk_p;
-    ri[1][tid >> 6] = bi_p;
-  }
-  __syncthreads();
-  bk_r = rk[0][0]; bi_r = ri[0][0]; bk_p = rk[1][0]; bi_p = ri[1][0];
-#pragma unroll
-  for (int w = 1; w < kThreads / kWave; ++w) {
-    if (better(rk[0][w], ri[0][w], bk_r, bi_r)) { bk_r = rk[0][w]; bi_r = ri[0][w]; }
-    if (better(rk[1][w], ri[1][w], bk_p, bi_p)) { bk_p = rk[1][w]; bi_p = ri[1][w]; }
   }
 }
 
@@ -305,7 +233,7 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
       }
     }
   }
-  block_best(bk_r, bi_r, bk_p, bi_p, rk, ri);
+  block_best<kThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
   if (tid == 0) {
     const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + c) * 2;
     p.race_key[slot] = bk_r;
@@ -333,7 +261,7 @@ sample_finish_kernel(const double* race_key, const int32_t* race_idx, const int3
     if (better(k0, i0, bk_r, bi_r)) { bk_r = k0; bi_r = i0; }
     if (better(k1, i1, bk_p, bi_p)) { bk_p = k1; bi_p = i1; }
   }
-  block_best(bk_r, bi_r, bk_p, bi_p, rk, ri);
+  block_best<kThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
   const int a = decision[b];
   // a race with no positive weight (a row with no finite logit) draws nothing: -1
   const int32_t token = (bk_r < INFINITY) ? bi_r : (bk_p < INFINITY ? bi_p : -1);
@@ -367,6 +295,17 @@ size_t sample_workspace_bytes(int B, int K, int V) {
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(int32_t); // race_idx
   off += static_cast<size_t>(B) * sizeof(int32_t);          // decision
   return (off + 15) & ~static_cast<size_t>(15);
+}
+
+hipError_t launch_row_lse(const SampleParams& p, sv_dtype dtype, hipStream_t stream) {
+  const dim3 g1(p.nchunk, p.B * (2 * p.K - 1));
+  if (dtype == SV_BF16)
+    hipLaunchKernelGGL(row_lse_kernel<true>, g1, dim3(kLseThreads), 0, stream, p.target, p.draft,
+                       p.B, p.K, p.V, p.chunk, p);
+  else
+    hipLaunchKernelGGL(row_lse_kernel<false>, g1, dim3(kLseThreads), 0, stream, p.target, p.draft,
+                       p.B, p.K, p.V, p.chunk, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stream) {

@@ -450,6 +450,82 @@ sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
                        "sv_accept_sample launch");
 }
 
+// ---------------------------------------------------------------- sampling over a tree
+sv_status sv_accept_sample_tree_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes) {
+  sv_status st = check_accept_shape(B, K, V, 2);
+  if (st != SV_OK) return st;
+  if (static_cast<int64_t>(B) * (2 * K - 1) > 65535)
+    return fail(SV_ERR_INVALID_ARG, "B * (2K - 1) must be <= 65535");
+  if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = sv::sample_tree_workspace_bytes(B, K, V);
+  return ok();
+}
+
+sv_status sv_accept_sample_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                                const void* target_logits, const void* draft_logits,
+                                const int32_t* parents, const int32_t* tokens, float temperature,
+                                uint64_t seed, uint64_t offset, int32_t* accept_len,
+                                int32_t* out_tokens, int32_t* accept_path, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  sv_status st = check_accept_shape(B, K, V, 2);
+  if (st != SV_OK) return st;
+  if (static_cast<int64_t>(B) * (2 * K - 1) > 65535)
+    return fail(SV_ERR_INVALID_ARG, "B * (2K - 1) must be <= 65535");
+  if (logit_dtype != SV_F32 && logit_dtype != SV_BF16)
+    return fail(SV_ERR_UNSUPPORTED, "sampling logits must be SV_F32 or SV_BF16");
+  if (!(temperature > 0.0f) || !isfinite(temperature))
+    return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0 (use the greedy calls for 0)");
+  if (!target_logits || !draft_logits || !parents || !tokens || !accept_len || !out_tokens ||
+      !accept_path)
+    return fail(SV_ERR_INVALID_ARG, "logits, parents, tokens and outputs are required");
+  if (!aligned16(target_logits) || !aligned16(draft_logits))
+    return fail(SV_ERR_INVALID_ARG, "target_logits and draft_logits must be 16-byte aligned");
+  for (int i = 1; i < K; ++i)
+    if (parents[i - 1] < 0 || parents[i - 1] >= i)
+      return fail(SV_ERR_INVALID_ARG, "parents[%d] = %d: the parent of node %d must be in [0, %d)",
+                  i - 1, parents[i - 1], i, i);
+  const size_t need = sv::sample_tree_workspace_bytes(B, K, V);
+  if (!workspace || workspace_bytes < need)
+    return fail(SV_ERR_WORKSPACE, "tree sampling needs %zu workspace bytes", need);
+  if (!aligned16(workspace)) return fail(SV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  sv::TreeSampleParams p;
+  memset(&p, 0, sizeof p);
+  p.target = target_logits;
+  p.draft = draft_logits;
+  p.tokens = tokens;
+  p.accept_len = accept_len;
+  p.out_tokens = out_tokens;
+  p.path = accept_path;
+  p.B = B;
+  p.K = K;
+  p.V = V;
+  p.nchunk = (V + sv::sample_chunk(V) - 1) / sv::sample_chunk(V);
+  p.inv_t = 1.0 / static_cast<double>(temperature);
+  p.seed = seed;
+  p.offset = offset;
+  const int rounds = sv::plan_sample_tree(p, parents);
+  int widest = 0;
+  for (int u = 0; u < K; ++u) widest = p.child_count[u] > 1 ? widest + 1 : widest;
+  if (static_cast<int64_t>(B) * (widest > 0 ? widest : 1) > 65535)
+    return fail(SV_ERR_INVALID_ARG, "B times the number of branching nodes must be <= 65535");
+  const size_t rows = static_cast<size_t>(B) * (2 * K - 1);
+  char* w = static_cast<char*>(workspace);
+  p.part_s = reinterpret_cast<double*>(w);
+  w += rows * p.nchunk * sizeof(double);
+  p.zpart = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(B) * K * p.nz * sizeof(double);
+  p.race_key = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(B) * p.race_nchunk * 2 * sizeof(double);
+  p.part_m = reinterpret_cast<float*>(w);
+  w += rows * p.nchunk * sizeof(float);
+  p.race_idx = reinterpret_cast<int32_t*>(w);
+  w += static_cast<size_t>(B) * p.race_nchunk * 2 * sizeof(int32_t);
+  p.stop = reinterpret_cast<int32_t*>(w);
+  return device_status(sv::launch_sample_tree(p, rounds, logit_dtype,
+                                              static_cast<hipStream_t>(stream)),
+                       "sv_accept_sample_tree launch");
+}
+
 // ---------------------------------------------------------------- compressor
 static sv_status check_compress(int32_t B, int32_t C, int32_t N, int32_t D) {
   if (B < 1 || B > 65535) return fail(SV_ERR_INVALID_ARG, "B must be in [1, 65535] (got %d)", B);

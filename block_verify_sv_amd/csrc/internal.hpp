@@ -118,6 +118,44 @@ size_t sample_workspace_bytes(int B, int K, int V);
 int sample_chunk(int V);
 int sample_race_chunk(int V);
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stream);
+// The per-chunk (max, sum) pass over every target and draft row alone (p.target, p.draft,
+// p.B, p.K, p.V, p.chunk, p.nchunk, p.part_m, p.part_s, p.inv_t).
+hipError_t launch_row_lse(const SampleParams& p, sv_dtype dtype, hipStream_t stream);
+
+// ---------------------------------------------------------------- sampling over a tree
+struct TreeSampleParams {
+  const void* target;         // [B][K][V]
+  const void* draft;          // [B][K-1][V]: row i-1 = the distribution node i was drawn from
+  const int32_t* tokens;      // [B][K-1]
+  int32_t* accept_len;
+  int32_t* out_tokens;        // [B][K]
+  int32_t* path;              // [B][K]
+  const float* part_m;        // [B*(2K-1)][nchunk] row_lse partials (target rows, then draft)
+  const double* part_s;
+  double* zpart;              // [B][K][nz] partial sums of each residual, slot = child node
+  double* race_key;           // [B][race_nchunk][2]
+  int32_t* race_idx;
+  int32_t* stop;              // [B][2]: node the walk stopped at, its children (all rejected)
+  int32_t B, K, V;
+  int32_t nchunk;
+  int32_t zchunk, nz;
+  int32_t race_chunk, race_nchunk;
+  double inv_t;
+  uint64_t seed, offset;
+  int8_t parent[kMaxBlock];       // parent of node i (node 0: -1)
+  int8_t sib[kMaxBlock];          // position of node i among its parent's children
+  int8_t child_start[kMaxBlock];  // first entry of node u's children in child_list
+  int8_t child_count[kMaxBlock];
+  int8_t child_list[kMaxBlock];   // children grouped by parent, increasing node order
+  int8_t by_count[kMaxBlock];     // nodes by decreasing child count (ties: node order)
+};
+
+size_t sample_tree_workspace_bytes(int B, int K, int V);
+// Fills the plan fields (chunks, tree tables) of p from the host tree; returns the number
+// of residual rounds (the largest child count - 1, at least 0).
+int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host);
+hipError_t launch_sample_tree(const TreeSampleParams& p, int rounds, sv_dtype dtype,
+                              hipStream_t stream);
 
 // ---------------------------------------------------------------- latent compressor
 struct CompressParams {

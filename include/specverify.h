@@ -17,6 +17,7 @@
  *   sv_kv_append         write new K/V rows into the paged cache
  *   sv_commit            close a cycle: grow the context, pick the next anchor
  *   sv_accept_greedy_tree  greedy verification of a draft tree (walk from the anchor)
+ *   sv_accept_sample_tree  sampling verification of a draft tree (recursive rejection)
  *   sv_commit_tree       close a tree cycle: move the accepted path's K/V into place
  *   sv_lm_head_greedy    the target's LM head fused with greedy acceptance
  *
@@ -260,6 +261,37 @@ sv_status sv_accept_greedy_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_
                                 const int32_t* tokens, int32_t* accept_len,
                                 int32_t* out_tokens, int32_t* accept_path, int32_t* argmax,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sampling verification of a draft tree: the standard acceptance-rejection rule (SpecFLASH
+ * README, "components") applied as recursive rejection over the children of the current
+ * node, for the tree-verified variant of the VFlash-FM results table.  At node u (target
+ * row u, p_u = softmax(row / T)) the children c_1 < c_2 < ... are tested in order; child
+ * c_j, token x_j drawn from q_j = softmax(draft row of c_j / T), passes iff
+ * u_j < min(1, r_{j-1}(x_j) / q_j(x_j)), with r_0 = p_u and, after each rejection,
+ * r_j = norm(max(0, r_{j-1} - q_j)) (p_u if that is all zero).  The first child that
+ * passes becomes the current node; when none does (or u is a leaf) the token is drawn
+ * from the last residual by the exponential race.  Uniforms as for sv_accept_sample: the
+ * test of node c uses purpose 0 with row c, the draw purpose 1 with the row of the node
+ * the walk stopped at; on a chain the call returns exactly what sv_accept_sample returns.
+ *   target_logits [B][K][V], draft_logits [B][K-1][V] (row i-1: the distribution node i was
+ *   drawn from; siblings may share one or differ), SV_F32 or SV_BF16, 16-byte aligned;
+ *   parents HOST [K-1] int32, the tree shared by the batch (parent of node i at [i-1], in
+ *   [0, i): checked, else SV_ERR_INVALID_ARG); tokens [B][K-1] device int32 (a token
+ *   outside [0, V) is rejected).  Outputs as for sv_accept_greedy_tree: accept_len [B],
+ *   out_tokens [B][K] (accepted nodes' tokens, the drawn token, then -1), accept_path
+ *   [B][K] (0, the accepted nodes, then -1); close the cycle with sv_commit_tree.
+ * -inf logits are probability 0 as for sv_accept_sample.  Limits: 2 <= K <= 64,
+ * B * (2K - 1) <= 65535, T > 0.  Workspace: sv_accept_sample_tree_workspace bytes, 16-byte
+ * aligned, no initial contents.  The tree's largest child count m sets m - 1 sequential
+ * residual passes over the vocabulary (none on a chain).
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_accept_sample_tree_workspace(int32_t B, int32_t K, int32_t V, size_t* bytes);
+sv_status sv_accept_sample_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+                                const void* target_logits, const void* draft_logits,
+                                const int32_t* parents, const int32_t* tokens, float temperature,
+                                uint64_t seed, uint64_t offset, int32_t* accept_len,
+                                int32_t* out_tokens, int32_t* accept_path, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Tree commit: per sequence b with a = accept_len[b] (clamped to [0, K-1]) and
  * K = desc->block, the K/V rows of the j-th accepted node move from position

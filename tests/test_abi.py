@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert lib.sv_version() == 1
@@ -229,4 +229,21 @@ def test_noalloc_validation(lib):
     assert _ws(lib, big)[1] > (32 << 20)
     assert lib.sv_verify_attention_noalloc(*args(big)) == WORKSPACE
     assert b"32" in lib.sv_last_error() or b"33554432" in lib.sv_last_error()
+
+
+def test_sample_tree_validation(lib):
+    n = ctypes.c_size_t()
+    assert lib.sv_accept_sample_tree_workspace(1, 61, 152064, ctypes.byref(n)) == OK and n.value > 0
+    assert lib.sv_accept_sample_tree_workspace(1, 1, 100, ctypes.byref(n)) == INVALID   # K >= 2
+    good = (ctypes.c_int32 * 3)(0, 0, 1)
+    call = lambda par, T=1.0, ws=FAKE, dt=sv.SV_BF16, tl=FAKE: lib.sv_accept_sample_tree(
+        1, 4, 100, dt, tl, FAKE, par, FAKE, T, 1, 0, FAKE, FAKE, FAKE, ws, 1 << 30, None)
+    assert call(good, T=0.0) == INVALID
+    assert call(good, dt=sv.SV_F16) == UNSUPPORTED
+    assert call(None) == INVALID
+    assert call((ctypes.c_int32 * 3)(0, 2, 1)) == INVALID              # parent of node 2 is 2
+    assert call((ctypes.c_int32 * 3)(0, 0, -1)) == INVALID
+    assert call(good, ws=None) == WORKSPACE
+    assert call(good, ws=ctypes.c_void_p(0x1008)) == INVALID
+    assert call(good, tl=ctypes.c_void_p(0x1008)) == INVALID
 

@@ -1,0 +1,118 @@
+"""GPU parity of sv_accept_sample_tree (sampling verification of a draft tree) against the
+float64 oracle: accept lengths, tokens and paths bit-exact; on a chain it equals
+sv_accept_sample."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_helpers import i32, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def tree_gpu(sv, ts, offset=None):
+    off = ts.offset if offset is None else offset
+    acc, toks, path = sv.accept_sample_tree(to_dev(ts.target_logits, ts.dtype),
+                                            to_dev(ts.draft_logits, ts.dtype), ts.parents,
+                                            i32(ts.tokens), ts.temperature, ts.seed, off)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), toks.cpu().numpy(), path.cpu().numpy()
+
+
+def assert_tree(sv, ts, where, offset=None):
+    off = ts.offset if offset is None else offset
+    acc, toks, path = tree_gpu(sv, ts, off)
+    r_acc, r_toks, r_path = oracle.accept_sample_tree_ref(ts.target_logits, ts.draft_logits,
+                                                          ts.parents, ts.tokens, ts.dtype,
+                                                          ts.temperature, ts.seed, off)
+    np.testing.assert_array_equal(acc, r_acc, err_msg=f"{where}: accept_len")
+    np.testing.assert_array_equal(path, r_path, err_msg=f"{where}: path")
+    np.testing.assert_array_equal(toks, r_toks, err_msg=f"{where}: out_tokens")
+    return acc
+
+
+def test_tree60_workload(gpu_lib):
+    """The static Tree-60 (61 nodes, the anchor with 10 children) over the full 152,064-token
+    vocabulary: 8 cycles of fresh inputs (2 sequences each, Philox offset = cycle), six at
+    T = 1 and two at T = 2.5; most tests reject, so the residual chains run deep."""
+    depths = []
+    for cyc in range(8):
+        ts = W.make_workload_tree_sample(cycle=cyc, B=2)
+        if cyc >= 6:
+            ts.temperature = 2.5
+        say(f"[tree sample] Tree-60 cycle={cyc} T={ts.temperature}")
+        depths += [int(a) for a in assert_tree(gpu_lib, ts, f"tree60/{cyc}")]
+    say(f"  accepted depths {depths}")
+    assert max(depths) > 0 and min(depths) < max(depths)
+
+
+@pytest.mark.parametrize("V,dtype,T", [(152064, "bf16", 1.0), (3001, "f32", 0.7)])
+def test_chain_topology_equals_chain_call(gpu_lib, V, dtype, T):
+    """A chain through the tree call returns exactly what sv_accept_sample returns."""
+    rng = np.random.default_rng(V)
+    s = W.make_sample(rng, B=3, K=16, V=V, dtype=dtype, temperature=T, seed=41, offset=0)
+    parents = np.arange(15, dtype=np.int32)
+    tl, dl, dr = to_dev(s.target_logits, dtype), to_dev(s.draft_logits, dtype), i32(s.drafts)
+    for off in range(6):
+        say(f"[tree sample] chain V={V} offset={off}")
+        a1, t1 = gpu_lib.accept_sample(tl, dl, dr, T, 41, off)
+        a2, t2, path = gpu_lib.accept_sample_tree(tl, dl, parents, dr, T, 41, off)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(a1.cpu().numpy(), a2.cpu().numpy())
+        np.testing.assert_array_equal(t1.cpu().numpy(), t2.cpu().numpy())
+        a = a2.cpu().numpy()
+        p = path.cpu().numpy()
+        for b in range(3):
+            assert list(p[b, :a[b] + 1]) == list(range(a[b] + 1))
+
+
+@pytest.mark.parametrize("shape", ["star", "random", "binary", "deep"])
+def test_tree_shapes_many_offsets(gpu_lib, shape):
+    """Small vocabularies, 8 sequences x 24 offsets per tree shape: a star (every node under
+    the anchor), a random tree, a binary tree, and a long chain with side branches."""
+    rng = np.random.default_rng(len(shape) * 31)
+    if shape == "star":
+        parents = np.zeros(20, np.int32)
+    elif shape == "random":
+        parents = np.array([int(rng.integers(0, i)) for i in range(1, 40)], np.int32)
+    elif shape == "binary":
+        parents = np.array([(i - 1) // 2 for i in range(1, 31)], np.int32)
+    else:
+        parents = np.array([max(0, i - 1 - (i % 3 == 0)) for i in range(1, 64)], np.int32)
+    ts = W.make_tree_sample(rng, B=8, V=2000, parents=parents, dtype="bf16", noise=0.7)
+    total = 0
+    for off in range(24):
+        if off % 8 == 0:
+            say(f"[tree sample] {shape} K={len(parents) + 1} offset={off}")
+        total += int(assert_tree(gpu_lib, ts, f"{shape}/{off}", off).sum())
+    assert total > 0
+
+
+def test_masked_vocabulary_and_invalid_tokens(gpu_lib):
+    """-inf stretches in target and draft rows, tokens outside the vocabulary, fp32 logits."""
+    rng = np.random.default_rng(5)
+    parents = np.array([0, 0, 0, 1, 1, 2, 4], np.int32)
+    ts = W.make_tree_sample(rng, B=6, V=20000, parents=parents, dtype="f32")
+    ts.target_logits[:, :, 8192:12000] = -np.inf
+    ts.draft_logits[:, :, 16384:20000] = -np.inf
+    ts.tokens[0, 0] = -5
+    ts.tokens[1, 1] = 20000
+    ts.tokens[2, 0] = 9000                        # masked for the target: never accepted
+    for off in range(10):
+        say(f"[tree sample] masked offset={off}")
+        acc = assert_tree(gpu_lib, ts, f"masked/{off}", off)
+        assert acc[2] == 0 or tree_gpu(gpu_lib, ts, off)[2][2, 1] != 1
+
+
+def test_deterministic_and_offset_sensitive(gpu_lib):
+    ts = W.make_tree_sample(np.random.default_rng(9), B=16, V=5000,
+                            parents=W.make_tree_topology(np.random.default_rng(3)), dtype="bf16")
+    say("[tree sample] determinism")
+    r1 = tree_gpu(gpu_lib, ts, 3)
+    r2 = tree_gpu(gpu_lib, ts, 3)
+    for x, y in zip(r1, r2):
+        np.testing.assert_array_equal(x, y)
+    r3 = tree_gpu(gpu_lib, ts, 4)
+    assert not all(np.array_equal(x, y) for x, y in zip(r1, r3))

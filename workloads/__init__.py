@@ -69,6 +69,7 @@ __all__ = [
     "all_ones_mask", "rng_for", "TreeInputs", "TREE60_LEVELS", "make_tree_topology",
     "chain_topology", "tree_mask", "make_tree_greedy", "workload_tree",
     "make_workload_tree", "LmHeadInputs", "make_lm_head", "make_workload_lm_head",
+    "TreeSampleInputs", "make_tree_sample", "make_workload_tree_sample",
 ]
 
 BASE_SEED = 1000
@@ -465,6 +466,57 @@ def make_sample(rng: np.random.Generator, *, B: int, K: int, V: int, dtype: str 
     drafts = np.argmax(_to_f64(draft, dtype) / temperature + g, axis=-1).astype(np.int32)
     return SampleInputs(B, K, V, dtype, target, draft, drafts, float(temperature),
                         int(seed), int(offset))
+
+
+@dataclass
+class TreeSampleInputs:
+    B: int
+    K: int                     # nodes, anchor included
+    V: int
+    dtype: str
+    target_logits: np.ndarray  # [B][K][V]: target row of every node
+    draft_logits: np.ndarray   # [B][K-1][V]: row i-1 = the distribution node i was drawn from
+    parents: np.ndarray        # int32 [K-1]: the tree (shared by the batch)
+    tokens: np.ndarray         # int32 [B][K-1]
+    temperature: float
+    seed: int
+    offset: int
+
+
+def make_tree_sample(rng: np.random.Generator, *, B: int, V: int, parents, dtype: str = "bf16",
+                     temperature: float = 1.0, std: float = 3.0, noise: float = 1.0,
+                     seed: int = 0x5EED, offset: int = 0) -> TreeSampleInputs:
+    """Target logits ~ N(0, std) for every node; the children of node u share one draft
+    row, round(target row u + N(0, noise)), and draw their tokens from it independently
+    (with replacement) by the Gumbel-max trick -- the drafter's part, not verification."""
+    parents = np.asarray(parents, dtype=np.int32)
+    K = len(parents) + 1
+    tl = rng.standard_normal(size=(B, K, V), dtype=np.float32)
+    tl *= np.float32(std)
+    target = _round_to(tl, dtype)
+    t32 = _to_f64(target, dtype).astype(np.float32)
+    draft = np.empty((B, K - 1, V), dtype=target.dtype)
+    tokens = np.zeros((B, K - 1), dtype=np.int32)
+    for u in sorted(set(int(x) for x in parents)):
+        kids = [i for i in range(1, K) if int(parents[i - 1]) == u]
+        dn = rng.standard_normal(size=(B, V), dtype=np.float32)
+        dn *= np.float32(noise)
+        row = _round_to(t32[:, u, :] + dn, dtype)
+        q64 = _to_f64(row, dtype) / temperature
+        for i in kids:
+            draft[:, i - 1, :] = row
+            g = -np.log(-np.log(rng.random(size=(B, V))))
+            tokens[:, i - 1] = np.argmax(q64 + g, axis=-1)
+    return TreeSampleInputs(B, K, V, dtype, target, draft, parents, tokens, float(temperature),
+                            int(seed), int(offset))
+
+
+def make_workload_tree_sample(name: str = "qwen7b_tree60", cycle: int = 0,
+                              B: int = 1) -> TreeSampleInputs:
+    """Sampling verification of the static Tree-60 of the tree workload (T = 1)."""
+    p = WORKLOADS[name].params
+    return make_tree_sample(rng_for(name, 30_000 + cycle), B=B, V=p["V"],
+                            parents=workload_tree(name), dtype=p["dtype"], offset=cycle)
 
 
 # --------------------------------------------------------------------------- compressor

@@ -220,6 +220,8 @@ ROWS = {
                       "slot queries x 64 heads (d 64, fp16) over 36 compressed rows + the 5 "
                       "slots, bidirectional within the block", 24),
     "tree60_accept": ("qwen7b_tree60", "greedy tree acceptance, 61 nodes over 152,064", 28),
+    "tree60_sample": ("qwen7b_tree60", "sampling tree acceptance (recursive rejection), Tree-60 "
+                      "over 152,064 (target + draft logits, T = 1)", 16),
     "commit_7b": ("qwen7b_25k", "cycle commit, 7B layer: the block's 16 K/V rows appended to "
                   "the paged cache (sv_kv_append), then the context-length and anchor update "
                   "(sv_commit); 32 calls per graph, inputs not rotated (64 KB)", 32),
@@ -329,6 +331,24 @@ def run_row(args):
 
         def call(i, st):
             sv.accept_greedy_tree(lg[i], par, tok, want_argmax=False, out=outs, stream=st)
+    elif args.row == "tree60_sample":
+        ts = W.make_workload_tree_sample(wl, 0)
+        tl = [dev_t(ts.target_logits, ts.dtype)]
+        dl = [dev_t(ts.draft_logits, ts.dtype)]
+        tl += [tl[0].clone() for _ in range(R - 1)]
+        dl += [dl[0].clone() for _ in range(R - 1)]
+        tk = i32(ts.tokens)
+        par = [int(x) for x in ts.parents]
+        outs = (torch.empty(ts.B, dtype=torch.int32, device=dev),
+                torch.empty(ts.B, ts.K, dtype=torch.int32, device=dev),
+                torch.empty(ts.B, ts.K, dtype=torch.int32, device=dev))
+        sv.accept_sample_tree(tl[0], dl[0], par, tk, ts.temperature, ts.seed, 0, out=outs)
+        nbytes = (tl[0].numel() + dl[0].numel()) * tl[0].element_size()
+        shape = {"B": ts.B, "K": ts.K, "V": ts.V, "T": ts.temperature}
+
+        def call(i, st):
+            sv.accept_sample_tree(tl[i], dl[i], par, tk, ts.temperature, ts.seed, i, out=outs,
+                                  stream=st)
     elif args.row == "lm_head":
         li = W.make_workload_lm_head(wl)
         hs = dev_t(li.hidden_states, li.dtype)

@@ -13,17 +13,20 @@
 //
 // Launches (the tree is host data, shared by the batch, so its shape fixes the plan):
 //   1. row_lse_kernel (the chain's): per-chunk (max, sum) of every target and draft row;
-//   2. for j = 1 .. (largest child count - 1): tree_residual_kernel, grid (vocabulary
-//      chunk, sequence x node with more than j children): the partial sums of Z_j at
-//      every such node, the residual rebuilt element by element from p_u, the first j
-//      draft rows and Z_1 .. Z_{j-1} (fp64);
-//   3. tree_walk_kernel, one workgroup per sequence: the row log-normalisers, every
-//      child's threshold and ACCEPT uniform (lane = node), then the walk from the anchor;
-//   4. tree_race_kernel, grid (1024-entry chunk, sequence): the exponential race over the
+//   2. tree_norm_kernel: every row's log-normaliser, one wave per row, into a table;
+//   3. for j = 1 .. (largest child count - 1): tree_residual_kernel, grid (1024-entry
+//      vocabulary chunk, sequence x node with more than j children): the residual after
+//      the j-th child, max(0, rhat_{j-1} - q_j), stored per element in fp64 (one row per
+//      branching node, updated in place pass after pass) and its partial sums, which the
+//      next pass folds into Z_j; after the last pass tree_z_kernel folds the last ones;
+//   4. tree_walk_kernel, one wave per sequence: every child's threshold and ACCEPT uniform
+//      (lane = node), then the walk from the anchor;
+//   5. tree_race_kernel, grid (1024-entry chunk, sequence): the exponential race over the
 //      stop node's last residual (the chain's race: RESAMPLE uniforms of the stop row,
 //      with a race over p_u carried along for an all-zero residual);
-//   5. tree_finish_kernel, one workgroup per sequence: the winner and the outputs.
+//   6. tree_finish_kernel, one workgroup per sequence: the winner and the outputs.
 // Kernel boundaries order everything; the workspace carries no state between calls.
+// Every reduction runs in a fixed order, so results are bitwise reproducible.
 #include <math.h>
 
 #include "common.hpp"
@@ -34,31 +37,9 @@ namespace sv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kZChunk = 16 * kThreads;            // vocabulary entries per residual workgroup
+constexpr int kZChunk = 4 * kThreads;             // vocabulary entries per residual workgroup
 constexpr int kRaceChunk = 4 * kThreads;          // vocabulary entries per race workgroup
 constexpr uint64_t kResample = 1ull << 32;        // RESAMPLE purpose in counter word 2
-
-// Log-normaliser L = m/T + log sum_c s_c e^((m_c - m)/T) of row rho from the chunk partials
-// (fixed order; the chain's combine).
-__device__ __forceinline__ double row_norm(const float* part_m, const double* part_s, int rho,
-                                           int nchunk, double it) {
-  const float* pm = part_m + static_cast<size_t>(rho) * nchunk;
-  const double* ps = part_s + static_cast<size_t>(rho) * nchunk;
-  float m = -INFINITY;
-  for (int q = 0; q < nchunk; ++q) m = fmaxf(m, pm[q]);
-  double s = 0.0;
-  for (int q = 0; q < nchunk; ++q)
-    s += ps[q] * exp((static_cast<double>(pm[q]) - static_cast<double>(m)) * it);
-  return static_cast<double>(m) * it + log(s);
-}
-
-// Z of the residual left by rejecting child node c (fixed-order sum of its partials).
-__device__ __forceinline__ double z_of(const double* zpart, int b, int K, int c, int nz) {
-  const double* z = zpart + (static_cast<size_t>(b) * K + c) * nz;
-  double s = 0.0;
-  for (int q = 0; q < nz; ++q) s += z[q];
-  return s;
-}
 
 // Row index rho of target row u / draft row of node c for the row_lse partials.
 __device__ __forceinline__ int target_rho(int b, int K, int u) { return b * K + u; }
@@ -66,12 +47,33 @@ __device__ __forceinline__ int draft_rho(int B, int b, int K, int c) {
   return B * K + b * (K - 1) + (c - 1);
 }
 
-// ---- 2. residual normalisers, round j: Z of the residual after rejecting the j-th child
+// ---- 2. every row's log-normaliser L = m/T + log sum_c s_c e^((m_c - m)/T), one wave per
+// row (lanes stride over the chunk partials; fixed shuffle order)
+__global__ void __launch_bounds__(kThreads)
+tree_norm_kernel(int32_t rows, const TreeSampleParams p) {
+  const int lane = threadIdx.x & 63;
+  const int rho = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  if (rho >= rows) return;                         // whole waves
+  const float* pm = p.part_m + static_cast<size_t>(rho) * p.nchunk;
+  const double* ps = p.part_s + static_cast<size_t>(rho) * p.nchunk;
+  float m = -INFINITY;
+  for (int q = lane; q < p.nchunk; q += kWave) m = fmaxf(m, pm[q]);
+  m = wave_max(m);
+  double s = 0.0;
+  for (int q = lane; q < p.nchunk; q += kWave)
+    s += ps[q] * exp((static_cast<double>(pm[q]) - static_cast<double>(m)) * p.inv_t);
+  s = wave_sum_f64(s);
+  if (lane == 0) p.lnorm[rho] = static_cast<double>(m) * p.inv_t + log(s);
+}
+
+// ---- 3a. residual pass j at every node with more than j children: the residual after
+// rejecting the j-th child, raw_j = max(0, rhat_{j-1} - q_j), stored per element (fp64) for
+// the next pass, and its partial sums.  rhat_0 = p_u; rhat_{j-1} = raw_{j-1} / Z_{j-1}
+// (p_u if Z_{j-1} = 0), with Z_{j-1} folded here from the previous pass's partial sums.
 template <bool kBF16>
 __global__ void __launch_bounds__(kThreads)
 tree_residual_kernel(int32_t j, int32_t n_nodes, const TreeSampleParams p) {
-  __shared__ double Lp_sh, Lq_sh[kMaxBlock], Z_sh[kMaxBlock];
-  __shared__ int32_t kid_sh[kMaxBlock];
+  __shared__ double zprev_sh;
   __shared__ double red[kThreads / kWave];
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
@@ -80,31 +82,54 @@ tree_residual_kernel(int32_t j, int32_t n_nodes, const TreeSampleParams p) {
   const int K = p.K, V = p.V;
   const double it = p.inv_t;
   const int first = p.child_start[u];
-  if (tid <= j) {                                  // lane 0: p_u; lane i: child i's row
+  const int c = p.child_list[first + j - 1];       // the child this pass subtracts
+  const double Lp = p.lnorm[target_rho(b, K, u)];
+  const double Lq = p.lnorm[draft_rho(p.B, b, K, c)];
+  double* buf = p.resid + (static_cast<size_t>(b) * p.nbranch + p.branch_slot[u]) * V;
+  const size_t trow = (static_cast<size_t>(b) * K + u) * V;
+  const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (c - 1)) * V;
+  // this thread's elements are loaded before the fold of Z_{j-1}, so the two round trips
+  // overlap (clamped, in-bounds indices; elements past V are dropped below)
+  constexpr int EPT = kZChunk / kThreads;
+  float xq[EPT], xp[EPT];
+  double rb[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int v = min(chunk * kZChunk + e * kThreads + tid, V - 1);
+    xq[e] = logit_at<kBF16>(p.draft, qrow + v);
+    if (j == 1) xp[e] = logit_at<kBF16>(p.target, trow + v);
+    else rb[e] = buf[v];
+  }
+  if (j > 1 && tid < kWave) {                      // Z_{j-1}, from the previous pass
+    const int cp = p.child_list[first + j - 2];
+    const double* z = p.zpart + (static_cast<size_t>(b) * K + cp) * p.nz;
+    double s = 0.0;
+    for (int q = tid; q < p.nz; q += kWave) s += z[q];
+    s = wave_sum_f64(s);
     if (tid == 0) {
-      Lp_sh = row_norm(p.part_m, p.part_s, target_rho(b, K, u), p.nchunk, it);
-    } else {
-      const int c = p.child_list[first + tid - 1];
-      kid_sh[tid - 1] = c;
-      Lq_sh[tid - 1] = row_norm(p.part_m, p.part_s, draft_rho(p.B, b, K, c), p.nchunk, it);
-      if (tid < j) Z_sh[tid - 1] = z_of(p.zpart, b, K, c, p.nz);
+      zprev_sh = s;
+      if (chunk == 0) p.ztab[static_cast<size_t>(b) * K + cp] = s;
     }
   }
   __syncthreads();
-  const size_t trow = (static_cast<size_t>(b) * K + u) * V;
+  const double zp = j > 1 ? zprev_sh : 1.0;
+  if (j > 1 && !(zp > 0.0)) {                      // Z_{j-1} = 0: the residual restarts at p_u
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      xp[e] = logit_at<kBF16>(p.target, trow + min(chunk * kZChunk + e * kThreads + tid, V - 1));
+  }
+  const bool from_p = j == 1 || !(zp > 0.0);
   double sum = 0.0;
-  for (int e = 0; e < kZChunk / kThreads; ++e) {
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
     const int v = chunk * kZChunk + e * kThreads + tid;
-    if (v >= V) break;
-    const double pv = exp(static_cast<double>(logit_at<kBF16>(p.target, trow + v)) * it - Lp_sh);
-    double r = pv, raw = 0.0;
-    for (int i = 0; i < j; ++i) {
-      const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (kid_sh[i] - 1)) * V;
-      const double qv = exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow + v)) * it - Lq_sh[i]);
-      raw = fmax(0.0, r - qv);
-      if (i + 1 < j) r = Z_sh[i] > 0.0 ? raw / Z_sh[i] : pv;
+    if (v < V) {
+      const double r = from_p ? exp(static_cast<double>(xp[e]) * it - Lp) : rb[e] / zp;
+      const double qv = exp(static_cast<double>(xq[e]) * it - Lq);
+      const double raw = fmax(0.0, r - qv);
+      buf[v] = raw;
+      sum += raw;
     }
-    sum += raw;
   }
   sum = wave_sum_f64(sum);
   if ((tid & 63) == 0) red[tid >> 6] = sum;
@@ -113,25 +138,34 @@ tree_residual_kernel(int32_t j, int32_t n_nodes, const TreeSampleParams p) {
     double t = 0.0;
 #pragma unroll
     for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
-    p.zpart[(static_cast<size_t>(b) * K + kid_sh[j - 1]) * p.nz + chunk] = t;
+    p.zpart[(static_cast<size_t>(b) * K + c) * p.nz + chunk] = t;
   }
 }
 
-// ---- 3. the tests and the walk, one workgroup per sequence
+// ---- 3b. after the last pass: Z of the last subtracted child of every branching node
+// (the earlier ones were folded by the passes), one wave per (sequence, node)
+__global__ void __launch_bounds__(kWave)
+tree_z_kernel(int32_t n_nodes, const TreeSampleParams p) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / n_nodes;
+  const int u = p.by_count[blockIdx.x - b * n_nodes];
+  const int c = p.child_list[p.child_start[u] + p.child_count[u] - 2];
+  const double* z = p.zpart + (static_cast<size_t>(b) * p.K + c) * p.nz;
+  double s = 0.0;
+  for (int q = lane; q < p.nz; q += kWave) s += z[q];
+  s = wave_sum_f64(s);
+  if (lane == 0) p.ztab[static_cast<size_t>(b) * p.K + c] = s;
+}
+
+// ---- 4. the tests and the walk, one wave per sequence
 template <bool kBF16>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kWave)
 tree_walk_kernel(const TreeSampleParams p) {
-  __shared__ double Lrow[2 * kMaxBlock];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int K = p.K, V = p.V;
   const double it = p.inv_t;
-  for (int row = tid; row < 2 * K - 1; row += kThreads)
-    Lrow[row] = row_norm(p.part_m, p.part_s,
-                         row < K ? target_rho(b, K, row) : draft_rho(p.B, b, K, row - K + 1),
-                         p.nchunk, it);
-  __syncthreads();
-  if (tid >= 64) return;
+  const double* L = p.lnorm;
   const int lane = tid;
   const int c = lane + 1;                          // the draft node this lane tests
   const bool node = c < K;
@@ -146,19 +180,21 @@ tree_walk_kernel(const TreeSampleParams p) {
       double thr = 0.0;
       if (lp != -INFINITY) {
         if (jj == 0) {                             // against p_u: the chain's log form
-          thr = exp(fmin(0.0, (lp - lq) * it - (Lrow[u] - Lrow[K + c - 1])));
+          thr = exp(fmin(0.0, (lp - lq) * it - (L[target_rho(b, K, u)] -
+                                                 L[draft_rho(p.B, b, K, c)])));
         } else {
-          const double pv = exp(lp * it - Lrow[u]);
+          const double pv = exp(lp * it - L[target_rho(b, K, u)]);
           double r = pv;
+#pragma unroll 4
           for (int i = 0; i < jj; ++i) {
             const int ci = p.child_list[p.child_start[u] + i];
             const double lqi = logit_at<kBF16>(p.draft, (static_cast<size_t>(b) * (K - 1) + (ci - 1)) * V + x);
-            const double qi = exp(lqi * it - Lrow[K + ci - 1]);
+            const double qi = exp(lqi * it - L[draft_rho(p.B, b, K, ci)]);
             const double raw = fmax(0.0, r - qi);
-            const double z = z_of(p.zpart, b, K, ci, p.nz);
+            const double z = p.ztab[static_cast<size_t>(b) * K + ci];
             r = z > 0.0 ? raw / z : pv;
           }
-          const double qc = exp(lq * it - Lrow[K + c - 1]);
+          const double qc = exp(lq * it - L[draft_rho(p.B, b, K, c)]);
           thr = r == 0.0 ? 0.0 : (qc == 0.0 ? 1.0 : fmin(1.0, r / qc));
         }
       }
@@ -194,12 +230,10 @@ tree_walk_kernel(const TreeSampleParams p) {
   }
 }
 
-// ---- 4. the race over the stop node's last residual
+// ---- 5. the race over the stop node's last residual
 template <bool kBF16>
 __global__ void __launch_bounds__(kThreads)
 tree_race_kernel(const TreeSampleParams p) {
-  __shared__ double Lp_sh, Lq_sh[kMaxBlock], Z_sh[kMaxBlock];
-  __shared__ int32_t kid_sh[kMaxBlock];
   __shared__ double rk[2][kThreads / kWave];
   __shared__ int32_t ri[2][kThreads / kWave];
   const int tid = threadIdx.x;
@@ -209,19 +243,15 @@ tree_race_kernel(const TreeSampleParams p) {
   const double it = p.inv_t;
   const int u = p.stop[2 * b];
   const int m = p.stop[2 * b + 1];                 // children rejected at u
-  const int first = p.child_start[u];
-  if (tid <= m) {
-    if (tid == 0) {
-      Lp_sh = row_norm(p.part_m, p.part_s, target_rho(b, K, u), p.nchunk, it);
-    } else {
-      const int c = p.child_list[first + tid - 1];
-      kid_sh[tid - 1] = c;
-      Lq_sh[tid - 1] = row_norm(p.part_m, p.part_s, draft_rho(p.B, b, K, c), p.nchunk, it);
-      if (tid < m) Z_sh[tid - 1] = z_of(p.zpart, b, K, c, p.nz);
-    }
-  }
-  __syncthreads();
+  const double Lp = p.lnorm[target_rho(b, K, u)];
+  const int c = m > 0 ? p.child_list[p.child_start[u] + m - 1] : 1;   // the last one
+  const double Lq = m > 0 ? p.lnorm[draft_rho(p.B, b, K, c)] : 0.0;
+  const double zp = m > 1 ? p.ztab[static_cast<size_t>(b) * K + p.child_list[p.child_start[u] + m - 2]]
+                          : 1.0;
+  const bool from_buf = m > 1 && zp > 0.0;         // rhat_{m-1} from the stored residual
+  const double* buf = p.resid + (static_cast<size_t>(b) * p.nbranch + p.branch_slot[u]) * V;
   const size_t trow = (static_cast<size_t>(b) * K + u) * V;
+  const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (c - 1)) * V;
   const int jb = chunk * p.race_chunk + 4 * tid;
   double bk_r = INFINITY, bk_p = INFINITY;
   int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
@@ -232,13 +262,12 @@ tree_race_kernel(const TreeSampleParams p) {
     for (int e = 0; e < 4; ++e) {
       const int v = jb + e;
       if (v >= V) break;
-      const double pv = exp(static_cast<double>(logit_at<kBF16>(p.target, trow + v)) * it - Lp_sh);
+      const double pv = exp(static_cast<double>(logit_at<kBF16>(p.target, trow + v)) * it - Lp);
       double r = pv;
-      for (int i = 0; i < m; ++i) {
-        const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (kid_sh[i] - 1)) * V;
-        const double qv = exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow + v)) * it - Lq_sh[i]);
-        const double raw = fmax(0.0, r - qv);
-        r = (i + 1 < m) ? (Z_sh[i] > 0.0 ? raw / Z_sh[i] : pv) : raw;
+      if (m > 0) {
+        const double rh = from_buf ? buf[v] / zp : pv;
+        const double qv = exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow + v)) * it - Lq);
+        r = fmax(0.0, rh - qv);
       }
       const double ej = -log1p(-to_uniform(w.x[e]));
       if (r > 0.0) {
@@ -261,7 +290,7 @@ tree_race_kernel(const TreeSampleParams p) {
   }
 }
 
-// ---- 5. the winner over every chunk, then the drawn token at slot accept_len
+// ---- 6. the winner over every chunk, then the drawn token at slot accept_len
 __global__ void __launch_bounds__(kThreads)
 tree_finish_kernel(const TreeSampleParams p) {
   __shared__ double rk[2][kThreads / kWave];
@@ -294,8 +323,12 @@ size_t sample_tree_workspace_bytes(int B, int K, int V) {
   size_t off = 0;
   off += rows * nchunk * sizeof(double);                        // part_s
   off += static_cast<size_t>(B) * K * nz * sizeof(double);      // zpart
+  off += static_cast<size_t>(B) * (K / 2) * V * sizeof(double); // resid: at most K/2 branching nodes
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(double);   // race_key
   off += rows * nchunk * sizeof(float);                         // part_m
+  off = (off + 7) & ~static_cast<size_t>(7);
+  off += rows * sizeof(double);                                 // lnorm
+  off += static_cast<size_t>(B) * K * sizeof(double);           // ztab
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(int32_t);  // race_idx
   off += static_cast<size_t>(B) * 2 * sizeof(int32_t);          // stop
   return (off + 15) & ~static_cast<size_t>(15);
@@ -329,6 +362,11 @@ int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host) {
     p.child_start[i] = 0;
     p.child_count[i] = 0;
   }
+  int nbr = 0;
+  for (int u = 0; u < kMaxBlock; ++u) p.branch_slot[u] = 0;
+  for (int u = 0; u < K; ++u)
+    if (count[u] > 1) p.branch_slot[u] = static_cast<int8_t>(nbr++);
+  p.nbranch = nbr > 0 ? nbr : 1;
   int nb = 0, mmax = 0;
   for (int cnt = K - 1; cnt >= 1; --cnt)        // nodes by decreasing child count
     for (int u = 0; u < K; ++u)
@@ -352,6 +390,11 @@ hipError_t launch_sample_tree(const TreeSampleParams& p, int rounds, sv_dtype dt
   lse.inv_t = p.inv_t;
   hipError_t e = launch_row_lse(lse, dtype, stream);
   if (e != hipSuccess) return e;
+  const int rows = p.B * (2 * p.K - 1);
+  hipLaunchKernelGGL(tree_norm_kernel, dim3((rows + kThreads / kWave - 1) / (kThreads / kWave)),
+                     dim3(kThreads), 0, stream, rows, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const bool bf = dtype == SV_BF16;
   for (int j = 1; j <= rounds; ++j) {
     int n = 0;                                    // nodes with more than j children
@@ -362,8 +405,15 @@ hipError_t launch_sample_tree(const TreeSampleParams& p, int rounds, sv_dtype dt
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (bf) hipLaunchKernelGGL(tree_walk_kernel<true>, dim3(p.B), dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL(tree_walk_kernel<false>, dim3(p.B), dim3(kThreads), 0, stream, p);
+  if (rounds > 0) {
+    int n = 0;                                    // branching nodes
+    for (int u = 0; u < p.K; ++u) n += p.child_count[u] > 1 ? 1 : 0;
+    hipLaunchKernelGGL(tree_z_kernel, dim3(p.B * n), dim3(kWave), 0, stream, n, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (bf) hipLaunchKernelGGL(tree_walk_kernel<true>, dim3(p.B), dim3(kWave), 0, stream, p);
+  else hipLaunchKernelGGL(tree_walk_kernel<false>, dim3(p.B), dim3(kWave), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gr(p.race_nchunk, p.B);

@@ -514,10 +514,17 @@ sv_status sv_accept_sample_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_
   w += rows * p.nchunk * sizeof(double);
   p.zpart = reinterpret_cast<double*>(w);
   w += static_cast<size_t>(B) * K * p.nz * sizeof(double);
+  p.resid = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(B) * (K / 2) * V * sizeof(double);
   p.race_key = reinterpret_cast<double*>(w);
   w += static_cast<size_t>(B) * p.race_nchunk * 2 * sizeof(double);
   p.part_m = reinterpret_cast<float*>(w);
   w += rows * p.nchunk * sizeof(float);
+  w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(w) + 7) & ~static_cast<uintptr_t>(7));
+  p.lnorm = reinterpret_cast<double*>(w);
+  w += rows * sizeof(double);
+  p.ztab = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(B) * K * sizeof(double);
   p.race_idx = reinterpret_cast<int32_t*>(w);
   w += static_cast<size_t>(B) * p.race_nchunk * 2 * sizeof(int32_t);
   p.stop = reinterpret_cast<int32_t*>(w);

@@ -133,6 +133,9 @@ struct TreeSampleParams {
   const float* part_m;        // [B*(2K-1)][nchunk] row_lse partials (target rows, then draft)
   const double* part_s;
   double* zpart;              // [B][K][nz] partial sums of each residual, slot = child node
+  double* ztab;               // [B][K] Z of the residual left by rejecting each child
+  double* resid;              // [B][nbranch][V] residual of each branching node (fp64)
+  double* lnorm;              // [B*(2K-1)] row log-normalisers (row_lse row order)
   double* race_key;           // [B][race_nchunk][2]
   int32_t* race_idx;
   int32_t* stop;              // [B][2]: node the walk stopped at, its children (all rejected)
@@ -148,6 +151,8 @@ struct TreeSampleParams {
   int8_t child_count[kMaxBlock];
   int8_t child_list[kMaxBlock];   // children grouped by parent, increasing node order
   int8_t by_count[kMaxBlock];     // nodes by decreasing child count (ties: node order)
+  int8_t branch_slot[kMaxBlock];  // row of resid of each node with two or more children
+  int32_t nbranch;
 };
 
 size_t sample_tree_workspace_bytes(int B, int K, int V);

@@ -377,7 +377,7 @@ int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host) {
 
 hipError_t launch_sample_tree(const TreeSampleParams& p, int rounds, sv_dtype dtype,
                               hipStream_t stream) {
-  SampleParams lse;
+  SampleParams lse{};
   lse.target = p.target;
   lse.draft = p.draft;
   lse.B = p.B;

@@ -364,3 +364,14 @@ def test_sample_masked_vocabulary(gpu_lib):
         assert acc[0] == 0
         tk = toks[np.arange(B), acc]
         assert not (((tk >= 8192) & (tk < 24576)) | ((tk >= 30001) & (tk < 31234))).any()
+
+
+def test_sample_many_chunk_partials(gpu_lib):
+    """K = 64 over a 300,000-token vocabulary: more chunk partials per sequence than a race
+    workgroup folds itself, so the separate normaliser pass runs."""
+    rng = np.random.default_rng(3030)
+    s = W.make_sample(rng, B=1, K=64, V=300000, dtype="bf16", seed=17, offset=0)
+    for off in range(3):
+        s.offset = off
+        say(f"[sample] K=64 V=300000 offset={off}")
+        assert_sample(gpu_lib, s, f"wide/{off}")

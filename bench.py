@@ -56,7 +56,7 @@ def parse():
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("attention.hip", "api.cpp", "common.hpp", "internal.hpp"):   # kernels + split plan
+    for f in ("attention.hip", "attention.hpp", "limits.hpp", "common.hpp"):  # kernels + split plan
         with open(os.path.join(ROOT, "block_verify_sv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

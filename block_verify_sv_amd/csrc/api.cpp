@@ -93,44 +93,6 @@ sv_status check_attn_desc(const sv_attn_desc* d) {
 
 }  // namespace
 
-namespace sv {
-
-AttnPlan plan_attention(const sv_attn_desc& d) {
-  AttnPlan pl;
-  const int64_t n_max = static_cast<int64_t>(d.max_ctx) + d.block;
-  pl.rows = d.block * (d.num_q_heads / d.num_kv_heads);
-  pl.row_halves = (pl.rows + 127) / 128;         // a workgroup holds 4 row blocks of 32
-  int64_t chunk = d.split_keys;
-  if (chunk == 0) {
-    // one workgroup per compute unit: total (context + block) keys over all KV heads and
-    // row halves, spread over the 256 CUs in whole 64-key tiles, and no longer than the
-    // longest sequence rounded up to min(P, 64) keys
-    const int64_t gran = d.page_size < 64 ? d.page_size : 64;
-    const int64_t ctx_sum =
-        d.sum_ctx_hint > 0 ? d.sum_ctx_hint : static_cast<int64_t>(d.batch) * d.max_ctx;
-    const int64_t work =
-        (ctx_sum + static_cast<int64_t>(d.batch) * d.block) * d.num_kv_heads * pl.row_halves;
-    chunk = (work + kNumCUs - 1) / kNumCUs;
-    // whole 64-key tiles: a split's last tile costs a full step however few keys it
-    // holds, so rounding up to the tile keeps the step count and needs fewer splits
-    chunk = (chunk + 63) / 64 * 64;
-    if (chunk < 64) chunk = 64;
-    const int64_t cap = (n_max + gran - 1) / gran * gran;
-    if (chunk > cap) chunk = cap;
-    if (chunk > kMaxSplitKeys) chunk = kMaxSplitKeys;
-  }
-  pl.chunk = static_cast<int>(chunk);
-  pl.nsplit = static_cast<int>((n_max + chunk - 1) / chunk);
-  const size_t esz = d.dtype == SV_F32 ? 4 : 2;
-  const size_t units = static_cast<size_t>(d.batch) * d.num_kv_heads * pl.nsplit;
-  // partial outputs are stored in whole 32-row blocks (the accumulator tile order)
-  const size_t padded_rows = static_cast<size_t>((pl.rows + 31) / 32 * 32);
-  pl.o_bytes = (units * padded_rows * d.head_dim * esz + 15) / 16 * 16;
-  pl.ws_bytes = pl.o_bytes + units * pl.rows * sizeof(float2);
-  return pl;
-}
-
-}  // namespace sv
 
 extern "C" {
 

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <string>
 
 #include "internal.hpp"
@@ -32,6 +33,20 @@ sv_status ok() {
 }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// The value a caller stored in an sv_dtype, read as its bytes: a C caller may pass any int,
+// and C++ may only load an enum value in the enumerators' range, so every check reads this.
+int32_t dtype_bits(const sv_dtype* p) {
+  int32_t v;
+  memcpy(&v, p, sizeof v);
+  return v;
+}
+
+bool dtype_in(int32_t v, std::initializer_list<sv_dtype> ok) {
+  for (sv_dtype d : ok)
+    if (v == static_cast<int32_t>(d)) return true;
+  return false;
+}
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -64,8 +79,8 @@ sv_status check_attn_desc(const sv_attn_desc* d) {
                 d->block * G, sv::kMaxRows);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(SV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
-  if (d->dtype != SV_F32 && d->dtype != SV_BF16 && d->dtype != SV_F16)
-    return fail(SV_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(d->dtype));
+  if (!dtype_in(dtype_bits(&d->dtype), {SV_F32, SV_BF16, SV_F16}))
+    return fail(SV_ERR_UNSUPPORTED, "unknown dtype %d", dtype_bits(&d->dtype));
   if (!pow2(d->page_size) || d->page_size < 16 || d->page_size > 256)
     return fail(SV_ERR_INVALID_ARG, "page_size must be a power of two in [16, 256] (got %d)",
                 d->page_size);
@@ -223,15 +238,16 @@ sv_status sv_accept_greedy_workspace(int32_t B, int32_t K, int32_t V, size_t* by
 }
 
 // The chain (parents == nullptr) and the tree walk share the argmax pass.
-static sv_status greedy_call(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype,
+static sv_status greedy_call(int32_t B, int32_t K, int32_t V, int32_t dtype_raw,
                              const void* logits, const int32_t* drafts, const int32_t* parents,
                              int32_t* path, int32_t* accept_len, int32_t* out_tokens,
                              int32_t* argmax, void* workspace, size_t workspace_bytes,
                              void* stream, const char* what) {
   sv_status st = check_accept_shape(B, K, V, 1);
   if (st != SV_OK) return st;
-  if (logit_dtype != SV_F32 && logit_dtype != SV_BF16)
+  if (!dtype_in(dtype_raw, {SV_F32, SV_BF16}))
     return fail(SV_ERR_UNSUPPORTED, "greedy logits must be SV_F32 or SV_BF16");
+  const sv_dtype logit_dtype = static_cast<sv_dtype>(dtype_raw);
   if (!logits || !accept_len || !out_tokens || (K > 1 && !drafts))
     return fail(SV_ERR_INVALID_ARG, "logits, drafts, accept_len and out_tokens are required");
   if (!aligned16(logits)) return fail(SV_ERR_INVALID_ARG, "logits must be 16-byte aligned");
@@ -264,7 +280,7 @@ sv_status sv_accept_greedy(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
                            const void* logits, const int32_t* drafts, int32_t* accept_len,
                            int32_t* out_tokens, int32_t* argmax, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return greedy_call(B, K, V, logit_dtype, logits, drafts, nullptr, nullptr, accept_len,
+  return greedy_call(B, K, V, dtype_bits(&logit_dtype), logits, drafts, nullptr, nullptr, accept_len,
                      out_tokens, argmax, workspace, workspace_bytes, stream,
                      "sv_accept_greedy launch");
 }
@@ -276,7 +292,7 @@ sv_status sv_accept_greedy_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_
                                 void* workspace, size_t workspace_bytes, void* stream) {
   if (K > 1 && !parents) return fail(SV_ERR_INVALID_ARG, "parents is required");
   if (!accept_path) return fail(SV_ERR_INVALID_ARG, "accept_path is required");
-  return greedy_call(B, K, V, logit_dtype, logits, tokens, parents, accept_path, accept_len,
+  return greedy_call(B, K, V, dtype_bits(&logit_dtype), logits, tokens, parents, accept_path, accept_len,
                      out_tokens, argmax, workspace, workspace_bytes, stream,
                      "sv_accept_greedy_tree launch");
 }
@@ -308,7 +324,7 @@ sv_status sv_lm_head_greedy(int32_t B, int32_t K, int32_t V, int32_t hidden, sv_
                             void* stream) {
   sv_status st = check_lm_head(B, K, V, hidden);
   if (st != SV_OK) return st;
-  if (dtype != SV_BF16 && dtype != SV_F16)
+  if (!dtype_in(dtype_bits(&dtype), {SV_BF16, SV_F16}))
     return fail(SV_ERR_UNSUPPORTED, "LM head operands must be SV_BF16 or SV_F16");
   if (!hidden_states || !weight || !accept_len || !out_tokens || (K > 1 && !drafts))
     return fail(SV_ERR_INVALID_ARG, "hidden_states, weight, drafts and outputs are required");
@@ -365,7 +381,7 @@ sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
   if (st != SV_OK) return st;
   if (static_cast<int64_t>(B) * (2 * K - 1) > 65535)
     return fail(SV_ERR_INVALID_ARG, "B * (2K - 1) must be <= 65535");
-  if (logit_dtype != SV_F32 && logit_dtype != SV_BF16)
+  if (!dtype_in(dtype_bits(&logit_dtype), {SV_F32, SV_BF16}))
     return fail(SV_ERR_UNSUPPORTED, "sampling logits must be SV_F32 or SV_BF16");
   if (!(temperature > 0.0f) || !isfinite(temperature))
     return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0 (use sv_accept_greedy for 0)");
@@ -433,7 +449,7 @@ sv_status sv_accept_sample_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_
   if (st != SV_OK) return st;
   if (static_cast<int64_t>(B) * (2 * K - 1) > 65535)
     return fail(SV_ERR_INVALID_ARG, "B * (2K - 1) must be <= 65535");
-  if (logit_dtype != SV_F32 && logit_dtype != SV_BF16)
+  if (!dtype_in(dtype_bits(&logit_dtype), {SV_F32, SV_BF16}))
     return fail(SV_ERR_UNSUPPORTED, "sampling logits must be SV_F32 or SV_BF16");
   if (!(temperature > 0.0f) || !isfinite(temperature))
     return fail(SV_ERR_INVALID_ARG, "temperature must be finite and > 0 (use the greedy calls for 0)");
@@ -518,7 +534,8 @@ sv_status sv_latent_compress(int32_t B, int32_t C, int32_t N, int32_t D, sv_dtyp
                              void* workspace, size_t workspace_bytes, void* stream) {
   sv_status st = check_compress(B, C, N, D);
   if (st != SV_OK) return st;
-  if (dtype != SV_F16) return fail(SV_ERR_UNSUPPORTED, "the compressor takes SV_F16 tensors");
+  if (!dtype_in(dtype_bits(&dtype), {SV_F16}))
+    return fail(SV_ERR_UNSUPPORTED, "the compressor takes SV_F16 tensors");
   if (!queries || !feats || !out) return fail(SV_ERR_INVALID_ARG, "queries, feats and out are required");
   if (!aligned16(queries) || !aligned16(feats) || !aligned16(out))
     return fail(SV_ERR_INVALID_ARG, "queries, feats and out must be 16-byte aligned");
@@ -555,7 +572,7 @@ sv_status sv_kv_append(const sv_attn_desc* desc, int32_t n, const void* k_new, c
     return fail(SV_ERR_INVALID_ARG, "page_size must be a power of two in [16, 256]");
   if (desc->max_pages_per_seq < 1 || desc->num_pages < 1)
     return fail(SV_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
-  if (desc->dtype != SV_F32 && desc->dtype != SV_BF16 && desc->dtype != SV_F16)
+  if (!dtype_in(dtype_bits(&desc->dtype), {SV_F32, SV_BF16, SV_F16}))
     return fail(SV_ERR_UNSUPPORTED, "unknown dtype");
   if (n < 1 || n > 65535) return fail(SV_ERR_INVALID_ARG, "n must be in [1, 65535] (got %d)", n);
   if (!k_new || !v_new || !start || !page_table || !k_cache || !v_cache)
@@ -612,7 +629,7 @@ sv_status sv_commit_tree(const sv_attn_desc* desc, const int32_t* accept_len,
     return fail(SV_ERR_INVALID_ARG, "page_size must be a power of two in [16, 256]");
   if (desc->max_pages_per_seq < 1 || desc->num_pages < 1)
     return fail(SV_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be >= 1");
-  if (desc->dtype != SV_F32 && desc->dtype != SV_BF16 && desc->dtype != SV_F16)
+  if (!dtype_in(dtype_bits(&desc->dtype), {SV_F32, SV_BF16, SV_F16}))
     return fail(SV_ERR_UNSUPPORTED, "unknown dtype");
   if (!accept_len || !out_tokens || !accept_path || !page_table || !k_cache || !v_cache ||
       !ctx_lens || !next_anchor)

@@ -247,3 +247,20 @@ def test_sample_tree_validation(lib):
     assert call(good, ws=ctypes.c_void_p(0x1008)) == INVALID
     assert call(good, tl=ctypes.c_void_p(0x1008)) == INVALID
 
+
+def test_out_of_range_dtype_values(lib):
+    """A C caller may pass any int as an sv_dtype: every entry point rejects values outside
+    the enumerators as unsupported, before touching anything else."""
+    for bad in (7, -1, 1 << 20):
+        assert lib.sv_accept_greedy(1, 4, 100, bad, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20,
+                                    None) == UNSUPPORTED
+        assert lib.sv_accept_sample(1, 4, 100, bad, FAKE, FAKE, FAKE, 1.0, 1, 0, FAKE, FAKE, FAKE,
+                                    1 << 30, None) == UNSUPPORTED
+        assert lib.sv_latent_compress(2, 4, 8, 128, bad, FAKE, FAKE, FAKE, 1.0, FAKE, 1 << 20,
+                                      None) == UNSUPPORTED
+        assert lib.sv_lm_head_greedy(1, 4, 100, 64, bad, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                     1 << 20, None) == UNSUPPORTED
+        d = _desc(dtype=bad)
+        assert lib.sv_kv_append(ctypes.byref(d), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                None) == UNSUPPORTED
+

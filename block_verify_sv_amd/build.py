@@ -4,8 +4,10 @@
 
 Objects go to ``block_verify_sv_amd/_build/``; the library to
 ``block_verify_sv_amd/libspecverify.so``.  The streaming-read probe the benchmark uses
-for its bandwidth ceiling is linked on its own into ``libsvprobe.so`` (measurement only;
-the verification library does not contain it).  Every call recompiles.
+for its bandwidth ceiling and the Philox probe the tests use to compare the device
+generator's words with the oracle's are linked on their own into ``libsvprobe.so``
+(measurement and test only; the verification library does not contain them).  Every
+call recompiles.
 """
 import os
 import subprocess
@@ -23,7 +25,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.cpp", "attention.hip", "accept_greedy.hip", "accept_sample.hip",
            "compress.hip", "kv_append.hip", "commit.hip", "lm_head.hip", "noalloc.hip",
            "accept_sample_tree.hip"]
-PROBE_SOURCES = ["hbm_probe.hip"]
+PROBE_SOURCES = ["hbm_probe.hip", "philox_probe.hip"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

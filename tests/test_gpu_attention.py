@@ -145,12 +145,13 @@ def test_more_splits_than_one_merge_round(gpu_lib):
 
 
 def test_deterministic_repeats(gpu_lib):
+    """100 identical calls give bit-identical outputs (every reduction has a fixed order)."""
     inp = W.make_verify(np.random.default_rng(3), B=2, K=16, Hq=28, Hkv=4, D=128,
                         ctx_lens=[3000, 1234], P=16, dtype="bf16", shuffle=True)
     d = upload_verify(inp)
-    say("[attention] determinism x20")
+    say("[attention] determinism x100")
     first = None
-    for _ in range(20):
+    for _ in range(100):
         out, lse = gpu_lib.verify_attention(d["q"], d["k_cache"], d["v_cache"], d["page_table"],
                                             d["ctx_lens"], max_ctx=3000)
         if first is None:

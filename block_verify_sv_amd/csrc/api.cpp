@@ -203,9 +203,9 @@ sv_status attention_call(const sv_attn_desc* desc, const void* q, const void* k_
   // a multiple of 8 keeps split s of every head on one XCD (measured 1-2% faster on the
   // 7B and batched workloads) and lets row groups share an XCD; below 8 splits with one
   // row group the padding would mostly add empty workgroups (8x for a single split)
-  p.nsplit_pad = (pl.row_halves > 1 || pl.nsplit >= 8) ? (pl.nsplit + 7) / 8 * 8 : pl.nsplit;
+  p.nsplit_pad = (pl.row_groups > 1 || pl.nsplit >= 8) ? (pl.nsplit + 7) / 8 * 8 : pl.nsplit;
   p.direct = pl.nsplit == 1 ? 1 : 0;
-  p.row_halves = pl.row_halves;
+  p.row_groups = pl.row_groups;
   const float scale = desc->scale > 0.0f ? desc->scale : 1.0f / sqrtf(static_cast<float>(desc->head_dim));
   p.scale_log2 = scale * 1.4426950408889634f;
   return device_status(sv::launch_attention(p, desc->head_dim, desc->dtype,

@@ -5,10 +5,13 @@
 // of its head group form one dense (K*G) x d tile, so the scores S = Q_g K^T and the
 // update O += P V are matrix products and run on MFMA (32x32x16 bf16/f16, 32x32x2 fp32).
 //
-// Split pass: one workgroup per (sequence b, KV head g, key split s, group of 128 query
-// rows), sized so the grid is about one workgroup per compute unit.  Eight waves: wave
-// (rg, kh) owns query-row block rg (32 rows) and key half kh of every 64-key tile; the
-// two key halves of a row block combine through LDS at the end.  The split's page ids
+// Split pass: one workgroup per (sequence b, KV head g, key split s, group of query
+// rows), sized so the grid is about one workgroup per compute unit.  Eight waves.  Up to
+// 128 rows per KV head, wave (rg, kh) owns query-row block rg (32 rows) and key half kh
+// of every 64-key tile, and the two key halves of a row block combine through LDS at the
+// end.  With more rows (16-bit data) each wave owns one row block of a 256-row group and
+// every key of the tile, so a tile staged in LDS serves twice the rows; fp32 keeps the
+// 128-row groups (the full-tile wave would spill).  The split's page ids
 // are staged in LDS once, then keys stream in tiles of 64: a ring of four register tiles
 // keeps three tiles (96 KB at bf16, d = 128) of global loads in flight while the fourth
 // is written to one of two LDS buffers, so the HBM latency is covered without a
@@ -123,7 +126,7 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
   const int l32 = lane & 31;
   const int rg = wave % RG;                      // row group: row blocks rg + RG*t
   const int kh = wave / RG;                      // key part of each tile
-  // blockIdx.x = rgroup * nsplit_pad + s: the row groups of 128 rows of one split are
+  // blockIdx.x = rgroup * nsplit_pad + s: the row groups of one split are
   // nsplit_pad (then a multiple of 8) workgroups apart, so round-robin dispatch puts them
   // on one XCD and the later reads of each KV tile come from that XCD's L2
   // With LOADS_FIRST no branch comes before the tile loads are issued: an exit taken on
@@ -725,9 +728,10 @@ template <class Tag, int D>
 hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   // 4 row-group waves x 2 key halves, one row block each (512 threads, two waves per
   // SIMD), a deep register ring for 16-bit data.  More than 4 row blocks (K*G > 128)
-  // run as up to four row groups of 128 rows of the same split.  One sequence issues its
+  // run as row groups of the same split: 8 row-block waves over whole tiles (256 rows)
+  // for 16-bit data, up to four groups of 128 rows for fp32.  One sequence issues its
   // start-up loads before reading its context length; a batch reads it first.
-  const dim3 grid(p.nsplit_pad * p.row_halves, p.Hkv, p.B);
+  const dim3 grid(p.nsplit_pad * p.row_groups, p.Hkv, p.B);
 #define SPLIT_ARGS p.page_table, p.k_cache, p.v_cache, p.ctx_lens, p.chunk, p.nsplit_pad, \
                    p.P_log2, p.max_pages, p.num_pages, p.Hkv, p
 #define MERGE_ARGS p.part_o, p.part_ml, p.R, p.B, p.Hkv, p.nsplit, p
@@ -740,7 +744,12 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
     if (small)
       hipLaunchKernelGGL((attn_split_kernel<Tag, D, 1, 1, 2, 2, false>), grid, dim3(128), 0, stream, SPLIT_ARGS);
   }
-  if (!small) {
+  if (!small && Tag::kBytes == 2 && p.R > 128) {
+    if (p.B == 1)
+      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 8, 1, 1, RING, true>), grid, dim3(512), 0, stream, SPLIT_ARGS);
+    else
+      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 8, 1, 1, RING, false>), grid, dim3(512), 0, stream, SPLIT_ARGS);
+  } else if (!small) {
     if (p.B == 1)
       hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, true>), grid, dim3(512), 0, stream, SPLIT_ARGS);
     else
@@ -765,17 +774,20 @@ AttnPlan plan_attention(const sv_attn_desc& d) {
   AttnPlan pl;
   const int64_t n_max = static_cast<int64_t>(d.max_ctx) + d.block;
   pl.rows = d.block * (d.num_q_heads / d.num_kv_heads);
-  pl.row_halves = (pl.rows + 127) / 128;         // a workgroup holds 4 row blocks of 32
+  // a workgroup holds 4 row blocks of 32 (two key halves each), or 8 (whole tiles) when
+  // a 16-bit head group has more than 128 rows
+  const int group_rows = (d.dtype != SV_F32 && pl.rows > 128) ? 256 : 128;
+  pl.row_groups = (pl.rows + group_rows - 1) / group_rows;
   int64_t chunk = d.split_keys;
   if (chunk == 0) {
     // one workgroup per compute unit: total (context + block) keys over all KV heads and
-    // row halves, spread over the 256 CUs in whole 64-key tiles, and no longer than the
+    // row groups, spread over the 256 CUs in whole 64-key tiles, and no longer than the
     // longest sequence rounded up to min(P, 64) keys
     const int64_t gran = d.page_size < 64 ? d.page_size : 64;
     const int64_t ctx_sum =
         d.sum_ctx_hint > 0 ? d.sum_ctx_hint : static_cast<int64_t>(d.batch) * d.max_ctx;
     const int64_t work =
-        (ctx_sum + static_cast<int64_t>(d.batch) * d.block) * d.num_kv_heads * pl.row_halves;
+        (ctx_sum + static_cast<int64_t>(d.batch) * d.block) * d.num_kv_heads * pl.row_groups;
     chunk = (work + kNumCUs - 1) / kNumCUs;
     // whole 64-key tiles: a split's last tile costs a full step however few keys it
     // holds, so rounding up to the tile keeps the step count and needs fewer splits

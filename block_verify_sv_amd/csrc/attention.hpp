@@ -29,7 +29,8 @@ struct AttnParams {
   int32_t nsplit_pad;   // grid spacing of row groups: nsplit, rounded up to a multiple of 8
                         // from 8 splits up or when there are several row groups
   int32_t direct;       // 1: one split per (b, g); the split kernel writes out and lse
-  int32_t row_halves;   // row groups of 128 rows (4 row blocks each): ceil(K*G / 128)
+  int32_t row_groups;   // row groups per split: ceil(K*G / group rows), a group being
+                        // 256 rows for 16-bit data and 128 rows for fp32
   float scale_log2;     // scale * log2(e)
   uint64_t mask[kMaxBlock];
 };
@@ -37,7 +38,7 @@ struct AttnParams {
 struct AttnPlan {
   int chunk;
   int nsplit;
-  int row_halves;
+  int row_groups;
   int rows;             // R = K * G
   size_t o_bytes;       // partial outputs (16-byte aligned), then (m, l) pairs
   size_t ws_bytes;

@@ -55,7 +55,8 @@ CASES = [
     ("bf16", 128, 16, 28, 4, 16, [40], 0, "causal", True),       # 112 rows, 512 threads
     ("f16", 64, 16, 64, 64, 5, [64, 64, 17], 0, "ones", True),   # 5 rows: 128-thread pair
     ("f32", 64, 16, 4, 2, 4, [30, 0], 0, "random", False),
-    ("bf16", 128, 16, 64, 8, 32, [20], 0, "causal", False),      # 256 rows: two row groups
+    ("bf16", 128, 16, 64, 8, 32, [20], 0, "causal", False),      # 256 rows: one 256-row group
+    ("f32", 64, 16, 32, 4, 20, [40], 0, "causal", True),         # 160 rows, fp32: two groups of 128
     # at most 32 rows at d 64: the 128-thread workgroup over many splits (then the merge),
     # and a split longer than its 8192-key page-id stage (the 512-thread kernel instead)
     ("bf16", 64, 16, 8, 8, 5, [3000], 0, "causal", True),

@@ -1,5 +1,5 @@
 """GPU parity of draft-tree verification against the float64 oracle (needs an MI355X):
-tree-masked attention (up to 4 row groups of 128 rows per KV head), the greedy tree walk,
+tree-masked attention (up to 2 row groups of 256 rows per KV head, 4 of 128 for fp32), the greedy tree walk,
 the tree commit, and chained device-resident tree cycles."""
 import numpy as np
 import pytest
@@ -43,8 +43,10 @@ def test_tree60_layer_full_size(gpu_lib):
 
 TREE_CASES = [
     # dtype, D, P, Hq, Hkv, K, ctx, split_keys
-    ("bf16", 128, 16, 28, 4, 61, [1000], 0),        # 427 rows: 4 row groups
-    ("bf16", 128, 16, 28, 4, 40, [777, 31], 64),    # 280 rows: 3 row groups, many splits
+    ("bf16", 128, 16, 28, 4, 61, [1000], 0),        # 427 rows: 2 row groups of 256
+    ("bf16", 128, 16, 28, 4, 40, [777, 31], 64),    # 280 rows: 2 row groups, many splits
+    ("bf16", 64, 16, 32, 2, 20, [400, 90], 0),      # 320 rows at d 64, two sequences
+    ("f32", 128, 16, 28, 4, 40, [300], 0),          # 280 rows, fp32: 3 row groups of 128
     ("f16", 128, 32, 16, 2, 60, [300], 0),          # 480 rows
     ("f32", 64, 16, 16, 2, 64, [130, 5], 32),       # 512 rows (the limit), fp32
     ("bf16", 64, 16, 8, 8, 13, [0], 0),             # empty context, G = 1

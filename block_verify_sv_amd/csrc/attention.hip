@@ -64,6 +64,17 @@ __device__ __forceinline__ int key_of_reg(int r, int h) { return 16 * (r >> 3) +
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
+// Combine a lane's value with that of lane l ^ 32 through the gfx950 half swap (no LDS
+// round trip).  Both halves see the same two operands in the same order.
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Zero the 16-bit elements e >= keep of a 16-byte chunk (branch-free).
 __device__ __forceinline__ u32x4 keep16(u32x4 v, int keep) {
 #pragma unroll
@@ -400,7 +411,7 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
       float mt = sv[0];
 #pragma unroll
       for (int e = 1; e < 16 * KBW; ++e) mt = fmaxf(mt, sv[e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_halves(mt);
       if (__any(mt > m_run[t] + resc)) {         // wave-uniform: rare after the first tile
         const float m_new = fmaxf(m_run[t], mt);
         const float alpha = fast_exp2((m_run[t] - m_new) * c2);
@@ -481,7 +492,7 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
   // compute the combined (m, l) from the same two pairs (m = max of the two, each side
   // weighted by exp2 of its distance to m); the kh = 0 wave stores it.
 #pragma unroll
-  for (int t = 0; t < NRB; ++t) l_run[t] += __shfl_xor(l_run[t], 32);
+  for (int t = 0; t < NRB; ++t) l_run[t] = sum_halves(l_run[t]);
   // Wave kh finishes d blocks kh*HB .. kh*HB+HB-1; its results end up in oacc[t][0..HB)
   // (registers are picked by value, never by a runtime index).
   constexpr int HB = KW == 2 ? DB / 2 : DB;
@@ -736,20 +747,24 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
                    p.P_log2, p.max_pages, p.num_pages, p.Hkv, p
 #define MERGE_ARGS p.part_o, p.part_ml, p.R, p.B, p.Hkv, p.nsplit, p
   constexpr int RING = Tag::kBytes == 2 ? kRingDeep : 2;
-  bool small = false;
+  bool launched = false;
   if constexpr (D == 64 && Tag::kBytes == 2) {
     // at most one row block per KV head (the semi-autoregressive block: 5 rows, G = 1):
     // one row-block wave pair of 128 threads, four workgroups per CU
-    small = p.R <= 32 && p.chunk <= kMaxSplitKeysSmall;
-    if (small)
+    launched = p.R <= 32 && p.chunk <= kMaxSplitKeysSmall;
+    if (launched)
       hipLaunchKernelGGL((attn_split_kernel<Tag, D, 1, 1, 2, 2, false>), grid, dim3(128), 0, stream, SPLIT_ARGS);
   }
-  if (!small && Tag::kBytes == 2 && p.R > 128) {
-    if (p.B == 1)
-      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 8, 1, 1, RING, true>), grid, dim3(512), 0, stream, SPLIT_ARGS);
-    else
-      hipLaunchKernelGGL((attn_split_kernel<Tag, D, 8, 1, 1, RING, false>), grid, dim3(512), 0, stream, SPLIT_ARGS);
-  } else if (!small) {
+  if constexpr (Tag::kBytes == 2) {
+    if (!launched && p.R > 128) {
+      if (p.B == 1)
+        hipLaunchKernelGGL((attn_split_kernel<Tag, D, 8, 1, 1, RING, true>), grid, dim3(512), 0, stream, SPLIT_ARGS);
+      else
+        hipLaunchKernelGGL((attn_split_kernel<Tag, D, 8, 1, 1, RING, false>), grid, dim3(512), 0, stream, SPLIT_ARGS);
+      launched = true;
+    }
+  }
+  if (!launched) {
     if (p.B == 1)
       hipLaunchKernelGGL((attn_split_kernel<Tag, D, 4, 1, 2, RING, true>), grid, dim3(512), 0, stream, SPLIT_ARGS);
     else

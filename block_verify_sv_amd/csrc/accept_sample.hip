@@ -162,11 +162,18 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
     const double* ps = part_s + static_cast<size_t>(rho) * nchunk;
     float m = -INFINITY;
     for (int q = sub; q < nchunk; q += lpr) m = fmaxf(m, pm[q]);
-    for (int o = 1; o < lpr; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    // over the lane group (lpr <= 16 lanes, aligned): uniform branches
+    if (lpr > 1) m = fmaxf(m, xlane_f32<0>(m));
+    if (lpr > 2) m = fmaxf(m, xlane_f32<1>(m));
+    if (lpr > 4) m = fmaxf(m, xlane_f32<2>(m));
+    if (lpr > 8) m = fmaxf(m, xlane_f32<3>(m));
     double s = 0.0;
     for (int q = sub; q < nchunk; q += lpr)
       s += ps[q] * exp((static_cast<double>(pm[q]) - static_cast<double>(m)) * it);
-    for (int o = 1; o < lpr; o <<= 1) s += __shfl_xor(s, o);
+    if (lpr > 1) s += xlane_f64<0>(s);
+    if (lpr > 2) s += xlane_f64<1>(s);
+    if (lpr > 4) s += xlane_f64<2>(s);
+    if (lpr > 8) s += xlane_f64<3>(s);
     if (has && sub == 0) Lrow[row] = static_cast<double>(m) * it + log(s);
   }
   __syncthreads();
@@ -295,17 +302,6 @@ size_t sample_workspace_bytes(int B, int K, int V) {
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(int32_t); // race_idx
   off += static_cast<size_t>(B) * sizeof(int32_t);          // decision
   return (off + 15) & ~static_cast<size_t>(15);
-}
-
-hipError_t launch_row_lse(const SampleParams& p, sv_dtype dtype, hipStream_t stream) {
-  const dim3 g1(p.nchunk, p.B * (2 * p.K - 1));
-  if (dtype == SV_BF16)
-    hipLaunchKernelGGL(row_lse_kernel<true>, g1, dim3(kLseThreads), 0, stream, p.target, p.draft,
-                       p.B, p.K, p.V, p.chunk, p);
-  else
-    hipLaunchKernelGGL(row_lse_kernel<false>, g1, dim3(kLseThreads), 0, stream, p.target, p.draft,
-                       p.B, p.K, p.V, p.chunk, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stream) {

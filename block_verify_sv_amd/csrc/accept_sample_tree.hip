@@ -11,20 +11,24 @@
 // decided in parallel once the normalisers are known, and the walk itself is a few
 // ballots.  On a chain this is the chain rule exactly (same uniforms, same arithmetic).
 //
-// Launches (the tree is host data, shared by the batch, so its shape fixes the plan):
-//   1. row_lse_kernel (the chain's): per-chunk (max, sum) of every target and draft row;
-//   2. tree_norm_kernel: every row's log-normaliser, one wave per row, into a table;
-//   3. for j = 1 .. (largest child count - 1): tree_residual_kernel, grid (1024-entry
+// Launches (the tree is host data, shared by the batch, so its shape fixes the plan and
+// the host hands every kernel flat tables of it):
+//   1. tree_row_norm_kernel: (max, sum) of each quarter of every target and draft row,
+//      which the later kernels fold into the row's log-normaliser;
+//   2. for j = 1 .. (largest child count - 1): tree_residual_kernel, grid (1024-entry
 //      vocabulary chunk, sequence x node with more than j children): the residual after
 //      the j-th child, max(0, rhat_{j-1} - q_j), stored per element in fp64 (one row per
 //      branching node, updated in place pass after pass) and its partial sums, which the
-//      next pass folds into Z_j; after the last pass tree_z_kernel folds the last ones;
-//   4. tree_walk_kernel, one wave per sequence: every child's threshold and ACCEPT uniform
-//      (lane = node), then the walk from the anchor;
-//   5. tree_race_kernel, grid (1024-entry chunk, sequence): the exponential race over the
+//      next pass folds into Z_j;
+//   3. tree_walk_kernel, one workgroup per sequence: its other waves gather the row
+//      normalisers, the residual normalisers (folding the ones no later pass folded) and
+//      every node's elder siblings' logits at its token while wave 0 loads its node's own;
+//      then wave 0 computes every threshold and its ACCEPT uniform (lane = node), walks
+//      from the anchor with ballots, and writes the stop node's record for the race;
+//   4. tree_race_kernel, grid (1024-entry chunk, sequence): the exponential race over the
 //      stop node's last residual (the chain's race: RESAMPLE uniforms of the stop row,
 //      with a race over p_u carried along for an all-zero residual);
-//   6. tree_finish_kernel, one workgroup per sequence: the winner and the outputs.
+//   5. tree_finish_kernel, one workgroup per sequence: the winner and the outputs.
 // Kernel boundaries order everything; the workspace carries no state between calls.
 // Every reduction runs in a fixed order, so results are bitwise reproducible.
 #include <math.h>
@@ -37,55 +41,158 @@ namespace sv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kNormSplit = 4;                    // workgroups per row of the normaliser pass
+constexpr int kNormThreads = 512;
+constexpr int kNormLoads = 10;                    // 16-byte loads in flight per thread (a
+                                                  // quarter of a bf16 row of 152k in one round)
+constexpr int kWalkThreads = 1024;                // wave 0 walks, the others fold Z
 constexpr int kZChunk = 4 * kThreads;             // vocabulary entries per residual workgroup
 constexpr int kRaceChunk = 4 * kThreads;          // vocabulary entries per race workgroup
 constexpr uint64_t kResample = 1ull << 32;        // RESAMPLE purpose in counter word 2
 
-// Row index rho of target row u / draft row of node c for the row_lse partials.
+// Row index rho of target row u / draft row of node c in the normaliser table.
 __device__ __forceinline__ int target_rho(int b, int K, int u) { return b * K + u; }
 __device__ __forceinline__ int draft_rho(int B, int b, int K, int c) {
   return B * K + b * (K - 1) + (c - 1);
 }
 
-// ---- 2. every row's log-normaliser L = m/T + log sum_c s_c e^((m_c - m)/T), one wave per
-// row (lanes stride over the chunk partials; fixed shuffle order)
-__global__ void __launch_bounds__(kThreads)
-tree_norm_kernel(int32_t rows, const TreeSampleParams p) {
-  const int lane = threadIdx.x & 63;
-  const int rho = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
-  if (rho >= rows) return;                         // whole waves
-  const float* pm = p.part_m + static_cast<size_t>(rho) * p.nchunk;
-  const double* ps = p.part_s + static_cast<size_t>(rho) * p.nchunk;
+// ---- 1. row log-normalisers L = m/T + log sum_v e^((x_v - m)/T), each row in
+// kNormSplit contiguous parts of one workgroup each.  A thread keeps a running maximum
+// (fp32, raw logits) and a sum of hardware exp2 terms relative to it (fp64; rescaled in
+// fp64 when the maximum moves) over a fixed set of elements; the threads' pairs are
+// combined in a fixed order into the part's (m, s).  The consumers fold a row's parts
+// (fold_lnorm).  -inf logits contribute nothing.
+template <bool kBF16>
+__global__ void __launch_bounds__(kNormThreads)
+tree_row_norm_kernel(const void* target, const void* draft, int32_t B, int32_t K, int32_t V,
+                     const TreeSampleParams p) {
+  __shared__ float red_m[kNormThreads / kWave];
+  __shared__ double red_s[kNormThreads / kWave];
+  const int tid = threadIdx.x;
+  const int part = blockIdx.x;
+  const int rho = blockIdx.y;
+  const int nt = B * K;
+  constexpr int ESZ = kBF16 ? 2 : 4;
+  constexpr int EPL = 16 / ESZ;                    // elements per 16-byte load
+  const char* row = rho < nt
+                        ? static_cast<const char*>(target) + static_cast<size_t>(rho) * V * ESZ
+                        : static_cast<const char*>(draft) + static_cast<size_t>(rho - nt) * V * ESZ;
+  const double it = p.inv_t;
+  const float c2 = static_cast<float>(it * 1.4426950408889634);
   float m = -INFINITY;
-  for (int q = lane; q < p.nchunk; q += kWave) m = fmaxf(m, pm[q]);
-  m = wave_max(m);
   double s = 0.0;
-  for (int q = lane; q < p.nchunk; q += kWave)
-    s += ps[q] * exp((static_cast<double>(pm[q]) - static_cast<double>(m)) * p.inv_t);
-  s = wave_sum_f64(s);
-  if (lane == 0) p.lnorm[rho] = static_cast<double>(m) * p.inv_t + log(s);
+  auto absorb = [&](const float* x, int n) {       // n values (invalid ones are -inf)
+    float lm = -INFINITY;
+    for (int e = 0; e < n; ++e) lm = fmaxf(lm, x[e]);
+    if (lm > m) {                                  // the running maximum moves
+      s = m == -INFINITY ? 0.0 : s * exp((static_cast<double>(m) - static_cast<double>(lm)) * it);
+      m = lm;
+    }
+    const float mref = m == -INFINITY ? 0.0f : m;
+    for (int e = 0; e < n; ++e) s += static_cast<double>(fast_exp2((x[e] - mref) * c2));
+  };
+  if (V % EPL == 0) {
+    // every load of a round is issued before any is consumed (clamped, in-bounds
+    // indices; those past the part's end are masked afterwards)
+    const int nvec = V / EPL;
+    const int span = (nvec + kNormSplit - 1) / kNormSplit;
+    const int v0 = part * span, v1 = min(v0 + span, nvec);
+    for (int base = v0; base < v1; base += kNormLoads * kNormThreads) {
+      u32x4 w[kNormLoads];
+#pragma unroll
+      for (int u = 0; u < kNormLoads; ++u) {
+        const int i = min(base + u * kNormThreads + tid, v1 - 1);
+        w[u] = *reinterpret_cast<const u32x4*>(row + static_cast<size_t>(i) * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < kNormLoads; ++u) {
+        const bool ok = base + u * kNormThreads + tid < v1;
+        float x[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float v;
+          if constexpr (kBF16) v = bf16_to_f32(static_cast<uint16_t>(w[u][e >> 1] >> (16 * (e & 1))));
+          else v = __uint_as_float(w[u][e]);
+          x[e] = ok ? v : -INFINITY;
+        }
+        absorb(x, EPL);
+      }
+    }
+  } else {                                         // rows not 16-byte aligned: element loads
+    const int span = (V + kNormSplit - 1) / kNormSplit;
+    const int v0 = part * span, v1 = min(v0 + span, V);
+    constexpr int kE = 4 * kNormLoads;
+    for (int base = v0; base < v1; base += kE * kNormThreads) {
+      float x[kE];
+#pragma unroll
+      for (int u = 0; u < kE; ++u) x[u] = logit_at<kBF16>(row, min(base + u * kNormThreads + tid, v1 - 1));
+#pragma unroll
+      for (int u = 0; u < kE; ++u)
+        if (base + u * kNormThreads + tid >= v1) x[u] = -INFINITY;
+      absorb(x, kE);
+    }
+  }
+  // the part's maximum, then every thread's sum scaled to it (fp64, fixed order)
+  float mb = wave_max(m);
+  if ((tid & 63) == 0) red_m[tid >> 6] = mb;
+  __syncthreads();
+  mb = red_m[0];
+#pragma unroll
+  for (int w = 1; w < kNormThreads / kWave; ++w) mb = fmaxf(mb, red_m[w]);
+  double t = m == -INFINITY ? 0.0 : s * exp((static_cast<double>(m) - static_cast<double>(mb)) * it);
+  t = wave_sum_f64(t);
+  if ((tid & 63) == 0) red_s[tid >> 6] = t;
+  __syncthreads();
+  if (tid == 0) {
+    double S = 0.0;
+#pragma unroll
+    for (int w = 0; w < kNormThreads / kWave; ++w) S += red_s[w];
+    p.part_m[static_cast<size_t>(rho) * kNormSplit + part] = mb;
+    p.part_s[static_cast<size_t>(rho) * kNormSplit + part] = S;
+  }
 }
 
-// ---- 3a. residual pass j at every node with more than j children: the residual after
+// A row's log-normaliser from its kNormSplit parts (fixed order, fp64).
+__device__ __forceinline__ double fold_lnorm(const TreeSampleParams& p, int rho) {
+  const float* pm = p.part_m + static_cast<size_t>(rho) * kNormSplit;
+  const double* ps = p.part_s + static_cast<size_t>(rho) * kNormSplit;
+  float m = pm[0];
+#pragma unroll
+  for (int k = 1; k < kNormSplit; ++k) m = fmaxf(m, pm[k]);
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < kNormSplit; ++k)
+    if (pm[k] != -INFINITY) s += ps[k] * exp((static_cast<double>(pm[k]) - static_cast<double>(m)) * p.inv_t);
+  return static_cast<double>(m) * p.inv_t + log(s);
+}
+
+// Pass-node word: the node u of a residual pass, the child c it subtracts, the child cp
+// subtracted by the previous pass (0xFF on the first) and u's residual row.
+__device__ __forceinline__ int pn_u(int32_t w) { return w & 0xFF; }
+__device__ __forceinline__ int pn_c(int32_t w) { return (w >> 8) & 0xFF; }
+__device__ __forceinline__ int pn_cp(int32_t w) { return (w >> 16) & 0xFF; }
+__device__ __forceinline__ int pn_slot(int32_t w) { return (w >> 24) & 0xFF; }
+
+// ---- 2. residual pass j at every node with more than j children: the residual after
 // rejecting the j-th child, raw_j = max(0, rhat_{j-1} - q_j), stored per element (fp64) for
 // the next pass, and its partial sums.  rhat_0 = p_u; rhat_{j-1} = raw_{j-1} / Z_{j-1}
 // (p_u if Z_{j-1} = 0), with Z_{j-1} folded here from the previous pass's partial sums.
+// The pass's nodes are words off .. off+n_nodes-1 of the pass table: one scalar load
+// gives everything the element loads need.
 template <bool kBF16>
 __global__ void __launch_bounds__(kThreads)
-tree_residual_kernel(int32_t j, int32_t n_nodes, const TreeSampleParams p) {
+tree_residual_kernel(int32_t j, int32_t off, int32_t n_nodes, const TreeSampleParams p) {
   __shared__ double zprev_sh;
+  __shared__ double lsh_pq[2];
   __shared__ double red[kThreads / kWave];
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
   const int b = blockIdx.y / n_nodes;
-  const int u = p.by_count[blockIdx.y - b * n_nodes];
+  const int32_t w = p.pass_node[off + blockIdx.y - b * n_nodes];
+  const int u = pn_u(w), c = pn_c(w), cp = pn_cp(w);
   const int K = p.K, V = p.V;
   const double it = p.inv_t;
-  const int first = p.child_start[u];
-  const int c = p.child_list[first + j - 1];       // the child this pass subtracts
-  const double Lp = p.lnorm[target_rho(b, K, u)];
-  const double Lq = p.lnorm[draft_rho(p.B, b, K, c)];
-  double* buf = p.resid + (static_cast<size_t>(b) * p.nbranch + p.branch_slot[u]) * V;
+  double* buf = p.resid + (static_cast<size_t>(b) * p.nbranch + pn_slot(w)) * V;
   const size_t trow = (static_cast<size_t>(b) * K + u) * V;
   const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (c - 1)) * V;
   // this thread's elements are loaded before the fold of Z_{j-1}, so the two round trips
@@ -100,18 +207,29 @@ tree_residual_kernel(int32_t j, int32_t n_nodes, const TreeSampleParams p) {
     if (j == 1) xp[e] = logit_at<kBF16>(p.target, trow + v);
     else rb[e] = buf[v];
   }
+  // row normalisers: the first pass folds its two rows from the parts (two lanes, shared
+  // through LDS) and its first workgroup writes every row's into the table the later
+  // kernels read
+  if (j == 1) {
+    if (tid < 2) lsh_pq[tid] = fold_lnorm(p, tid == 0 ? target_rho(b, K, u) : draft_rho(p.B, b, K, c));
+    if (chunk == 0 && blockIdx.y == 0) {
+      const int rows = p.B * (2 * K - 1);
+      for (int r = tid; r < rows; r += kThreads) p.lnorm[r] = fold_lnorm(p, r);
+    }
+  }
   if (j > 1 && tid < kWave) {                      // Z_{j-1}, from the previous pass
-    const int cp = p.child_list[first + j - 2];
     const double* z = p.zpart + (static_cast<size_t>(b) * K + cp) * p.nz;
-    double s = 0.0;
-    for (int q = tid; q < p.nz; q += kWave) s += z[q];
-    s = wave_sum_f64(s);
+    double sz = 0.0;
+    for (int q = tid; q < p.nz; q += kWave) sz += z[q];
+    sz = wave_sum_f64(sz);
     if (tid == 0) {
-      zprev_sh = s;
-      if (chunk == 0) p.ztab[static_cast<size_t>(b) * K + cp] = s;
+      zprev_sh = sz;
+      if (chunk == 0) p.ztab[static_cast<size_t>(b) * K + cp] = sz;
     }
   }
   __syncthreads();
+  const double Lp = j == 1 ? lsh_pq[0] : p.lnorm[target_rho(b, K, u)];
+  const double Lq = j == 1 ? lsh_pq[1] : p.lnorm[draft_rho(p.B, b, K, c)];
   const double zp = j > 1 ? zprev_sh : 1.0;
   if (j > 1 && !(zp > 0.0)) {                      // Z_{j-1} = 0: the residual restarts at p_u
 #pragma unroll
@@ -137,75 +255,116 @@ tree_residual_kernel(int32_t j, int32_t n_nodes, const TreeSampleParams p) {
   if (tid == 0) {
     double t = 0.0;
 #pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
+    for (int q = 0; q < kThreads / kWave; ++q) t += red[q];
     p.zpart[(static_cast<size_t>(b) * K + c) * p.nz + chunk] = t;
   }
 }
 
-// ---- 3b. after the last pass: Z of the last subtracted child of every branching node
-// (the earlier ones were folded by the passes), one wave per (sequence, node)
-__global__ void __launch_bounds__(kWave)
-tree_z_kernel(int32_t n_nodes, const TreeSampleParams p) {
-  const int lane = threadIdx.x;
-  const int b = blockIdx.x / n_nodes;
-  const int u = p.by_count[blockIdx.x - b * n_nodes];
-  const int c = p.child_list[p.child_start[u] + p.child_count[u] - 2];
-  const double* z = p.zpart + (static_cast<size_t>(b) * p.K + c) * p.nz;
-  double s = 0.0;
-  for (int q = lane; q < p.nz; q += kWave) s += z[q];
-  s = wave_sum_f64(s);
-  if (lane == 0) p.ztab[static_cast<size_t>(b) * p.K + c] = s;
-}
-
-// ---- 4. the tests and the walk, one wave per sequence
+// ---- 3. the tests and the walk, one workgroup per sequence.  The other waves first
+// gather everything the tests need, all loads in flight together: the row normalisers
+// (folded from the parts), the Z of every elder sibling (from the passes' table, or
+// folded here for each branching node's second-to-last child, which no later pass
+// folded) and each node's elder siblings' draft logits at its token.  Wave 0 meanwhile
+// loads its own node's two logits; then it decides every test (lane = node) and walks.
 template <bool kBF16>
-__global__ void __launch_bounds__(kWave)
+__global__ void __launch_bounds__(kWalkThreads)
 tree_walk_kernel(const TreeSampleParams p) {
+  __shared__ double lsh[2 * kMaxBlock];            // L: target row u at u, draft row of c at K-1+c
+  __shared__ double zc[kMaxBlock];                 // Z after child c, from the passes' table
+  __shared__ double zlast[kMaxBlock];              // Z after child c, folded here
+  __shared__ double qv[kMaxBlock][kMaxBlock];      // [c][l]: q_l(x_c), elder sibling l's probability of c's token
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int lane = tid & 63;
   const int b = blockIdx.x;
   const int K = p.K, V = p.V;
+  const int32_t* tok_b = p.tokens + static_cast<size_t>(b) * (K - 1);
+  if (wave > 0) {                                  // each wave meets exactly one barrier
+    if (wave < 8) {
+      // elder siblings' probabilities of each node's token: wave w takes nodes c = w,
+      // w + 7, ...; lane l computes q_l(x_c) when node l is an elder sibling of c (all loads
+      // first; elder siblings exist only when a residual pass ran, so lnorm is written)
+      constexpr int kSlots = (kMaxBlock + 6) / 7;
+      float v[kSlots];
+      double Ll = 0.0;
+      if (p.has_lnorm && lane >= 1 && lane < K) Ll = p.lnorm[draft_rho(p.B, b, K, lane)];
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl) {
+        const int c = min(wave + 7 * sl, K - 1);
+        const bool mine = wave + 7 * sl < K && ((p.elder[c] >> lane) & 1u);
+        const int32_t x = tok_b[c - 1];
+        const int xs = (x >= 0 && x < V) ? x : 0;
+        v[sl] = mine ? logit_at<kBF16>(p.draft, (static_cast<size_t>(b) * (K - 1) + (lane - 1)) * V + xs)
+                     : 0.0f;
+      }
+      const double it = p.inv_t;
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl) {
+        const int c = wave + 7 * sl;
+        if (c < K && ((p.elder[c] >> lane) & 1u)) qv[c][lane] = exp(static_cast<double>(v[sl]) * it - Ll);
+      }
+    } else if (wave < 10) {
+      // row normalisers and the passes' Z table, one thread per entry
+      const int r = tid - 8 * kWave;               // 0 .. 127
+      if (r < 2 * K - 1) {
+        const int rho = r < K ? target_rho(b, K, r) : draft_rho(p.B, b, K, r - K + 1);
+        lsh[r] = p.has_lnorm ? p.lnorm[rho] : fold_lnorm(p, rho);   // written by the first pass
+      }
+      if (r < K) zc[r] = p.ztab[static_cast<size_t>(b) * K + r];
+    } else {
+      // Z after each branching node's second-to-last child: wave w folds entries
+      // w - 10, w - 4, ... of last_z
+      for (int k = wave - 10; k < p.n_last; k += kWalkThreads / kWave - 10) {
+        const int cz = p.last_z[k];
+        const double* z = p.zpart + (static_cast<size_t>(b) * K + cz) * p.nz;
+        double sz = 0.0;
+        for (int q = lane; q < p.nz; q += kWave) sz += z[q];
+        sz = wave_sum_f64(sz);
+        if (lane == 0) zlast[cz] = sz;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   const double it = p.inv_t;
-  const double* L = p.lnorm;
-  const int lane = tid;
   const int c = lane + 1;                          // the draft node this lane tests
   const bool node = c < K;
+  const int u = node ? p.parent[c] : 0;
+  const bool first_child = node && p.elder[c] == 0;   // tested against p_u itself
+  const int32_t x = node ? tok_b[c - 1] : -1;
+  const bool in_v = x >= 0 && x < V;
+  const int xs = in_v ? x : 0;
+  const double lp = logit_at<kBF16>(p.target, (static_cast<size_t>(b) * K + u) * V + xs);
+  const double lq = logit_at<kBF16>(p.draft, (static_cast<size_t>(b) * (K - 1) + (node ? c - 1 : 0)) * V + xs);
+  __syncthreads();                                 // the gathered values are in LDS
+  const double Lu = lsh[u];
+  const double Lc = lsh[K - 1 + (node ? c : 1)];
   bool pass = false;
-  if (node) {
-    const int u = p.parent[c];
-    const int jj = p.sib[c];                      // elder siblings rejected before this test
-    const int32_t x = p.tokens[static_cast<size_t>(b) * (K - 1) + (c - 1)];
-    if (x >= 0 && x < V) {
-      const double lp = logit_at<kBF16>(p.target, (static_cast<size_t>(b) * K + u) * V + x);
-      const double lq = logit_at<kBF16>(p.draft, (static_cast<size_t>(b) * (K - 1) + (c - 1)) * V + x);
-      double thr = 0.0;
-      if (lp != -INFINITY) {
-        if (jj == 0) {                             // against p_u: the chain's log form
-          thr = exp(fmin(0.0, (lp - lq) * it - (L[target_rho(b, K, u)] -
-                                                 L[draft_rho(p.B, b, K, c)])));
-        } else {
-          const double pv = exp(lp * it - L[target_rho(b, K, u)]);
-          double r = pv;
-#pragma unroll 4
-          for (int i = 0; i < jj; ++i) {
-            const int ci = p.child_list[p.child_start[u] + i];
-            const double lqi = logit_at<kBF16>(p.draft, (static_cast<size_t>(b) * (K - 1) + (ci - 1)) * V + x);
-            const double qi = exp(lqi * it - L[draft_rho(p.B, b, K, ci)]);
-            const double raw = fmax(0.0, r - qi);
-            const double z = p.ztab[static_cast<size_t>(b) * K + ci];
-            r = z > 0.0 ? raw / z : pv;
-          }
-          const double qc = exp(lq * it - L[draft_rho(p.B, b, K, c)]);
-          thr = r == 0.0 ? 0.0 : (qc == 0.0 ? 1.0 : fmin(1.0, r / qc));
-        }
+  if (node && in_v && lp != -INFINITY) {
+    double thr;
+    if (first_child) {                             // against p_u: the chain's log form
+      thr = exp(fmin(0.0, (lp - lq) * it - (Lu - Lc)));
+    } else {
+      const double pv = exp(lp * it - Lu);
+      double r = pv;
+      // the elder siblings in increasing node order (the order they are tested in)
+      for (uint64_t e = p.elder[c]; e; e &= e - 1) {
+        const int ci = __builtin_ctzll(e);
+        const double raw = fmax(0.0, r - qv[c][ci]);
+        // Z after child ci: from the pass after it, or (a second-to-last child) folded here
+        const double z = ((p.zl_mask >> ci) & 1u) ? zlast[ci] : zc[ci];
+        r = z > 0.0 ? raw / z : pv;
       }
-      const U64x4 w = philox(p.offset, static_cast<uint64_t>(b), static_cast<uint64_t>(c), 0,
-                             p.seed, 0);
-      pass = to_uniform(w.x[0]) < thr;
+      const double qc = exp(lq * it - Lc);
+      thr = r == 0.0 ? 0.0 : (qc == 0.0 ? 1.0 : fmin(1.0, r / qc));
     }
+    const U64x4 wv = philox(p.offset, static_cast<uint64_t>(b), static_cast<uint64_t>(c), 0,
+                            p.seed, 0);
+    pass = to_uniform(wv.x[0]) < thr;
   }
   // the walk: at the current node the lowest-numbered passing child (children are
   // tested in increasing node order); node numbers only grow, so it ends within K-1 steps
-  const int par = node ? p.parent[c] : -1;
+  const int par = node ? u : -1;
   int cur = 0, a = 0;
   int32_t my_path = lane == 0 ? 0 : -1;            // lane j ends up holding path[j]
   for (int step = 1; step < K; ++step) {
@@ -215,7 +374,7 @@ tree_walk_kernel(const TreeSampleParams p) {
     a = step;
     if (lane == step) my_path = cur;
   }
-  const int32_t tok = node ? p.tokens[static_cast<size_t>(b) * (K - 1) + (c - 1)] : 0;
+  const int32_t tok = node ? x : 0;
   const int32_t next_node = __shfl(my_path, lane < 63 ? lane + 1 : 63);   // path[j+1]
   const int32_t next_tok = __shfl(tok, next_node > 0 ? next_node - 1 : 0);
   if (lane < K) {
@@ -224,13 +383,23 @@ tree_walk_kernel(const TreeSampleParams p) {
     p.path[o] = my_path;
   }
   if (lane == 0) {
+    // the race draws from max(0, rhat_{m-1} - q_c) at the stop node (every child c_1 ..
+    // c_m rejected; c = c_m), or from p_u at a leaf
+    const int m = p.child_count[cur];
+    TreeStop st;
+    st.u = cur;
+    st.m = m;
+    st.c = m > 0 ? p.child_list[p.child_start[cur] + m - 1] : 1;
+    st.slot = p.branch_slot[cur];
+    st.zp = m > 1 ? zlast[p.child_list[p.child_start[cur] + m - 2]] : 1.0;
+    st.lp = lsh[cur];
+    st.lq = m > 0 ? lsh[K - 1 + st.c] : 0.0;
+    p.stop[b] = st;
     p.accept_len[b] = a;
-    p.stop[2 * b] = cur;
-    p.stop[2 * b + 1] = p.child_count[cur];
   }
 }
 
-// ---- 5. the race over the stop node's last residual
+// ---- 4. the race over the stop node's last residual
 template <bool kBF16>
 __global__ void __launch_bounds__(kThreads)
 tree_race_kernel(const TreeSampleParams p) {
@@ -241,15 +410,11 @@ tree_race_kernel(const TreeSampleParams p) {
   const int b = blockIdx.y;
   const int K = p.K, V = p.V;
   const double it = p.inv_t;
-  const int u = p.stop[2 * b];
-  const int m = p.stop[2 * b + 1];                 // children rejected at u
-  const double Lp = p.lnorm[target_rho(b, K, u)];
-  const int c = m > 0 ? p.child_list[p.child_start[u] + m - 1] : 1;   // the last one
-  const double Lq = m > 0 ? p.lnorm[draft_rho(p.B, b, K, c)] : 0.0;
-  const double zp = m > 1 ? p.ztab[static_cast<size_t>(b) * K + p.child_list[p.child_start[u] + m - 2]]
-                          : 1.0;
+  const TreeStop st = p.stop[b];
+  const int u = st.u, m = st.m, c = st.c;
+  const double zp = st.zp;
   const bool from_buf = m > 1 && zp > 0.0;         // rhat_{m-1} from the stored residual
-  const double* buf = p.resid + (static_cast<size_t>(b) * p.nbranch + p.branch_slot[u]) * V;
+  const double* buf = p.resid + (static_cast<size_t>(b) * p.nbranch + st.slot) * V;
   const size_t trow = (static_cast<size_t>(b) * K + u) * V;
   const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (c - 1)) * V;
   const int jb = chunk * p.race_chunk + 4 * tid;
@@ -262,11 +427,11 @@ tree_race_kernel(const TreeSampleParams p) {
     for (int e = 0; e < 4; ++e) {
       const int v = jb + e;
       if (v >= V) break;
-      const double pv = exp(static_cast<double>(logit_at<kBF16>(p.target, trow + v)) * it - Lp);
+      const double pv = exp(static_cast<double>(logit_at<kBF16>(p.target, trow + v)) * it - st.lp);
       double r = pv;
       if (m > 0) {
         const double rh = from_buf ? buf[v] / zp : pv;
-        const double qv = exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow + v)) * it - Lq);
+        const double qv = exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow + v)) * it - st.lq);
         r = fmax(0.0, rh - qv);
       }
       const double ej = -log1p(-to_uniform(w.x[e]));
@@ -290,7 +455,7 @@ tree_race_kernel(const TreeSampleParams p) {
   }
 }
 
-// ---- 6. the winner over every chunk, then the drawn token at slot accept_len
+// ---- 5. the winner over every chunk, then the drawn token at slot accept_len
 __global__ void __launch_bounds__(kThreads)
 tree_finish_kernel(const TreeSampleParams p) {
   __shared__ double rk[2][kThreads / kWave];
@@ -315,38 +480,67 @@ tree_finish_kernel(const TreeSampleParams p) {
 
 }  // namespace
 
+// Workspace, in order: zpart [B][K][nz], resid [B][K/2][V] (fp64), race_key
+// [B][race_nchunk][2], part_s [B(2K-1)][kNormSplit], lnorm [B(2K-1)], ztab [B][K], stop [B] records,
+// race_idx [B][race_nchunk][2], part_m [B(2K-1)][kNormSplit] (fp32).
 size_t sample_tree_workspace_bytes(int B, int K, int V) {
   const size_t rows = static_cast<size_t>(B) * (2 * K - 1);
-  const size_t nchunk = (static_cast<size_t>(V) + sample_chunk(V) - 1) / sample_chunk(V);
   const size_t nz = (static_cast<size_t>(V) + kZChunk - 1) / kZChunk;
   const size_t nrace = (static_cast<size_t>(V) + kRaceChunk - 1) / kRaceChunk;
   size_t off = 0;
-  off += rows * nchunk * sizeof(double);                        // part_s
   off += static_cast<size_t>(B) * K * nz * sizeof(double);      // zpart
   off += static_cast<size_t>(B) * (K / 2) * V * sizeof(double); // resid: at most K/2 branching nodes
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(double);   // race_key
-  off += rows * nchunk * sizeof(float);                         // part_m
-  off = (off + 7) & ~static_cast<size_t>(7);
+  off += rows * kNormSplit * sizeof(double);                    // part_s
   off += rows * sizeof(double);                                 // lnorm
   off += static_cast<size_t>(B) * K * sizeof(double);           // ztab
+  off += static_cast<size_t>(B) * sizeof(TreeStop);             // stop
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(int32_t);  // race_idx
-  off += static_cast<size_t>(B) * 2 * sizeof(int32_t);          // stop
+  off += rows * kNormSplit * sizeof(float);                     // part_m
   return (off + 15) & ~static_cast<size_t>(15);
 }
 
-int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host) {
+void carve_sample_tree_workspace(TreeSampleParams& p, void* workspace) {
+  const size_t rows = static_cast<size_t>(p.B) * (2 * p.K - 1);
+  char* w = static_cast<char*>(workspace);
+  p.zpart = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(p.B) * p.K * p.nz * sizeof(double);
+  p.resid = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(p.B) * (p.K / 2) * p.V * sizeof(double);
+  p.race_key = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(p.B) * p.race_nchunk * 2 * sizeof(double);
+  p.part_s = reinterpret_cast<double*>(w);
+  w += rows * kNormSplit * sizeof(double);
+  p.lnorm = reinterpret_cast<double*>(w);
+  w += rows * sizeof(double);
+  p.ztab = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(p.B) * p.K * sizeof(double);
+  p.stop = reinterpret_cast<TreeStop*>(w);
+  w += static_cast<size_t>(p.B) * sizeof(TreeStop);
+  p.race_idx = reinterpret_cast<int32_t*>(w);
+  w += static_cast<size_t>(p.B) * p.race_nchunk * 2 * sizeof(int32_t);
+  p.part_m = reinterpret_cast<float*>(w);
+}
+
+int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host, TreePassPlan& plan) {
   const int K = p.K;
-  p.zchunk = kZChunk;
   p.nz = (p.V + kZChunk - 1) / kZChunk;
   p.race_chunk = kRaceChunk;
   p.race_nchunk = (p.V + kRaceChunk - 1) / kRaceChunk;
-  p.parent[0] = -1;
-  p.sib[0] = 0;
+  for (int i = 0; i < kMaxBlock; ++i) {
+    p.parent[i] = -1;
+    p.child_start[i] = 0;
+    p.child_count[i] = 0;
+    p.child_list[i] = 0;
+    p.branch_slot[i] = 0;
+    p.pass_node[i] = 0;
+    p.last_z[i] = 0;
+    p.elder[i] = 0;
+  }
   int count[kMaxBlock] = {0};
   for (int i = 1; i < K; ++i) {
     const int par = parents_host[i - 1];
     p.parent[i] = static_cast<int8_t>(par);
-    p.sib[i] = static_cast<int8_t>(count[par]);
     ++count[par];
   }
   int pos = 0;
@@ -356,64 +550,68 @@ int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host) {
     for (int i = u + 1; i < K; ++i)
       if (parents_host[i - 1] == u) p.child_list[pos++] = static_cast<int8_t>(i);
   }
-  for (int i = K; i < kMaxBlock; ++i) {
-    p.parent[i] = -1;
-    p.sib[i] = 0;
-    p.child_start[i] = 0;
-    p.child_count[i] = 0;
+  for (int c = 1; c < K; ++c) {                    // elder siblings: same parent, lower number
+    uint64_t e = 0;
+    for (int i = 1; i < c; ++i)
+      if (parents_host[i - 1] == parents_host[c - 1]) e |= 1ull << i;
+    p.elder[c] = e;
   }
-  int nbr = 0;
-  for (int u = 0; u < kMaxBlock; ++u) p.branch_slot[u] = 0;
-  for (int u = 0; u < K; ++u)
-    if (count[u] > 1) p.branch_slot[u] = static_cast<int8_t>(nbr++);
+  int nbr = 0, mmax = 0;
+  p.n_last = 0;
+  p.zl_mask = 0;
+  for (int u = 0; u < K; ++u) {
+    mmax = count[u] > mmax ? count[u] : mmax;
+    if (count[u] > 1) {
+      p.branch_slot[u] = static_cast<int8_t>(nbr++);
+      p.last_z[p.n_last++] = p.child_list[p.child_start[u] + count[u] - 2];
+      p.zl_mask |= 1ull << p.child_list[p.child_start[u] + count[u] - 2];
+    }
+  }
   p.nbranch = nbr > 0 ? nbr : 1;
-  int nb = 0, mmax = 0;
-  for (int cnt = K - 1; cnt >= 1; --cnt)        // nodes by decreasing child count
-    for (int u = 0; u < K; ++u)
-      if (count[u] == cnt) p.by_count[nb++] = static_cast<int8_t>(u);
-  for (int u = 0; u < K; ++u) mmax = count[u] > mmax ? count[u] : mmax;
-  return mmax > 1 ? mmax - 1 : 0;
+  // pass j (1 .. mmax-1) covers the nodes with more than j children, by decreasing child
+  // count (ties: node order); each gets a word (u, c_j, c_{j-1}, residual row)
+  const int rounds = mmax > 1 ? mmax - 1 : 0;
+  p.has_lnorm = rounds > 0 ? 1 : 0;               // the first pass writes the table
+  int words = 0;
+  for (int j = 1; j <= rounds; ++j) {
+    plan.off[j] = words;
+    for (int cnt = K - 1; cnt > j; --cnt)
+      for (int u = 0; u < K; ++u) {
+        if (count[u] != cnt) continue;
+        const int c = p.child_list[p.child_start[u] + j - 1];
+        const int cp = j > 1 ? p.child_list[p.child_start[u] + j - 2] : 0xFF;
+        p.pass_node[words++] = u | (c << 8) | (cp << 16) | (p.branch_slot[u] << 24);
+      }
+    plan.n[j] = words - plan.off[j];
+  }
+  return rounds;
 }
 
-hipError_t launch_sample_tree(const TreeSampleParams& p, int rounds, sv_dtype dtype,
-                              hipStream_t stream) {
-  SampleParams lse{};
-  lse.target = p.target;
-  lse.draft = p.draft;
-  lse.B = p.B;
-  lse.K = p.K;
-  lse.V = p.V;
-  lse.chunk = sample_chunk(p.V);
-  lse.nchunk = p.nchunk;
-  lse.part_m = const_cast<float*>(p.part_m);
-  lse.part_s = const_cast<double*>(p.part_s);
-  lse.inv_t = p.inv_t;
-  hipError_t e = launch_row_lse(lse, dtype, stream);
-  if (e != hipSuccess) return e;
-  const int rows = p.B * (2 * p.K - 1);
-  hipLaunchKernelGGL(tree_norm_kernel, dim3((rows + kThreads / kWave - 1) / (kThreads / kWave)),
-                     dim3(kThreads), 0, stream, rows, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_sample_tree(const TreeSampleParams& p, const TreePassPlan& plan, int rounds,
+                              sv_dtype dtype, hipStream_t stream) {
   const bool bf = dtype == SV_BF16;
+  const int rows = p.B * (2 * p.K - 1);
+  if (bf)
+    hipLaunchKernelGGL(tree_row_norm_kernel<true>, dim3(kNormSplit, rows), dim3(kNormThreads), 0,
+                       stream, p.target, p.draft, p.B, p.K, p.V, p);
+  else
+    hipLaunchKernelGGL(tree_row_norm_kernel<false>, dim3(kNormSplit, rows), dim3(kNormThreads), 0,
+                       stream, p.target, p.draft, p.B, p.K, p.V, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   for (int j = 1; j <= rounds; ++j) {
-    int n = 0;                                    // nodes with more than j children
-    for (int u = 0; u < p.K; ++u) n += p.child_count[u] > j ? 1 : 0;
-    const dim3 g(p.nz, p.B * n);
-    if (bf) hipLaunchKernelGGL(tree_residual_kernel<true>, g, dim3(kThreads), 0, stream, j, n, p);
-    else hipLaunchKernelGGL(tree_residual_kernel<false>, g, dim3(kThreads), 0, stream, j, n, p);
+    const dim3 g(p.nz, p.B * plan.n[j]);
+    if (bf)
+      hipLaunchKernelGGL(tree_residual_kernel<true>, g, dim3(kThreads), 0, stream, j, plan.off[j],
+                         plan.n[j], p);
+    else
+      hipLaunchKernelGGL(tree_residual_kernel<false>, g, dim3(kThreads), 0, stream, j, plan.off[j],
+                         plan.n[j], p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (rounds > 0) {
-    int n = 0;                                    // branching nodes
-    for (int u = 0; u < p.K; ++u) n += p.child_count[u] > 1 ? 1 : 0;
-    hipLaunchKernelGGL(tree_z_kernel, dim3(p.B * n), dim3(kWave), 0, stream, n, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (bf) hipLaunchKernelGGL(tree_walk_kernel<true>, dim3(p.B), dim3(kWave), 0, stream, p);
-  else hipLaunchKernelGGL(tree_walk_kernel<false>, dim3(p.B), dim3(kWave), 0, stream, p);
+  if (bf) hipLaunchKernelGGL(tree_walk_kernel<true>, dim3(p.B), dim3(kWalkThreads), 0, stream, p);
+  else hipLaunchKernelGGL(tree_walk_kernel<false>, dim3(p.B), dim3(kWalkThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gr(p.race_nchunk, p.B);

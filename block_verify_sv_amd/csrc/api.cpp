@@ -477,36 +477,15 @@ sv_status sv_accept_sample_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_
   p.B = B;
   p.K = K;
   p.V = V;
-  p.nchunk = (V + sv::sample_chunk(V) - 1) / sv::sample_chunk(V);
   p.inv_t = 1.0 / static_cast<double>(temperature);
   p.seed = seed;
   p.offset = offset;
-  const int rounds = sv::plan_sample_tree(p, parents);
-  int widest = 0;
-  for (int u = 0; u < K; ++u) widest = p.child_count[u] > 1 ? widest + 1 : widest;
-  if (static_cast<int64_t>(B) * (widest > 0 ? widest : 1) > 65535)
+  sv::TreePassPlan plan;
+  const int rounds = sv::plan_sample_tree(p, parents, plan);
+  if (static_cast<int64_t>(B) * p.nbranch > 65535)
     return fail(SV_ERR_INVALID_ARG, "B times the number of branching nodes must be <= 65535");
-  const size_t rows = static_cast<size_t>(B) * (2 * K - 1);
-  char* w = static_cast<char*>(workspace);
-  p.part_s = reinterpret_cast<double*>(w);
-  w += rows * p.nchunk * sizeof(double);
-  p.zpart = reinterpret_cast<double*>(w);
-  w += static_cast<size_t>(B) * K * p.nz * sizeof(double);
-  p.resid = reinterpret_cast<double*>(w);
-  w += static_cast<size_t>(B) * (K / 2) * V * sizeof(double);
-  p.race_key = reinterpret_cast<double*>(w);
-  w += static_cast<size_t>(B) * p.race_nchunk * 2 * sizeof(double);
-  p.part_m = reinterpret_cast<float*>(w);
-  w += rows * p.nchunk * sizeof(float);
-  w = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(w) + 7) & ~static_cast<uintptr_t>(7));
-  p.lnorm = reinterpret_cast<double*>(w);
-  w += rows * sizeof(double);
-  p.ztab = reinterpret_cast<double*>(w);
-  w += static_cast<size_t>(B) * K * sizeof(double);
-  p.race_idx = reinterpret_cast<int32_t*>(w);
-  w += static_cast<size_t>(B) * p.race_nchunk * 2 * sizeof(int32_t);
-  p.stop = reinterpret_cast<int32_t*>(w);
-  return device_status(sv::launch_sample_tree(p, rounds, logit_dtype,
+  sv::carve_sample_tree_workspace(p, workspace);
+  return device_status(sv::launch_sample_tree(p, plan, rounds, logit_dtype,
                                               static_cast<hipStream_t>(stream)),
                        "sv_accept_sample_tree launch");
 }

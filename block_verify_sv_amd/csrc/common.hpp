@@ -112,27 +112,87 @@ struct Mfma<TagF32> {
 };
 
 // ------------------------------------------------------------------ wave reductions
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o);
-    v = w > v ? w : v;
+// Cross-lane exchange without an LDS round trip.  Stage S (0..5) pairs every lane with a
+// lane in the other half of its aligned group of 2^(S+1) lanes: lane ^ 1 and lane ^ 2 (DPP
+// quad permutes), the mirror lane within 8 and within 16 (DPP row half-mirror and row
+// mirror), then lane ^ 16 and lane ^ 32 (the gfx950 row and half swaps).  After stages
+// 0 .. S-1 of a reduction every lane of an aligned group of 2^S lanes holds the same
+// value, so each stage combines two complete halves; the combining operations used here
+// are commutative, so every lane of the group ends with bitwise the same result.
+template <int S>
+__device__ __forceinline__ uint32_t xlane(uint32_t v) {
+  static_assert(S >= 0 && S < 6, "stage");
+  if constexpr (S == 0) return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+  else if constexpr (S == 1) return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+  else if constexpr (S == 2) return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false));
+  else if constexpr (S == 3) return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false));
+  else if constexpr (S == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
   }
+}
+template <int S>
+__device__ __forceinline__ uint64_t xlane64(uint64_t v) {
+  const uint32_t lo = xlane<S>(static_cast<uint32_t>(v));
+  const uint32_t hi = xlane<S>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+template <int S>
+__device__ __forceinline__ float xlane_f32(float v) { return __uint_as_float(xlane<S>(__float_as_uint(v))); }
+template <int S>
+__device__ __forceinline__ double xlane_f64(double v) {
+  return __builtin_bit_cast(double, xlane64<S>(__builtin_bit_cast(uint64_t, v)));
+}
+
+// Reductions over aligned groups of 2^N lanes (N = 6: the whole wave).
+template <int N = 6>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (N > 0) v = fmaxf(v, xlane_f32<0>(v));
+  if constexpr (N > 1) v = fmaxf(v, xlane_f32<1>(v));
+  if constexpr (N > 2) v = fmaxf(v, xlane_f32<2>(v));
+  if constexpr (N > 3) v = fmaxf(v, xlane_f32<3>(v));
+  if constexpr (N > 4) v = fmaxf(v, xlane_f32<4>(v));
+  if constexpr (N > 5) v = fmaxf(v, xlane_f32<5>(v));
   return v;
 }
+template <int N = 6>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N > 0) v += xlane_f32<0>(v);
+  if constexpr (N > 1) v += xlane_f32<1>(v);
+  if constexpr (N > 2) v += xlane_f32<2>(v);
+  if constexpr (N > 3) v += xlane_f32<3>(v);
+  if constexpr (N > 4) v += xlane_f32<4>(v);
+  if constexpr (N > 5) v += xlane_f32<5>(v);
+  return v;
+}
+template <int N = 6>
+__device__ __forceinline__ double group_sum_f64(double v) {
+  if constexpr (N > 0) v += xlane_f64<0>(v);
+  if constexpr (N > 1) v += xlane_f64<1>(v);
+  if constexpr (N > 2) v += xlane_f64<2>(v);
+  if constexpr (N > 3) v += xlane_f64<3>(v);
+  if constexpr (N > 4) v += xlane_f64<4>(v);
+  if constexpr (N > 5) v += xlane_f64<5>(v);
+  return v;
+}
+template <int N = 6>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+  uint64_t w;
+  if constexpr (N > 0) { w = xlane64<0>(v); v = w > v ? w : v; }
+  if constexpr (N > 1) { w = xlane64<1>(v); v = w > v ? w : v; }
+  if constexpr (N > 2) { w = xlane64<2>(v); v = w > v ? w : v; }
+  if constexpr (N > 3) { w = xlane64<3>(v); v = w > v ? w : v; }
+  if constexpr (N > 4) { w = xlane64<4>(v); v = w > v ? w : v; }
+  if constexpr (N > 5) { w = xlane64<5>(v); v = w > v ? w : v; }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) { return group_max<6>(v); }
+__device__ __forceinline__ double wave_sum_f64(double v) { return group_sum_f64<6>(v); }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) { return group_max_u64<6>(v); }
 
 // Order-preserving map of a finite float to uint32 (-0.0 is folded onto +0.0, so equal
 // values give equal keys).

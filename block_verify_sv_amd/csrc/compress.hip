@@ -161,8 +161,7 @@ softmax_kernel(const float* scores, uint16_t* weights, float* rowsum, int32_t B,
     }
     wr[n] = wv;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  sum = group_sum<6>(sum);
   if (lane == 0) rowsum[b * kMaxC + c] = sum;
 }
 

@@ -80,11 +80,16 @@ size_t sample_workspace_bytes(int B, int K, int V);
 int sample_chunk(int V);
 int sample_race_chunk(int V);
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stream);
-// The per-chunk (max, sum) pass over every target and draft row alone (p.target, p.draft,
-// p.B, p.K, p.V, p.chunk, p.nchunk, p.part_m, p.part_s, p.inv_t).
-hipError_t launch_row_lse(const SampleParams& p, sv_dtype dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------- sampling over a tree
+// Where the race of a sequence draws from: the stop node u, the children it rejected (m,
+// the last one c), u's residual row, Z of the residual before c (1 if m < 2) and the
+// log-normalisers of target row u and draft row c.
+struct TreeStop {
+  double zp, lp, lq;
+  int32_t u, c, m, slot;
+};
+
 struct TreeSampleParams {
   const void* target;         // [B][K][V]
   const void* draft;          // [B][K-1][V]: row i-1 = the distribution node i was drawn from
@@ -92,37 +97,49 @@ struct TreeSampleParams {
   int32_t* accept_len;
   int32_t* out_tokens;        // [B][K]
   int32_t* path;              // [B][K]
-  const float* part_m;        // [B*(2K-1)][nchunk] row_lse partials (target rows, then draft)
-  const double* part_s;
   double* zpart;              // [B][K][nz] partial sums of each residual, slot = child node
   double* ztab;               // [B][K] Z of the residual left by rejecting each child
   double* resid;              // [B][nbranch][V] residual of each branching node (fp64)
-  double* lnorm;              // [B*(2K-1)] row log-normalisers (row_lse row order)
+  float* part_m;              // [B*(2K-1)][4] row parts' maxima (target rows, then draft)
+  double* part_s;             // [B*(2K-1)][4] row parts' sums of e^((x - m) / T)
+  double* lnorm;              // [B*(2K-1)] row log-normalisers (written by the first pass)
   double* race_key;           // [B][race_nchunk][2]
   int32_t* race_idx;
-  int32_t* stop;              // [B][2]: node the walk stopped at, its children (all rejected)
+  TreeStop* stop;             // [B]
   int32_t B, K, V;
-  int32_t nchunk;
-  int32_t zchunk, nz;
+  int32_t nz;                 // residual chunks per row
   int32_t race_chunk, race_nchunk;
+  int32_t nbranch;            // nodes with two or more children (at least 1)
+  int32_t n_last;             // entries of last_z
+  int32_t has_lnorm;          // 1: a residual pass runs and writes lnorm
   double inv_t;
   uint64_t seed, offset;
+  uint64_t elder[kMaxBlock];      // bit i: node i is an elder sibling of node c
+  uint64_t zl_mask;               // bit c: c is a second-to-last child (Z folded by the walk)
+  int32_t pass_node[kMaxBlock];   // residual-pass words (u | c << 8 | c_prev << 16 | row << 24)
   int8_t parent[kMaxBlock];       // parent of node i (node 0: -1)
-  int8_t sib[kMaxBlock];          // position of node i among its parent's children
   int8_t child_start[kMaxBlock];  // first entry of node u's children in child_list
   int8_t child_count[kMaxBlock];
   int8_t child_list[kMaxBlock];   // children grouped by parent, increasing node order
-  int8_t by_count[kMaxBlock];     // nodes by decreasing child count (ties: node order)
   int8_t branch_slot[kMaxBlock];  // row of resid of each node with two or more children
-  int32_t nbranch;
+  int8_t last_z[kMaxBlock];       // second-to-last child of every branching node
+};
+
+// Host side of the plan: where pass j's words start in pass_node and how many it has.
+struct TreePassPlan {
+  int off[kMaxBlock];
+  int n[kMaxBlock];
 };
 
 size_t sample_tree_workspace_bytes(int B, int K, int V);
-// Fills the plan fields (chunks, tree tables) of p from the host tree; returns the number
-// of residual rounds (the largest child count - 1, at least 0).
-int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host);
-hipError_t launch_sample_tree(const TreeSampleParams& p, int rounds, sv_dtype dtype,
-                              hipStream_t stream);
+// Points p's scratch arrays into the workspace (p.B, p.K, p.V and the plan's chunk counts
+// set).
+void carve_sample_tree_workspace(TreeSampleParams& p, void* workspace);
+// Fills the plan fields (chunks, tree tables, pass words) of p from the host tree; returns
+// the number of residual passes (the largest child count - 1, at least 0).
+int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host, TreePassPlan& plan);
+hipError_t launch_sample_tree(const TreeSampleParams& p, const TreePassPlan& plan, int rounds,
+                              sv_dtype dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------- latent compressor
 struct CompressParams {

@@ -130,11 +130,7 @@ lm_head_argmax_kernel(const void* hidden, const void* weight, int32_t M, int32_t
         const uint64_t key = v < V ? argmax_key(acc[mt][nb][r], static_cast<uint32_t>(v)) : 0;
         best = key > best ? key : best;
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {          // over the 16 columns of the lane group
-        const uint64_t w = __shfl_xor(best, o);
-        best = w > best ? w : best;
-      }
+      best = group_max_u64<4>(best);               // over the 16 columns of the lane group
       if (l16 == 0) red[wave][16 * mt + 4 * g + r] = best;
     }
   }

@@ -56,20 +56,28 @@ __device__ __forceinline__ bool better(double k, int32_t i, double bk, int32_t b
 }
 
 // Smallest (key, index) of a workgroup, for the residual race and the p race.
+// One exchange stage of the (key, index) minimum of two races (better() is symmetric).
+template <int S>
+__device__ __forceinline__ void best_stage(double& bk_r, int32_t& bi_r, double& bk_p, int32_t& bi_p) {
+  const double kr = xlane_f64<S>(bk_r);
+  const int32_t ir = static_cast<int32_t>(xlane<S>(static_cast<uint32_t>(bi_r)));
+  if (better(kr, ir, bk_r, bi_r)) { bk_r = kr; bi_r = ir; }
+  const double kp = xlane_f64<S>(bk_p);
+  const int32_t ip = static_cast<int32_t>(xlane<S>(static_cast<uint32_t>(bi_p)));
+  if (better(kp, ip, bk_p, bi_p)) { bk_p = kp; bi_p = ip; }
+}
+
 template <int kThreads>
 __device__ __forceinline__ void block_best(double& bk_r, int32_t& bi_r, double& bk_p,
                                            int32_t& bi_p, double (*rk)[kThreads / kWave],
                                            int32_t (*ri)[kThreads / kWave]) {
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double kr = __shfl_xor(bk_r, o);
-    const int32_t ir = __shfl_xor(bi_r, o);
-    if (better(kr, ir, bk_r, bi_r)) { bk_r = kr; bi_r = ir; }
-    const double kp = __shfl_xor(bk_p, o);
-    const int32_t ip = __shfl_xor(bi_p, o);
-    if (better(kp, ip, bk_p, bi_p)) { bk_p = kp; bi_p = ip; }
-  }
+  best_stage<0>(bk_r, bi_r, bk_p, bi_p);
+  best_stage<1>(bk_r, bi_r, bk_p, bi_p);
+  best_stage<2>(bk_r, bi_r, bk_p, bi_p);
+  best_stage<3>(bk_r, bi_r, bk_p, bi_p);
+  best_stage<4>(bk_r, bi_r, bk_p, bi_p);
+  best_stage<5>(bk_r, bi_r, bk_p, bi_p);
   if ((tid & 63) == 0) {
     rk[0][tid >> 6] = bk_r;
     ri[0][tid >> 6] = bi_r;

@@ -47,7 +47,8 @@ constexpr int kNormLoads = 10;                    // 16-byte loads in flight per
                                                   // quarter of a bf16 row of 152k in one round)
 constexpr int kWalkThreads = 1024;                // wave 0 walks, the others fold Z
 constexpr int kZChunk = 4 * kThreads;             // vocabulary entries per residual workgroup
-constexpr int kRaceChunk = 4 * kThreads;          // vocabulary entries per race workgroup
+constexpr int kRaceThreads = 256;
+constexpr int kRaceChunk = 4 * kRaceThreads;      // vocabulary entries per race workgroup
 constexpr uint64_t kResample = 1ull << 32;        // RESAMPLE purpose in counter word 2
 
 // Row index rho of target row u / draft row of node c in the normaliser table.
@@ -185,6 +186,7 @@ tree_residual_kernel(int32_t j, int32_t off, int32_t n_nodes, const TreeSamplePa
   __shared__ double zprev_sh;
   __shared__ double lsh_pq[2];
   __shared__ double red[kThreads / kWave];
+  __shared__ int32_t tok_sh[kMaxBlock];            // every node's token (node 0: none)
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
   const int b = blockIdx.y / n_nodes;
@@ -207,6 +209,7 @@ tree_residual_kernel(int32_t j, int32_t off, int32_t n_nodes, const TreeSamplePa
     if (j == 1) xp[e] = logit_at<kBF16>(p.target, trow + v);
     else rb[e] = buf[v];
   }
+  if (tid < p.K - 1) tok_sh[tid + 1] = p.tokens[static_cast<size_t>(b) * (p.K - 1) + tid];
   // row normalisers: the first pass folds its two rows from the parts (two lanes, shared
   // through LDS) and its first workgroup writes every row's into the table the later
   // kernels read
@@ -249,6 +252,15 @@ tree_residual_kernel(int32_t j, int32_t off, int32_t n_nodes, const TreeSamplePa
       sum += raw;
     }
   }
+  // q_c at the tokens of c's younger siblings that fall in this chunk (the walk's
+  // threshold of sibling s after rejecting c needs it): lane s of wave 0 (same arithmetic
+  // as the elements above)
+  if (tid < K && ((p.younger[c] >> tid) & 1u)) {
+    const int xs = tok_sh[tid];
+    if (xs >= chunk * kZChunk && xs < min((chunk + 1) * kZChunk, V))
+      p.qpair[(static_cast<size_t>(b) * K + tid) * kMaxBlock + c] =
+          exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow + xs)) * it - Lq);
+  }
   sum = wave_sum_f64(sum);
   if ((tid & 63) == 0) red[tid >> 6] = sum;
   __syncthreads();
@@ -281,27 +293,20 @@ tree_walk_kernel(const TreeSampleParams p) {
   const int32_t* tok_b = p.tokens + static_cast<size_t>(b) * (K - 1);
   if (wave > 0) {                                  // each wave meets exactly one barrier
     if (wave < 8) {
-      // elder siblings' probabilities of each node's token: wave w takes nodes c = w,
-      // w + 7, ...; lane l computes q_l(x_c) when node l is an elder sibling of c (all loads
-      // first; elder siblings exist only when a residual pass ran, so lnorm is written)
+      // elder siblings' probabilities of each node's token (q_l(x_c), written by the pass
+      // that subtracted l): wave w takes nodes c = w, w + 7, ..., lane l sibling l
       constexpr int kSlots = (kMaxBlock + 6) / 7;
-      float v[kSlots];
-      double Ll = 0.0;
-      if (p.has_lnorm && lane >= 1 && lane < K) Ll = p.lnorm[draft_rho(p.B, b, K, lane)];
+      double v[kSlots];
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
         const int c = min(wave + 7 * sl, K - 1);
         const bool mine = wave + 7 * sl < K && ((p.elder[c] >> lane) & 1u);
-        const int32_t x = tok_b[c - 1];
-        const int xs = (x >= 0 && x < V) ? x : 0;
-        v[sl] = mine ? logit_at<kBF16>(p.draft, (static_cast<size_t>(b) * (K - 1) + (lane - 1)) * V + xs)
-                     : 0.0f;
+        v[sl] = mine ? p.qpair[(static_cast<size_t>(b) * K + c) * kMaxBlock + lane] : 0.0;
       }
-      const double it = p.inv_t;
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
         const int c = wave + 7 * sl;
-        if (c < K && ((p.elder[c] >> lane) & 1u)) qv[c][lane] = exp(static_cast<double>(v[sl]) * it - Ll);
+        if (c < K && ((p.elder[c] >> lane) & 1u)) qv[c][lane] = v[sl];
       }
     } else if (wave < 10) {
       // row normalisers and the passes' Z table, one thread per entry
@@ -312,15 +317,25 @@ tree_walk_kernel(const TreeSampleParams p) {
       }
       if (r < K) zc[r] = p.ztab[static_cast<size_t>(b) * K + r];
     } else {
-      // Z after each branching node's second-to-last child: wave w folds entries
-      // w - 10, w - 4, ... of last_z
-      for (int k = wave - 10; k < p.n_last; k += kWalkThreads / kWave - 10) {
-        const int cz = p.last_z[k];
+      // Z after each branching node's second-to-last child: the six waves' 16-lane groups
+      // fold entries g, g + 24, ... of last_z, every partial of a round in flight
+      constexpr int kGroups = (kWalkThreads / kWave - 10) * 4;
+      constexpr int kU = 12;
+      const int g = (wave - 10) * 4 + (lane >> 4), l16 = lane & 15;
+      for (int k0 = 0; k0 < p.n_last; k0 += kGroups) {
+        const int k = k0 + g;
+        const int cz = p.last_z[min(k, p.n_last - 1)];
         const double* z = p.zpart + (static_cast<size_t>(b) * K + cz) * p.nz;
         double sz = 0.0;
-        for (int q = lane; q < p.nz; q += kWave) sz += z[q];
-        sz = wave_sum_f64(sz);
-        if (lane == 0) zlast[cz] = sz;
+        for (int q0 = l16; q0 < p.nz; q0 += 16 * kU) {
+          double t[kU];
+#pragma unroll
+          for (int i = 0; i < kU; ++i) t[i] = q0 + 16 * i < p.nz ? z[q0 + 16 * i] : 0.0;
+#pragma unroll
+          for (int i = 0; i < kU; ++i) sz += t[i];
+        }
+        sz = group_sum_f64<4>(sz);
+        if (l16 == 0 && k < p.n_last) zlast[cz] = sz;
       }
     }
     __syncthreads();
@@ -336,32 +351,37 @@ tree_walk_kernel(const TreeSampleParams p) {
   const int xs = in_v ? x : 0;
   const double lp = logit_at<kBF16>(p.target, (static_cast<size_t>(b) * K + u) * V + xs);
   const double lq = logit_at<kBF16>(p.draft, (static_cast<size_t>(b) * (K - 1) + (node ? c - 1 : 0)) * V + xs);
-  __syncthreads();                                 // the gathered values are in LDS
-  const double Lu = lsh[u];
-  const double Lc = lsh[K - 1 + (node ? c : 1)];
-  bool pass = false;
-  if (node && in_v && lp != -INFINITY) {
-    double thr;
+  const int rho_u = target_rho(b, K, u), rho_c = draft_rho(p.B, b, K, node ? c : 1);
+  const double Lu = p.has_lnorm ? p.lnorm[rho_u] : fold_lnorm(p, rho_u);
+  const double Lc = p.has_lnorm ? p.lnorm[rho_c] : fold_lnorm(p, rho_c);
+  // everything that needs no gathered value, before the barrier: the uniform, a first
+  // child's threshold, p_u and q_c at the token
+  const U64x4 wv = philox(p.offset, static_cast<uint64_t>(b), static_cast<uint64_t>(c), 0, p.seed, 0);
+  const double uc = to_uniform(wv.x[0]);
+  const bool live = node && in_v && lp != -INFINITY;
+  double thr = 0.0, pv = 0.0, qc = 0.0;
+  if (live) {
     if (first_child) {                             // against p_u: the chain's log form
       thr = exp(fmin(0.0, (lp - lq) * it - (Lu - Lc)));
     } else {
-      const double pv = exp(lp * it - Lu);
-      double r = pv;
-      // the elder siblings in increasing node order (the order they are tested in)
-      for (uint64_t e = p.elder[c]; e; e &= e - 1) {
-        const int ci = __builtin_ctzll(e);
-        const double raw = fmax(0.0, r - qv[c][ci]);
-        // Z after child ci: from the pass after it, or (a second-to-last child) folded here
-        const double z = ((p.zl_mask >> ci) & 1u) ? zlast[ci] : zc[ci];
-        r = z > 0.0 ? raw / z : pv;
-      }
-      const double qc = exp(lq * it - Lc);
-      thr = r == 0.0 ? 0.0 : (qc == 0.0 ? 1.0 : fmin(1.0, r / qc));
+      pv = exp(lp * it - Lu);
+      qc = exp(lq * it - Lc);
     }
-    const U64x4 wv = philox(p.offset, static_cast<uint64_t>(b), static_cast<uint64_t>(c), 0,
-                            p.seed, 0);
-    pass = to_uniform(wv.x[0]) < thr;
   }
+  __syncthreads();                                 // the gathered values are in LDS
+  if (live && !first_child) {
+    double r = pv;
+    // the elder siblings in increasing node order (the order they are tested in)
+    for (uint64_t e = p.elder[c]; e; e &= e - 1) {
+      const int ci = __builtin_ctzll(e);
+      const double raw = fmax(0.0, r - qv[c][ci]);
+      // Z after child ci: from the pass after it, or (a second-to-last child) folded here
+      const double z = ((p.zl_mask >> ci) & 1u) ? zlast[ci] : zc[ci];
+      r = z > 0.0 ? raw / z : pv;
+    }
+    thr = r == 0.0 ? 0.0 : (qc == 0.0 ? 1.0 : fmin(1.0, r / qc));
+  }
+  const bool pass = live && uc < thr;
   // the walk: at the current node the lowest-numbered passing child (children are
   // tested in increasing node order); node numbers only grow, so it ends within K-1 steps
   const int par = node ? u : -1;
@@ -401,10 +421,10 @@ tree_walk_kernel(const TreeSampleParams p) {
 
 // ---- 4. the race over the stop node's last residual
 template <bool kBF16>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kRaceThreads)
 tree_race_kernel(const TreeSampleParams p) {
-  __shared__ double rk[2][kThreads / kWave];
-  __shared__ int32_t ri[2][kThreads / kWave];
+  __shared__ double rk[2][kRaceThreads / kWave];
+  __shared__ int32_t ri[2][kRaceThreads / kWave];
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
   const int b = blockIdx.y;
@@ -417,7 +437,7 @@ tree_race_kernel(const TreeSampleParams p) {
   const double* buf = p.resid + (static_cast<size_t>(b) * p.nbranch + st.slot) * V;
   const size_t trow = (static_cast<size_t>(b) * K + u) * V;
   const size_t qrow = (static_cast<size_t>(b) * (K - 1) + (c - 1)) * V;
-  const int jb = chunk * p.race_chunk + 4 * tid;
+  const int jb = chunk * p.race_chunk + 4 * tid;   // one Philox block (4 tokens) a thread
   double bk_r = INFINITY, bk_p = INFINITY;
   int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
   if (jb < V) {
@@ -445,7 +465,7 @@ tree_race_kernel(const TreeSampleParams p) {
       }
     }
   }
-  block_best<kThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
+  block_best<kRaceThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
   if (tid == 0) {
     const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + chunk) * 2;
     p.race_key[slot] = bk_r;
@@ -481,7 +501,8 @@ tree_finish_kernel(const TreeSampleParams p) {
 }  // namespace
 
 // Workspace, in order: zpart [B][K][nz], resid [B][K/2][V] (fp64), race_key
-// [B][race_nchunk][2], part_s [B(2K-1)][kNormSplit], lnorm [B(2K-1)], ztab [B][K], stop [B] records,
+// [B][race_nchunk][2], part_s [B(2K-1)][kNormSplit], lnorm [B(2K-1)], qpair [B][K][64],
+// ztab [B][K], stop [B] records,
 // race_idx [B][race_nchunk][2], part_m [B(2K-1)][kNormSplit] (fp32).
 size_t sample_tree_workspace_bytes(int B, int K, int V) {
   const size_t rows = static_cast<size_t>(B) * (2 * K - 1);
@@ -493,6 +514,7 @@ size_t sample_tree_workspace_bytes(int B, int K, int V) {
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(double);   // race_key
   off += rows * kNormSplit * sizeof(double);                    // part_s
   off += rows * sizeof(double);                                 // lnorm
+  off += static_cast<size_t>(B) * K * kMaxBlock * sizeof(double); // qpair
   off += static_cast<size_t>(B) * K * sizeof(double);           // ztab
   off += static_cast<size_t>(B) * sizeof(TreeStop);             // stop
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(int32_t);  // race_idx
@@ -513,6 +535,8 @@ void carve_sample_tree_workspace(TreeSampleParams& p, void* workspace) {
   w += rows * kNormSplit * sizeof(double);
   p.lnorm = reinterpret_cast<double*>(w);
   w += rows * sizeof(double);
+  p.qpair = reinterpret_cast<double*>(w);
+  w += static_cast<size_t>(p.B) * p.K * kMaxBlock * sizeof(double);
   p.ztab = reinterpret_cast<double*>(w);
   w += static_cast<size_t>(p.B) * p.K * sizeof(double);
   p.stop = reinterpret_cast<TreeStop*>(w);
@@ -556,6 +580,9 @@ int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host, TreePassP
       if (parents_host[i - 1] == parents_host[c - 1]) e |= 1ull << i;
     p.elder[c] = e;
   }
+  for (int c = 0; c < kMaxBlock; ++c) p.younger[c] = 0;
+  for (int c = 1; c < K; ++c)
+    for (uint64_t e = p.elder[c]; e; e &= e - 1) p.younger[__builtin_ctzll(e)] |= 1ull << c;
   int nbr = 0, mmax = 0;
   p.n_last = 0;
   p.zl_mask = 0;
@@ -615,8 +642,8 @@ hipError_t launch_sample_tree(const TreeSampleParams& p, const TreePassPlan& pla
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 gr(p.race_nchunk, p.B);
-  if (bf) hipLaunchKernelGGL(tree_race_kernel<true>, gr, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL(tree_race_kernel<false>, gr, dim3(kThreads), 0, stream, p);
+  if (bf) hipLaunchKernelGGL(tree_race_kernel<true>, gr, dim3(kRaceThreads), 0, stream, p);
+  else hipLaunchKernelGGL(tree_race_kernel<false>, gr, dim3(kRaceThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tree_finish_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);

@@ -103,6 +103,7 @@ struct TreeSampleParams {
   float* part_m;              // [B*(2K-1)][4] row parts' maxima (target rows, then draft)
   double* part_s;             // [B*(2K-1)][4] row parts' sums of e^((x - m) / T)
   double* lnorm;              // [B*(2K-1)] row log-normalisers (written by the first pass)
+  double* qpair;              // [B][K][64]: [s][c] = q_c(x_s) for c an elder sibling of s
   double* race_key;           // [B][race_nchunk][2]
   int32_t* race_idx;
   TreeStop* stop;             // [B]
@@ -115,6 +116,7 @@ struct TreeSampleParams {
   double inv_t;
   uint64_t seed, offset;
   uint64_t elder[kMaxBlock];      // bit i: node i is an elder sibling of node c
+  uint64_t younger[kMaxBlock];    // bit i: node i is a younger sibling of node c
   uint64_t zl_mask;               // bit c: c is a second-to-last child (Z folded by the walk)
   int32_t pass_node[kMaxBlock];   // residual-pass words (u | c << 8 | c_prev << 16 | row << 24)
   int8_t parent[kMaxBlock];       // parent of node i (node 0: -1)

@@ -229,7 +229,7 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
       const double pj = exp(static_cast<double>(xp[e]) * it - Lp);
       double rj = pj;
       if (resid) rj = fmax(0.0, pj - exp(static_cast<double>(xq[e]) * it - Lq));
-      const double ej = -log1p(-to_uniform(w.x[e]));
+      const double ej = neg_log1m(to_uniform(w.x[e]));
       if (rj > 0.0) {
         const double k = ej / rj;
         if (better(k, j, bk_r, bi_r)) { bk_r = k; bi_r = j; }

@@ -454,7 +454,7 @@ tree_race_kernel(const TreeSampleParams p) {
         const double qv = exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow + v)) * it - st.lq);
         r = fmax(0.0, rh - qv);
       }
-      const double ej = -log1p(-to_uniform(w.x[e]));
+      const double ej = neg_log1m(to_uniform(w.x[e]));
       if (r > 0.0) {
         const double k = ej / r;
         if (better(k, v, bk_r, bi_r)) { bk_r = k; bi_r = v; }

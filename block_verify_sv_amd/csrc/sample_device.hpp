@@ -45,6 +45,41 @@ __device__ __forceinline__ double to_uniform(uint64_t w) {
   return static_cast<double>(w >> 11) * 0x1.0p-53;
 }
 
+// E = -ln(1 - u) for a uniform u in [0, 1) on the 2^-53 grid, in fp64: the exponential
+// variate of the race.  1 - u is exact; with 1 - u = m 2^k, m in [sqrt(1/2), sqrt(2)),
+// ln m = 2 atanh(s), s = (m - 1) / (m + 1), |s| <= 0.172, summed as the odd series
+// 2 (s + s^3/3 + ... + s^21/21) (truncation below 2^-60 relative), and k ln 2 with ln 2
+// split in two parts.  About 35 instructions against 136 for the library log1p; the
+// result is within a few ulp of -log1p(-u).
+__device__ __forceinline__ double neg_log1m(double u) {
+  // ln 2 in two parts: hi is ln 2 rounded to a multiple of 2^-32 (so k * hi is exact for
+  // |k| < 2^20), lo = ln 2 - hi rounded to fp64
+  constexpr double kLn2Hi = 0x1.62e42ff000000p-1;
+  constexpr double kLn2Lo = -0x1.718432a1b0e26p-35;
+  const double x = 1.0 - u;
+  int k;
+  double m = frexp(x, &k);                         // x = m 2^k, m in [1/2, 1)
+  if (m < 0.70710678118654752440) {
+    m *= 2.0;
+    --k;
+  }
+  const double s = (m - 1.0) / (m + 1.0);
+  const double z = s * s;
+  double q = 1.0 / 21.0;
+  q = fma(q, z, 1.0 / 19.0);
+  q = fma(q, z, 1.0 / 17.0);
+  q = fma(q, z, 1.0 / 15.0);
+  q = fma(q, z, 1.0 / 13.0);
+  q = fma(q, z, 1.0 / 11.0);
+  q = fma(q, z, 1.0 / 9.0);
+  q = fma(q, z, 1.0 / 7.0);
+  q = fma(q, z, 1.0 / 5.0);
+  q = fma(q, z, 1.0 / 3.0);
+  const double lm = 2.0 * fma(s * z, q, s);        // ln m
+  const double dk = static_cast<double>(k);
+  return -(fma(dk, kLn2Hi, fma(dk, kLn2Lo, lm)));
+}
+
 template <bool kBF16>
 __device__ __forceinline__ float logit_at(const void* base, size_t i) {
   if constexpr (kBF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);

@@ -19,12 +19,14 @@
 //      vocabulary chunk, sequence x node with more than j children): the residual after
 //      the j-th child, max(0, rhat_{j-1} - q_j), stored per element in fp64 (one row per
 //      branching node, updated in place pass after pass) and its partial sums, which the
-//      next pass folds into Z_j;
+//      next pass folds into Z_j.  The first pass also writes every row's normaliser into
+//      a table, and each pass writes q_j at the tokens of c_j's younger siblings;
 //   3. tree_walk_kernel, one workgroup per sequence: its other waves gather the row
 //      normalisers, the residual normalisers (folding the ones no later pass folded) and
-//      every node's elder siblings' logits at its token while wave 0 loads its node's own;
-//      then wave 0 computes every threshold and its ACCEPT uniform (lane = node), walks
-//      from the anchor with ballots, and writes the stop node's record for the race;
+//      every node's elder siblings' probabilities of its token while wave 0 loads its
+//      node's own logits; then wave 0 computes every threshold and its ACCEPT uniform
+//      (lane = node), walks from the anchor with ballots, and writes the stop node's
+//      record for the race;
 //   4. tree_race_kernel, grid (1024-entry chunk, sequence): the exponential race over the
 //      stop node's last residual (the chain's race: RESAMPLE uniforms of the stop row,
 //      with a race over p_u carried along for an all-zero residual);
@@ -45,7 +47,7 @@ constexpr int kNormSplit = 4;                    // workgroups per row of the no
 constexpr int kNormThreads = 512;
 constexpr int kNormLoads = 10;                    // 16-byte loads in flight per thread (a
                                                   // quarter of a bf16 row of 152k in one round)
-constexpr int kWalkThreads = 1024;                // wave 0 walks, the others fold Z
+constexpr int kWalkThreads = 1024;                // wave 0 walks, the others gather
 constexpr int kZChunk = 4 * kThreads;             // vocabulary entries per residual workgroup
 constexpr int kRaceThreads = 256;
 constexpr int kRaceChunk = 4 * kRaceThreads;      // vocabulary entries per race workgroup
@@ -274,10 +276,12 @@ tree_residual_kernel(int32_t j, int32_t off, int32_t n_nodes, const TreeSamplePa
 
 // ---- 3. the tests and the walk, one workgroup per sequence.  The other waves first
 // gather everything the tests need, all loads in flight together: the row normalisers
-// (folded from the parts), the Z of every elder sibling (from the passes' table, or
-// folded here for each branching node's second-to-last child, which no later pass
-// folded) and each node's elder siblings' draft logits at its token.  Wave 0 meanwhile
-// loads its own node's two logits; then it decides every test (lane = node) and walks.
+// (from the first pass's table, or folded from the parts when no pass ran), the Z of
+// every elder sibling (from the passes' table, or folded here for each branching node's
+// second-to-last child, which no later pass folded) and each node's elder siblings'
+// probabilities of its token (written by the passes).  Wave 0 meanwhile loads its own
+// node's two logits and computes what needs none of that; then it decides every test
+// (lane = node) and walks.
 template <bool kBF16>
 __global__ void __launch_bounds__(kWalkThreads)
 tree_walk_kernel(const TreeSampleParams p) {

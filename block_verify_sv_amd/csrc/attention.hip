@@ -19,7 +19,10 @@
 // context length arrives; a batch reads the context length first and lets the splits
 // past a shorter sequence's end leave at once.
 // With at most 32 query rows per KV head and d = 64 (16-bit), the workgroup is one
-// row-block wave pair (128 threads, two-tile ring) so that several share a CU.
+// row-block wave pair (128 threads, two-tile ring) so that several share a CU; when every
+// (b, g) also fits one split of at most two tiles (the semi-autoregressive block), a pairs
+// kernel takes several (b, g) per workgroup and loads the next one's tiles while the
+// current one computes.
 // Per tile and row block the wave computes S^T = K_tile . Q^T (keys on the MFMA M axis,
 // query rows on N, so each lane owns one query row), applies the block mask, runs the
 // online softmax in registers, and accumulates O^T = V^T . P^T.
@@ -606,6 +609,275 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
   }
 }
 
+// Pairs kernel: several (sequence, KV head) pairs per workgroup, each pair's keys (at most
+// two 64-key tiles, such as the semi-autoregressive block's compressed rows plus its
+// slots) in one split whose output is written directly.  While a pair computes, the next
+// pair's two tiles are already loading into registers (and the pair after it has its
+// page ids and query rows loading), so the start-up round trips of every pair but the
+// first hide under work.  One row block of at most 32 rows, two key-half waves, 16-bit
+// data; the per-tile math is the split kernel's.
+template <class Tag, int D>
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_pairs_kernel(const int32_t* page_table, const void* k_cache, const void* v_cache,
+                  const int32_t* ctx_lens, int32_t npairs, int32_t P_log2, int32_t max_pages,
+                  int32_t num_pages, int32_t Hkv, const AttnParams p) {
+  using S = typename Tag::store_t;
+  using Op = typename Mfma<Tag>::op_t;
+  static_assert(Tag::kBytes == 2 && Tag::KPL == 8, "16-bit data");
+  constexpr int T = 128;
+  constexpr int EPC = 8;
+  constexpr int KROW = D + EPC;
+  constexpr int VROW = kTK + EPC;
+  constexpr int CPK = D / EPC;
+  constexpr int K_PER_T = kTK * D / EPC / T;
+  constexpr int V_PER_T = D * kTK / EPC / T;
+  constexpr int KSTEPS = D / 16;
+  constexpr int PSW = 2;                         // MFMA steps over a wave's 32 keys
+  constexpr int DB = D / 32;
+  constexpr int HB = DB / 2;
+  constexpr int NT = 2;                          // tiles per pair
+  constexpr int K_LDS = NT * kTK * KROW * 2;
+  constexpr int V_LDS = NT * D * VROW * 2;
+  static_assert((4 * DB + 1) * 64 * 16 <= K_LDS + V_LDS, "combine stage");
+  __shared__ __align__(16) char smem[K_LDS + V_LDS];
+  S* const k_lds = reinterpret_cast<S*>(smem);
+  S* const v_lds = reinterpret_cast<S*>(smem + K_LDS);
+
+  const int tid = threadIdx.x;
+  const int kh = __builtin_amdgcn_readfirstlane(tid >> 6);   // key half of every tile
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int Pm1 = (1 << P_log2) - 1;
+  const int last_page = max_pages - 1;
+  const int KR = min(Pm1 + 1, kTK);
+  const int TPR = T * KR / kTK;
+  const int run = tid / TPR;
+  const int li = tid - run * TPR;
+  const int KGR = KR / EPC;
+  int k_goff[K_PER_T], k_loff[K_PER_T], v_goff[V_PER_T], v_loff[V_PER_T], v_key[V_PER_T];
+#pragma unroll
+  for (int u = 0; u < K_PER_T; ++u) {
+    const int ci = li + TPR * u;
+    const int key = ci / CPK, part = ci - (ci / CPK) * CPK;
+    k_goff[u] = key * D + part * EPC;
+    k_loff[u] = key_row(run * KR + key) * KROW + part * EPC;
+  }
+#pragma unroll
+  for (int u = 0; u < V_PER_T; ++u) {
+    const int ci = li + TPR * u;
+    const int d = ci / KGR, kp = ci - (ci / KGR) * KGR;
+    v_goff[u] = (d << P_log2) + kp * EPC;
+    v_loff[u] = d * VROW + run * KR + kp * EPC;
+    v_key[u] = run * KR + kp * EPC;
+  }
+  const uint32_t pstride = static_cast<uint32_t>(Hkv * D) << P_log2;
+  const S* const kc = static_cast<const S*>(k_cache);
+  const S* const vc = static_cast<const S*>(v_cache);
+  const float c2 = p.scale_log2;
+  const float resc = kRescale / c2;
+  const int r = min(l32, p.R - 1);               // this lane's query row
+  const int ri = r / p.G;
+  const uint64_t rmask = p.mask[ri];
+
+  // per pair: where it is and what its loads need (all loads unconditional, clamped)
+  struct Meta {
+    int b, g, ctx;
+    int pg[NT];
+  };
+  auto meta = [&](int q, Meta& m) {
+    const int qq = min(q, npairs - 1);
+    m.b = qq / Hkv;
+    m.g = qq - m.b * Hkv;
+    m.ctx = ctx_lens[m.b];
+    const int32_t* table = page_table + static_cast<size_t>(m.b) * max_pages;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) m.pg[t] = table[min((t * kTK + run * KR) >> P_log2, last_page)];
+  };
+  auto load_q = [&](const Meta& m, Op (&qo)[KSTEPS]) {
+    const int head = m.g * p.G + (r - ri * p.G);
+    const S* qp = static_cast<const S*>(p.q) + ((static_cast<size_t>(m.b) * p.K + ri) * p.Hq + head) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qo[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 16 + h * 8);
+  };
+  u32x4 tk[NT][K_PER_T], tv[NT][V_PER_T];
+  bool pok[NT];
+  auto load_tiles = [&](const Meta& m) {
+    const S* kc_h = kc + (static_cast<size_t>(m.g * D) << P_log2);
+    const S* vc_h = vc + (static_cast<size_t>(m.g * D) << P_log2);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      pok[t] = static_cast<unsigned>(m.pg[t]) < static_cast<unsigned>(num_pages);
+      const uint32_t page = pok[t] ? static_cast<uint32_t>(m.pg[t]) : 0u;
+      const uint32_t slot = static_cast<uint32_t>((t * kTK + run * KR) & Pm1);
+      const size_t poff = static_cast<size_t>(page) * pstride;
+      const S* kb = kc_h + poff + slot * D;
+      const S* vb = vc_h + poff + slot;
+#pragma unroll
+      for (int u = 0; u < K_PER_T; ++u) tk[t][u] = *reinterpret_cast<const u32x4*>(kb + k_goff[u]);
+#pragma unroll
+      for (int u = 0; u < V_PER_T; ++u) tv[t][u] = *reinterpret_cast<const u32x4*>(vb + v_goff[u]);
+    }
+  };
+
+  Meta cur, nxt;
+  Op qcur[KSTEPS], qnxt[KSTEPS];
+  const int stride = gridDim.x;
+  int q = blockIdx.x;
+  meta(q, cur);
+  load_tiles(cur);
+  load_q(cur, qnxt);
+  meta(q + stride, nxt);
+  for (; q < npairs; q += stride) {
+    const int ctx = cur.ctx < 0 ? 0 : (cur.ctx > p.max_ctx ? p.max_ctx : cur.ctx);
+    const int nk = ctx + p.K;                    // at most NT tiles (checked at launch)
+    // ---- both tiles into LDS (keys past nk zeroed in V; their scores are masked)
+    __syncthreads();                             // the previous pair's epilogue is done with LDS
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      S* kl = k_lds + t * kTK * KROW;
+      S* vl = v_lds + t * D * VROW;
+      const bool ok = pok[t] && t * kTK + run * KR < nk;
+      const int left = nk - t * kTK;
+#pragma unroll
+      for (int u = 0; u < K_PER_T; ++u)
+        *reinterpret_cast<u32x4*>(kl + k_loff[u]) = ok ? tk[t][u] : zero4();
+#pragma unroll
+      for (int u = 0; u < V_PER_T; ++u) {
+        u32x4 v = ok ? tv[t][u] : zero4();
+        v = keep16(v, left - v_key[u]);
+        *reinterpret_cast<u32x4*>(vl + v_loff[u]) = v;
+      }
+    }
+    __syncthreads();
+    // ---- the next pair's tiles load while this one computes; the one after that
+    // fetches its page ids and query rows
+    const int ub = cur.b, ug = cur.g;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qcur[ks] = qnxt[ks];
+    load_tiles(nxt);
+    load_q(nxt, qnxt);
+    cur = nxt;
+    meta(q + 2 * stride, nxt);
+
+    float m_run = kNegBig, l_run = 0.0f;
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int kt = t * kTK;
+      if (kt >= nk) break;                       // workgroup-uniform
+      const S* krow = k_lds + t * kTK * KROW + (kh * 32 + l32) * KROW;
+      Op kop[KSTEPS];
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) kop[ks] = *reinterpret_cast<const u32x4*>(krow + ks * 16 + h * 8);
+      f32x16 sacc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) sacc = Mfma<Tag>::step(kop[ks], qcur[ks], sacc);
+      // visible: context keys, block key t2 iff bit t2 of the row's mask, nothing past nk
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int pos = kt + kh * 32 + key_of_reg(rr, h);
+        const int t2 = pos - ctx;
+        const uint32_t bit = static_cast<uint32_t>(rmask >> (t2 & 63)) & 1u;
+        const uint32_t vis = static_cast<uint32_t>(pos < nk) & (static_cast<uint32_t>(t2 < 0) | bit);
+        sacc[rr] = vis ? sacc[rr] : -INFINITY;
+      }
+      float mt = sacc[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
+      mt = max_halves(mt);
+      if (__any(mt > m_run + resc)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = fast_exp2((m_run - m_new) * c2);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      }
+      const float mneg = -m_run * c2;
+      float sv[16];
+      float psum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sv[e] = fast_exp2(fmaf(sacc[e], c2, mneg));
+        psum += sv[e];
+      }
+      l_run += psum;
+#pragma unroll
+      for (int psi = 0; psi < PSW; ++psi) {
+        const float* pv8 = &sv[psi * 8];
+        const Op pb = u32x4{Tag::pack2(pv8[0], pv8[1]), Tag::pack2(pv8[2], pv8[3]),
+                            Tag::pack2(pv8[4], pv8[5]), Tag::pack2(pv8[6], pv8[7])};
+        const int ps = kh * PSW + psi;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const S* vrow = v_lds + t * D * VROW + (db * 32 + l32) * VROW;
+          const Op vop = *reinterpret_cast<const u32x4*>(vrow + ps * 16 + h * 8);
+          oacc[db] = Mfma<Tag>::step(vop, pb, oacc[db]);
+        }
+      }
+    }
+    // ---- the key halves combine through LDS (as in the split kernel), then the rows go
+    // straight to the output
+    l_run = sum_halves(l_run);
+    __syncthreads();                             // both waves are done reading the tiles
+    f32x4* stage = reinterpret_cast<f32x4*>(smem);
+    float2* stage_ml = reinterpret_cast<float2*>(smem);
+    auto slot = [&](int c) { return c * 64 + lane; };
+    const bool lo_half = kh == 0;
+#pragma unroll
+    for (int j = 0; j < HB; ++j)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 lo = {oacc[j][4 * q4], oacc[j][4 * q4 + 1], oacc[j][4 * q4 + 2], oacc[j][4 * q4 + 3]};
+        const f32x4 hi = {oacc[j + HB][4 * q4], oacc[j + HB][4 * q4 + 1], oacc[j + HB][4 * q4 + 2],
+                          oacc[j + HB][4 * q4 + 3]};
+        stage[slot(kh * 4 * HB + 4 * j + q4)] = lo_half ? hi : lo;
+      }
+    stage_ml[2 * slot(4 * DB) + kh] = make_float2(m_run, l_run);
+    __syncthreads();
+    const float2 ml2 = stage_ml[2 * slot(4 * DB) + 1 - kh];
+    const float mm = fmaxf(m_run, ml2.x);
+    const float a1 = fast_exp2((m_run - mm) * c2), a2 = fast_exp2((ml2.x - mm) * c2);
+    const float L = l_run * a1 + ml2.y * a2;
+#pragma unroll
+    for (int j = 0; j < HB; ++j)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 o2 = stage[slot((1 - kh) * 4 * HB + 4 * j + q4)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float own = lo_half ? oacc[j][4 * q4 + e] : oacc[j + HB][4 * q4 + e];
+          oacc[j][4 * q4 + e] = own * a1 + o2[e] * a2;
+        }
+      }
+    if (l32 < p.R) {
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      const size_t orow = (static_cast<size_t>(ub) * p.K + ri) * p.Hq + ug * p.G + (r - ri * p.G);
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        const int db = kh * HB + j;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          S* dst = static_cast<S*>(p.out) + orow * D + db * 32 + 8 * q4 + 4 * h;
+          const uint2 v = {Tag::pack2(oacc[j][4 * q4] * inv, oacc[j][4 * q4 + 1] * inv),
+                           Tag::pack2(oacc[j][4 * q4 + 2] * inv, oacc[j][4 * q4 + 3] * inv)};
+          *reinterpret_cast<uint2*>(dst) = v;
+        }
+      }
+      if (p.lse && h == 0 && kh == 0) p.lse[orow] = (mm * c2 + log2f(L)) * 0.69314718055994531f;
+    }
+  }
+}
+
 // Four consecutive partial-output elements as floats.
 template <class Tag>
 __device__ __forceinline__ f32x4 load4(const typename Tag::store_t* src) {
@@ -749,6 +1021,16 @@ hipError_t launch_typed(const AttnParams& p, hipStream_t stream) {
   constexpr int RING = Tag::kBytes == 2 ? kRingDeep : 2;
   bool launched = false;
   if constexpr (D == 64 && Tag::kBytes == 2) {
+    // at most one row block and two tiles per (b, g) (the semi-autoregressive block):
+    // workgroups of one row-block wave pair that take several pairs each
+    if (p.direct && p.R <= 32 && p.max_ctx + p.K <= 2 * kTK) {
+      const int npairs = p.B * p.Hkv;
+      const int nwg = npairs < 4 * kNumCUs ? npairs : 4 * kNumCUs;
+      hipLaunchKernelGGL((attn_pairs_kernel<Tag, D>), dim3(nwg), dim3(128), 0, stream,
+                         p.page_table, p.k_cache, p.v_cache, p.ctx_lens, npairs, p.P_log2,
+                         p.max_pages, p.num_pages, p.Hkv, p);
+      return hipGetLastError();
+    }
     // at most one row block per KV head (the semi-autoregressive block: 5 rows, G = 1):
     // one row-block wave pair of 128 threads, four workgroups per CU
     launched = p.R <= 32 && p.chunk <= kMaxSplitKeysSmall;

@@ -227,7 +227,11 @@ ROWS = {
                   "(sv_commit); 32 calls per graph, inputs not rotated (64 KB)", 32),
     "lm_head": ("qwen7b_lmhead", "LM head fused with greedy acceptance: 16 x 3584 hidden "
                 "states against the 152,064 x 3584 bf16 output embedding (1.09 GB, more than "
-                "twice the Infinity Cache, so no rotation)", 1),
+                "twice the Infinity Cache, so no rotation), packed once beforehand by "
+                "sv_lm_head_pack (outside the timed region, as at model load)", 1),
+    "lm_head_plain": ("qwen7b_lmhead", "LM head fused with greedy acceptance over the plain "
+                      "[V][hidden] weight: 16 x 3584 hidden states against the 152,064 x 3584 "
+                      "bf16 output embedding (1.09 GB, no rotation)", 1),
 }
 
 
@@ -349,20 +353,27 @@ def run_row(args):
         def call(i, st):
             sv.accept_sample_tree(tl[i], dl[i], par, tk, ts.temperature, ts.seed, i, out=outs,
                                   stream=st)
-    elif args.row == "lm_head":
+    elif args.row in ("lm_head", "lm_head_plain"):
         li = W.make_workload_lm_head(wl)
         hs = dev_t(li.hidden_states, li.dtype)
         wt = dev_t(li.weight, li.dtype)
         dr = i32(li.drafts)
         outs = (torch.empty(li.B, dtype=torch.int32, device=dev),
                 torch.empty(li.B, li.K, dtype=torch.int32, device=dev), None)
-        sv.lm_head_greedy(hs, wt, dr, want_argmax=False, out=outs)
         nbytes = (wt.numel() + hs.numel()) * 2
         flops = 2.0 * li.B * li.K * li.V * li.hidden
         shape = {"B": li.B, "K": li.K, "hidden": li.hidden, "V": li.V}
+        if args.row == "lm_head":
+            wp = sv.lm_head_pack(wt)
+            del wt
 
-        def call(i, st):
-            sv.lm_head_greedy(hs, wt, dr, want_argmax=False, out=outs, stream=st)
+            def call(i, st):
+                sv.lm_head_greedy_packed(hs, wp, li.V, dr, want_argmax=False, out=outs,
+                                         stream=st)
+        else:
+            def call(i, st):
+                sv.lm_head_greedy(hs, wt, dr, want_argmax=False, out=outs, stream=st)
+        call(0, None)
     elif args.row == "sample_72b":
         smp = W.make_workload_sample(wl, 0)
         tl = [dev_t(smp.target_logits, smp.dtype)]

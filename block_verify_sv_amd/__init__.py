@@ -23,8 +23,10 @@ import torch
 __all__ = [
     "LIB_PATH", "load", "SvError", "AttnDesc", "verify_attention", "verify_attention_into",
     "verify_attention_noalloc_into",
-    "attention_workspace_bytes", "accept_greedy", "accept_sample", "latent_compress",
-    "kv_append", "commit", "make_desc", "SV_F32", "SV_BF16", "SV_F16",
+    "attention_workspace_bytes", "mask_array", "accept_greedy", "accept_greedy_tree",
+    "accept_sample", "accept_sample_tree", "lm_head_greedy", "lm_head_pack",
+    "lm_head_greedy_packed", "latent_compress", "kv_append", "commit", "commit_tree",
+    "make_desc", "SV_F32", "SV_BF16", "SV_F16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
@@ -82,6 +84,10 @@ _SIGNATURES = {
     "sv_lm_head_greedy_workspace": (c_i32, [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz)]),
     "sv_lm_head_greedy": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
                                   c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "sv_lm_head_pack_bytes": (c_i32, [c_i32, c_i32, ctypes.POINTER(c_sz)]),
+    "sv_lm_head_pack": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "sv_lm_head_greedy_packed": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                         c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
 }
 
 
@@ -298,19 +304,60 @@ def accept_greedy_tree(logits: torch.Tensor, parents: torch.Tensor, tokens: torc
     return acc, toks, path, am
 
 
+def lm_head_pack(weight: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """Rearranges the LM head weight [V][hidden] (bf16 or fp16) once into the packed tile
+    layout that lm_head_greedy_packed reads: a flat tensor of ceil(V / 32) * 32 * hidden
+    elements of the weight's dtype."""
+    _require(weight, "weight")
+    if weight.dim() != 2 or weight.dtype not in (torch.bfloat16, torch.float16):
+        raise SvError("weight must be a [V][hidden] bfloat16 or float16 tensor")
+    V, Hd = weight.shape
+    lib = load()
+    n = c_sz()
+    _check(lib.sv_lm_head_pack_bytes(V, Hd, ctypes.byref(n)), "sv_lm_head_pack_bytes")
+    elems = n.value // weight.element_size()
+    if out is None:
+        out = torch.empty(elems, dtype=weight.dtype, device=weight.device)
+        _on_stream(stream, out)
+    elif out.dtype != weight.dtype or out.numel() != elems or not out.is_contiguous():
+        raise SvError(f"out must be a contiguous {weight.dtype} tensor of {elems} elements")
+    _check(lib.sv_lm_head_pack(V, Hd, _DTYPES[weight.dtype], _ptr(weight), _ptr(out),
+                               _stream(stream)), "sv_lm_head_pack")
+    return out
+
+
+def lm_head_greedy_packed(hidden_states: torch.Tensor, packed: torch.Tensor, V: int,
+                          drafts: torch.Tensor, want_argmax: bool = True, out=None,
+                          workspace=None, stream=None):
+    """lm_head_greedy over a weight packed by lm_head_pack (V = the weight's row count)."""
+    _require(packed, "packed", hidden_states.dtype)
+    Hd = hidden_states.shape[-1]
+    n = c_sz()
+    _check(load().sv_lm_head_pack_bytes(V, Hd, ctypes.byref(n)), "sv_lm_head_pack_bytes")
+    if packed.numel() * packed.element_size() != n.value:
+        raise SvError(f"packed must hold {n.value} bytes for V={V}, hidden={Hd}")
+    return _lm_head(hidden_states, packed, V, drafts, want_argmax, out, workspace, stream, True)
+
+
 def lm_head_greedy(hidden_states: torch.Tensor, weight: torch.Tensor, drafts: torch.Tensor,
                    want_argmax: bool = True, out=None, workspace=None, stream=None):
     """LM head + greedy acceptance: hidden_states [B][K][hidden], weight [V][hidden] (bf16
     or fp16).  Returns (accept_len [B], out_tokens [B][K], argmax [B][K] or None)."""
-    _require(hidden_states, "hidden_states")
     _require(weight, "weight", hidden_states.dtype)
+    if weight.dim() != 2 or weight.shape[1] != hidden_states.shape[-1]:
+        raise SvError("weight must be [V][hidden]")
+    return _lm_head(hidden_states, weight, weight.shape[0], drafts, want_argmax, out, workspace,
+                    stream, False)
+
+
+def _lm_head(hidden_states, weight, V, drafts, want_argmax, out, workspace, stream, packed):
+    _require(hidden_states, "hidden_states")
     _require(drafts, "drafts", torch.int32)
     B, K, Hd = hidden_states.shape
-    V = weight.shape[0]
     if hidden_states.dtype not in (torch.bfloat16, torch.float16):
         raise SvError("LM head operands must be bfloat16 or float16")
-    if weight.shape[1] != Hd or tuple(drafts.shape) != (B, K - 1):
-        raise SvError("weight must be [V][hidden] and drafts [B][K-1]")
+    if tuple(drafts.shape) != (B, K - 1):
+        raise SvError("drafts must be [B][K-1]")
     lib = load()
     n = c_sz()
     _check(lib.sv_lm_head_greedy_workspace(B, K, V, Hd, ctypes.byref(n)),
@@ -324,10 +371,11 @@ def lm_head_greedy(hidden_states: torch.Tensor, weight: torch.Tensor, drafts: to
         _on_stream(stream, acc, toks, am)
     else:
         acc, toks, am = out
-    _check(lib.sv_lm_head_greedy(B, K, V, Hd, _DTYPES[hidden_states.dtype], _ptr(hidden_states),
-                                 _ptr(weight), _ptr(drafts), _ptr(acc), _ptr(toks), _ptr(am),
-                                 _ptr(workspace), workspace.numel(), _stream(stream)),
-           "sv_lm_head_greedy")
+    fn, name = ((lib.sv_lm_head_greedy_packed, "sv_lm_head_greedy_packed") if packed
+                else (lib.sv_lm_head_greedy, "sv_lm_head_greedy"))
+    _check(fn(B, K, V, Hd, _DTYPES[hidden_states.dtype], _ptr(hidden_states), _ptr(weight),
+              _ptr(drafts), _ptr(acc), _ptr(toks), _ptr(am), _ptr(workspace), workspace.numel(),
+              _stream(stream)), name)
     return acc, toks, am
 
 

@@ -317,14 +317,16 @@ sv_status sv_lm_head_greedy_workspace(int32_t B, int32_t K, int32_t V, int32_t h
   return ok();
 }
 
-sv_status sv_lm_head_greedy(int32_t B, int32_t K, int32_t V, int32_t hidden, sv_dtype dtype,
-                            const void* hidden_states, const void* weight,
-                            const int32_t* drafts, int32_t* accept_len, int32_t* out_tokens,
-                            int32_t* argmax, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+// dtype arrives as its raw bits: a C caller may pass any int, which is not a valid
+// sv_dtype value until checked.
+static sv_status lm_head_call(int32_t B, int32_t K, int32_t V, int32_t hidden, int32_t dtype,
+                              const void* hidden_states, const void* weight, bool packed,
+                              const int32_t* drafts, int32_t* accept_len, int32_t* out_tokens,
+                              int32_t* argmax, void* workspace, size_t workspace_bytes,
+                              void* stream, const char* what) {
   sv_status st = check_lm_head(B, K, V, hidden);
   if (st != SV_OK) return st;
-  if (!dtype_in(dtype_bits(&dtype), {SV_BF16, SV_F16}))
+  if (!dtype_in(dtype, {SV_BF16, SV_F16}))
     return fail(SV_ERR_UNSUPPORTED, "LM head operands must be SV_BF16 or SV_F16");
   if (!hidden_states || !weight || !accept_len || !out_tokens || (K > 1 && !drafts))
     return fail(SV_ERR_INVALID_ARG, "hidden_states, weight, drafts and outputs are required");
@@ -345,6 +347,7 @@ sv_status sv_lm_head_greedy(int32_t B, int32_t K, int32_t V, int32_t hidden, sv_
   p.M = M;
   p.V = V;
   p.Hd = hidden;
+  p.packed = packed ? 1 : 0;
   sv::GreedyParams w;
   memset(&w, 0, sizeof w);
   w.drafts = drafts;
@@ -357,8 +360,57 @@ sv_status sv_lm_head_greedy(int32_t B, int32_t K, int32_t V, int32_t hidden, sv_
   w.V = V;
   w.chunk = V;
   w.nchunk = 1;
-  return device_status(sv::launch_lm_head(p, w, dtype, static_cast<hipStream_t>(stream)),
-                       "sv_lm_head_greedy launch");
+  return device_status(sv::launch_lm_head(p, w, static_cast<sv_dtype>(dtype),
+                                               static_cast<hipStream_t>(stream)), what);
+}
+
+sv_status sv_lm_head_greedy(int32_t B, int32_t K, int32_t V, int32_t hidden, sv_dtype dtype,
+                            const void* hidden_states, const void* weight,
+                            const int32_t* drafts, int32_t* accept_len, int32_t* out_tokens,
+                            int32_t* argmax, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return lm_head_call(B, K, V, hidden, dtype_bits(&dtype), hidden_states, weight, false, drafts,
+                      accept_len, out_tokens, argmax, workspace, workspace_bytes, stream,
+                      "sv_lm_head_greedy launch");
+}
+
+static sv_status check_lm_head_pack(int32_t V, int32_t hidden) {
+  if (V < 1) return fail(SV_ERR_INVALID_ARG, "V must be >= 1 (got %d)", V);
+  if (hidden < 32 || hidden % 32 != 0 || hidden > (1 << 20))
+    return fail(SV_ERR_INVALID_ARG, "hidden must be a positive multiple of 32 (got %d)", hidden);
+  return SV_OK;
+}
+
+sv_status sv_lm_head_pack_bytes(int32_t V, int32_t hidden, size_t* bytes) {
+  sv_status st = check_lm_head_pack(V, hidden);
+  if (st != SV_OK) return st;
+  if (!bytes) return fail(SV_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = sv::lm_head_packed_elems(V, hidden) * 2;
+  return ok();
+}
+
+sv_status sv_lm_head_pack(int32_t V, int32_t hidden, sv_dtype dtype, const void* weight,
+                          void* packed, void* stream) {
+  sv_status st = check_lm_head_pack(V, hidden);
+  if (st != SV_OK) return st;
+  if (!dtype_in(dtype_bits(&dtype), {SV_BF16, SV_F16}))
+    return fail(SV_ERR_UNSUPPORTED, "LM head weights must be SV_BF16 or SV_F16");
+  if (!weight || !packed) return fail(SV_ERR_INVALID_ARG, "weight and packed are required");
+  if (!aligned16(weight) || !aligned16(packed))
+    return fail(SV_ERR_INVALID_ARG, "weight and packed must be 16-byte aligned");
+  return device_status(sv::launch_lm_head_pack(weight, packed, V, hidden,
+                                               static_cast<hipStream_t>(stream)),
+                       "sv_lm_head_pack launch");
+}
+
+sv_status sv_lm_head_greedy_packed(int32_t B, int32_t K, int32_t V, int32_t hidden,
+                                   sv_dtype dtype, const void* hidden_states,
+                                   const void* packed_weight, const int32_t* drafts,
+                                   int32_t* accept_len, int32_t* out_tokens, int32_t* argmax,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return lm_head_call(B, K, V, hidden, dtype_bits(&dtype), hidden_states, packed_weight, true,
+                      drafts, accept_len, out_tokens, argmax, workspace, workspace_bytes, stream,
+                      "sv_lm_head_greedy_packed launch");
 }
 
 // ---------------------------------------------------------------- sampling

@@ -45,15 +45,19 @@ hipError_t launch_greedy_walk(const GreedyParams& p, hipStream_t stream);   // w
 // ---------------------------------------------------------------- LM head + greedy
 struct LmHeadParams {
   const void* hidden;         // [M][Hd]
-  const void* weight;         // [V][Hd]
+  const void* weight;         // [V][Hd], or the packed tile layout when packed != 0
   unsigned long long* part;   // [M][nwg] per-workgroup argmax keys
   unsigned long long* keys;   // [M] row argmax keys (the walk's nchunk = 1)
   int32_t M, V, Hd;
   int32_t nwg;
+  int32_t packed;
 };
 
 int lm_head_workgroups(int V);
 size_t lm_head_workspace_bytes(int M, int V);
+size_t lm_head_packed_elems(int V, int Hd);   // ceil(V / 32) * 32 * Hd
+hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int Hd,
+                               hipStream_t stream);
 hipError_t launch_lm_head(const LmHeadParams& p, const GreedyParams& walk, sv_dtype dtype,
                           hipStream_t stream);
 

@@ -5,16 +5,27 @@
 //
 // Pass 1 (lm_head_argmax_kernel): each workgroup owns 128 vocabulary rows, 32 per wave
 // as two 16-row MFMA blocks (16x16x32 bf16/f16, fp32 accumulate).  The contraction
-// runs over Hd in 64-wide load steps (two MFMA steps): lane (j, g) of a wave loads 32
-// contiguous bytes of W row v0 + 16*blk + j, so the four lanes of a row read one whole
-// 128-byte line per step, and H the same way, straight into MFMA operand registers
-// through a register ring; no LDS staging, no barriers in the loop.  The weight is read
-// exactly once, so the pass is bound by HBM on it.  The epilogue turns every logit into
-// a packed key (orderable value bits << 32 | ~index), reduces each row over the wave's
-// 32 columns with shuffles and over the four waves through LDS, and stores one key per
-// (row, workgroup).
+// runs over Hd in 32-column chunks, one MFMA each: lane (j, g) of a wave holds columns
+// 32q + 8g .. 32q + 8g + 7 of W row v0 + 16*blk + j (and of H row j), loaded as 16 bytes
+// straight into MFMA operand registers through a register ring; no LDS staging, no
+// barriers in the loop.  The weight is read exactly once, so the pass is bound by HBM on
+// it.  W comes either as the plain [V][Hd] matrix (each load instruction reads 64 bytes
+// of 16 rows) or pre-packed by lm_head_pack_kernel into 1 KB tiles in exactly the order
+// the waves consume them, so every load instruction of a wave reads one contiguous
+// kilobyte; the packed stream is read with non-temporal loads.  The epilogue turns every
+// logit into a packed key (orderable value bits << 32 | ~index), reduces each row over
+// the wave's 32 columns with shuffles and over the four waves through LDS, and stores
+// one key per (row, workgroup).
 // Pass 2 (lm_head_reduce_kernel): one workgroup per row folds its keys into one.
 // Pass 3: the greedy walk of the chain rule over those keys.
+//
+// Packed layout: W is cut into tiles of 16 rows x 32 columns.  Tile (u, q, h) covers rows
+// 32u + 16h .. 32u + 16h + 15 and columns 32q .. 32q + 31; its 16-byte piece l = 16g + j
+// holds row 32u + 16h + j, columns 32q + 8g .. 32q + 8g + 7 (the operand of lane l).
+// Tiles are stored in the order u, then q, then h; rows at or past V are zero.  Size:
+// ceil(V / 32) * 32 * Hd elements.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -43,16 +54,16 @@ __device__ __forceinline__ f32x4v mfma16<TagF16>(u32x4 a, u32x4 b, f32x4v c) {
 
 // MT = row tiles of 16 (M <= 16*MT).  The MFMA contraction pairs element e of lane
 // (i, g) in A with element e of lane (j, g) in B, so any map of (g, e) to columns that
-// both operands share sums every column exactly once.  One load step covers 32*SUB
-// columns: lane (j, g) reads the 16*SUB contiguous bytes at columns 8*SUB*g .. of the
-// step, and its c-th 16-byte piece feeds MFMA c of the step.  With SUB = 2 the four lanes
-// of a row read one 128-byte line per step.
+// both operands share sums every column exactly once; here lane (., g) holds columns
+// 32q + 8g + e of chunk q in both.  One load step covers SUB chunks (MFMAs).
+// PACKED: W is in the tile layout above (unit u = the wave's 32 rows).
 // Kernels take the fields their first loads need as leading plain arguments (preloaded
 // into SGPRs), then the whole parameter block.
-template <class Tag, int MT, int SUB, int RING>
+template <class Tag, int MT, int SUB, int RING, bool PACKED>
 __global__ void __launch_bounds__(kThreads)
 lm_head_argmax_kernel(const void* hidden, const void* weight, int32_t M, int32_t V, int32_t Hd,
                       const LmHeadParams p) {
+  static_assert(kBlocks == 2, "the packed tile order assumes 32-row units of two blocks");
   __shared__ uint64_t red[kThreads / kWave][16 * MT];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -62,28 +73,38 @@ lm_head_argmax_kernel(const void* hidden, const void* weight, int32_t M, int32_t
   const uint16_t* H = static_cast<const uint16_t*>(hidden);
   // rows past V or M are clamped in bounds; their keys are never kept
   const uint16_t* wrow[kBlocks];
+  const u32x4* wunit = nullptr;
+  if constexpr (PACKED) {
+    const int unit = min(v0, V - 1) / kRowsPerWave;
+    wunit = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(unit) * kRowsPerWave * Hd) + lane;
+  } else {
 #pragma unroll
-  for (int nb = 0; nb < kBlocks; ++nb)
-    wrow[nb] = W + static_cast<size_t>(min(v0 + 16 * nb + l16, V - 1)) * Hd + 8 * SUB * g;
+    for (int nb = 0; nb < kBlocks; ++nb)
+      wrow[nb] = W + static_cast<size_t>(min(v0 + 16 * nb + l16, V - 1)) * Hd + 8 * g;
+  }
   const uint16_t* hrow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    hrow[mt] = H + static_cast<size_t>(min(16 * mt + l16, M - 1)) * Hd + 8 * SUB * g;
+    hrow[mt] = H + static_cast<size_t>(min(16 * mt + l16, M - 1)) * Hd + 8 * g;
 
   const int steps = Hd / (32 * SUB);
   struct St { u32x4 w[kBlocks][SUB]; u32x4 h[MT][SUB]; };
   auto load = [&](St& s, int st) {
-    const int k = min(st, steps - 1) * 32 * SUB;  // past the end: re-read the last step
+    const int q0 = min(st, steps - 1) * SUB;      // past the end: re-read the last step
 #pragma unroll
     for (int nb = 0; nb < kBlocks; ++nb)
 #pragma unroll
-      for (int c = 0; c < SUB; ++c)
-        s.w[nb][c] = *reinterpret_cast<const u32x4*>(wrow[nb] + k + 8 * c);
+      for (int c = 0; c < SUB; ++c) {
+        if constexpr (PACKED)
+          s.w[nb][c] = __builtin_nontemporal_load(wunit + ((q0 + c) * kBlocks + nb) * kWave);
+        else
+          s.w[nb][c] = *reinterpret_cast<const u32x4*>(wrow[nb] + 32 * (q0 + c));
+      }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int c = 0; c < SUB; ++c)
-        s.h[mt][c] = *reinterpret_cast<const u32x4*>(hrow[mt] + k + 8 * c);
+        s.h[mt][c] = *reinterpret_cast<const u32x4*>(hrow[mt] + 32 * (q0 + c));
   };
   f32x4v acc[MT][kBlocks];
 #pragma unroll
@@ -161,23 +182,42 @@ lm_head_reduce_kernel(const unsigned long long* part, int32_t M, int32_t nwg,
   }
 }
 
-// Up to 16 rows with a 64-column-multiple width: 128-byte row runs (one cache line per
-// row and step), 3-step ring (104 VGPRs, four waves per SIMD); otherwise single MFMA
-// steps through a 6-step ring.
-template <class Tag>
+// Copies W [V][Hd] into the packed tile layout, one 16-byte piece per thread and step;
+// pieces of rows at or past V are zero.
+__global__ void __launch_bounds__(kThreads)
+lm_head_pack_kernel(const u32x4* weight, u32x4* packed, int32_t V, int32_t Hd, int64_t pieces) {
+  const int nq = Hd / 32;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < pieces;
+       i += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int l = static_cast<int>(i & (kWave - 1));
+    const int64_t tile = i / kWave;
+    const int h = static_cast<int>(tile % kBlocks);
+    const int64_t uq = tile / kBlocks;
+    const int q = static_cast<int>(uq % nq);
+    const int64_t row = (uq / nq) * kRowsPerWave + 16 * h + (l & 15);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < V) v = weight[row * (Hd / 8) + 4 * q + (l >> 4)];
+    packed[i] = v;
+  }
+}
+
+// Up to 16 rows with a 64-column-multiple width: two chunks per load step (128 contiguous
+// bytes of a row, or 4 KB of the packed stream), 3-step ring (four waves per SIMD
+// unpacked, five packed); otherwise single MFMA steps through a 6-step ring.
+template <class Tag, bool PACKED>
 hipError_t launch_typed(const LmHeadParams& p, hipStream_t stream) {
   const dim3 grid(p.nwg), block(kThreads);
   if (p.M <= 16 && p.Hd % (32 * kSub) == 0)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, kSub, 3>), grid, block, 0, stream,
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, kSub, 3, PACKED>), grid, block, 0, stream,
                        p.hidden, p.weight, p.M, p.V, p.Hd, p);
   else if (p.M <= 16)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, 1, 6>), grid, block, 0, stream,
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, 1, 6, PACKED>), grid, block, 0, stream,
                        p.hidden, p.weight, p.M, p.V, p.Hd, p);
   else if (p.M <= 32)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 2, 1, 6>), grid, block, 0, stream,
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 2, 1, 6, PACKED>), grid, block, 0, stream,
                        p.hidden, p.weight, p.M, p.V, p.Hd, p);
   else
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 4, 1, 6>), grid, block, 0, stream,
+    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 4, 1, 6, PACKED>), grid, block, 0, stream,
                        p.hidden, p.weight, p.M, p.V, p.Hd, p);
   return hipGetLastError();
 }
@@ -193,9 +233,25 @@ size_t lm_head_workspace_bytes(int M, int V) {
   return (static_cast<size_t>(M) * lm_head_workgroups(V) + M) * sizeof(uint64_t);
 }
 
+size_t lm_head_packed_elems(int V, int Hd) {
+  return static_cast<size_t>((V + kRowsPerWave - 1) / kRowsPerWave) * kRowsPerWave * Hd;
+}
+
+hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int Hd,
+                               hipStream_t stream) {
+  const int64_t pieces = static_cast<int64_t>(lm_head_packed_elems(V, Hd)) / 8;
+  const int64_t blocks = std::min<int64_t>((pieces + kThreads - 1) / kThreads, 16384);
+  hipLaunchKernelGGL(lm_head_pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                     0, stream, static_cast<const u32x4*>(weight), static_cast<u32x4*>(packed),
+                     V, Hd, pieces);
+  return hipGetLastError();
+}
+
 hipError_t launch_lm_head(const LmHeadParams& p, const GreedyParams& walk, sv_dtype dtype,
                           hipStream_t stream) {
-  hipError_t e = dtype == SV_F16 ? launch_typed<TagF16>(p, stream) : launch_typed<TagBF16>(p, stream);
+  hipError_t e = p.packed
+      ? (dtype == SV_F16 ? launch_typed<TagF16, true>(p, stream) : launch_typed<TagBF16, true>(p, stream))
+      : (dtype == SV_F16 ? launch_typed<TagF16, false>(p, stream) : launch_typed<TagBF16, false>(p, stream));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lm_head_reduce_kernel, dim3(p.M), dim3(kThreads), 0, stream,
                      p.part, p.M, p.nwg, p);

@@ -20,6 +20,7 @@
  *   sv_accept_sample_tree  sampling verification of a draft tree (recursive rejection)
  *   sv_commit_tree       close a tree cycle: move the accepted path's K/V into place
  *   sv_lm_head_greedy    the target's LM head fused with greedy acceptance
+ *   sv_lm_head_pack, sv_lm_head_greedy_packed  the same over a weight packed once
  *
  * Conventions for every call
  *   - Array arguments are DEVICE pointers unless stated otherwise.  The caller
@@ -324,6 +325,31 @@ sv_status sv_lm_head_greedy(int32_t B, int32_t K, int32_t V, int32_t hidden, sv_
                             const int32_t* drafts, int32_t* accept_len, int32_t* out_tokens,
                             int32_t* argmax, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/* -------------------------------------------------------------------------------------
+ * The same LM head over a pre-packed weight.  The output embedding does not change
+ * between cycles, so it can be rearranged once, when it is loaded, into the order in
+ * which the argmax pass consumes it: every load instruction then reads one contiguous
+ * kilobyte and the stream is read with non-temporal loads.
+ * sv_lm_head_pack_bytes: the packed size, ceil(V / 32) * 32 * hidden * 2 bytes.
+ * sv_lm_head_pack: weight [V][hidden] (SV_BF16 or SV_F16) -> packed, in the tile layout:
+ *   tiles of 16 rows x 32 columns; tile (u, q, h) covers rows 32u + 16h .. 32u + 16h + 15
+ *   and columns 32q .. 32q + 31, its 16-byte piece 16g + j holding row 32u + 16h + j,
+ *   columns 32q + 8g .. 32q + 8g + 7; tiles stored in the order u, q, h; rows at or past V
+ *   are zero.  Both device pointers, 16-byte aligned, not overlapping; V >= 1, hidden a
+ *   positive multiple of 32.  Enqueued on stream; no workspace.
+ * sv_lm_head_greedy_packed: exactly sv_lm_head_greedy (same arguments, limits, workspace
+ *   and outputs, bit for bit) with packed_weight = the output of sv_lm_head_pack for the
+ *   same V, hidden and dtype in place of weight.
+ * ------------------------------------------------------------------------------------ */
+sv_status sv_lm_head_pack_bytes(int32_t V, int32_t hidden, size_t* bytes);
+sv_status sv_lm_head_pack(int32_t V, int32_t hidden, sv_dtype dtype, const void* weight,
+                          void* packed, void* stream);
+sv_status sv_lm_head_greedy_packed(int32_t B, int32_t K, int32_t V, int32_t hidden,
+                                   sv_dtype dtype, const void* hidden_states,
+                                   const void* packed_weight, const int32_t* drafts,
+                                   int32_t* accept_len, int32_t* out_tokens, int32_t* argmax,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

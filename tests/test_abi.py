@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert lib.sv_version() == 1
@@ -213,6 +213,32 @@ def test_lm_head_validation(lib):
     assert call(sv.SV_BF16, FAKE, FAKE, 8) == WORKSPACE
 
 
+def test_lm_head_pack_validation(lib):
+    """The packed size is ceil(V / 32) * 32 rows of hidden 2-byte elements; the pack and
+    the packed LM head reject bad shapes, dtypes and alignments on the host."""
+    n = ctypes.c_size_t()
+    assert lib.sv_lm_head_pack_bytes(152064, 3584, ctypes.byref(n)) == OK
+    assert n.value == 152064 * 3584 * 2
+    assert lib.sv_lm_head_pack_bytes(777, 96, ctypes.byref(n)) == OK and n.value == 800 * 96 * 2
+    assert lib.sv_lm_head_pack_bytes(1, 32, ctypes.byref(n)) == OK and n.value == 32 * 32 * 2
+    for V, Hd in [(0, 64), (10, 48), (10, 0), (-1, 64)]:
+        assert lib.sv_lm_head_pack_bytes(V, Hd, ctypes.byref(n)) == INVALID
+    assert lib.sv_lm_head_pack_bytes(10, 64, None) == INVALID
+    pack = lambda dt, w, out: lib.sv_lm_head_pack(100, 64, dt, w, out, None)
+    assert pack(sv.SV_F32, FAKE, FAKE) == UNSUPPORTED
+    assert pack(sv.SV_BF16, None, FAKE) == INVALID
+    assert pack(sv.SV_BF16, FAKE, None) == INVALID
+    assert pack(sv.SV_F16, ctypes.c_void_p(0x1008), FAKE) == INVALID
+    assert lib.sv_lm_head_pack(0, 64, sv.SV_BF16, FAKE, FAKE, None) == INVALID
+    call = lambda dt, h, ws, nbytes, B=1: lib.sv_lm_head_greedy_packed(
+        B, 16, 1000, 64, dt, h, FAKE, FAKE, FAKE, FAKE, None, ws, nbytes, None)
+    assert call(sv.SV_F32, FAKE, FAKE, 1 << 20) == UNSUPPORTED
+    assert call(sv.SV_BF16, None, FAKE, 1 << 20) == INVALID
+    assert call(sv.SV_BF16, ctypes.c_void_p(0x1008), FAKE, 1 << 20) == INVALID
+    assert call(sv.SV_BF16, FAKE, FAKE, 8) == WORKSPACE
+    assert call(sv.SV_BF16, FAKE, FAKE, 1 << 20, B=5) == INVALID    # B * K > 64
+
+
 def test_status_strings(lib):
     assert lib.sv_status_string(0) == b"ok"
     assert lib.sv_status_string(-3) == b"workspace too small"
@@ -260,6 +286,9 @@ def test_out_of_range_dtype_values(lib):
                                       None) == UNSUPPORTED
         assert lib.sv_lm_head_greedy(1, 4, 100, 64, bad, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                                      1 << 20, None) == UNSUPPORTED
+        assert lib.sv_lm_head_greedy_packed(1, 4, 100, 64, bad, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                            FAKE, 1 << 20, None) == UNSUPPORTED
+        assert lib.sv_lm_head_pack(100, 64, bad, FAKE, FAKE, None) == UNSUPPORTED
         d = _desc(dtype=bad)
         assert lib.sv_kv_append(ctypes.byref(d), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 None) == UNSUPPORTED

@@ -13,9 +13,16 @@ from gpu_helpers import i32, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _run(sv, li):
-    acc, toks, am = sv.lm_head_greedy(to_dev(li.hidden_states, li.dtype),
-                                      to_dev(li.weight, li.dtype), i32(li.drafts))
+def _call(sv, hs, w, drafts, packed):
+    """The plain call, or the same over the weight packed once by lm_head_pack."""
+    if packed:
+        return sv.lm_head_greedy_packed(hs, sv.lm_head_pack(w), w.shape[0], drafts)
+    return sv.lm_head_greedy(hs, w, drafts)
+
+
+def _run(sv, li, packed=False):
+    acc, toks, am = _call(sv, to_dev(li.hidden_states, li.dtype), to_dev(li.weight, li.dtype),
+                          i32(li.drafts), packed)
     torch.cuda.synchronize()
     r_acc, r_toks, r_am, _ = oracle.lm_head_greedy_ref(li.hidden_states, li.weight, li.drafts,
                                                        li.dtype)
@@ -25,11 +32,32 @@ def _run(sv, li):
     return r_acc
 
 
-def test_qwen7b_lm_head_full_size(gpu_lib):
+@pytest.mark.parametrize("packed", [False, True])
+def test_qwen7b_lm_head_full_size(gpu_lib, packed):
     li = W.make_workload_lm_head()
-    say(f"[lm head] qwen7b_lmhead B={li.B} K={li.K} hidden={li.hidden} V={li.V}")
-    r_acc = _run(gpu_lib, li)
+    say(f"[lm head] qwen7b_lmhead B={li.B} K={li.K} hidden={li.hidden} V={li.V} packed={packed}")
+    r_acc = _run(gpu_lib, li, packed)
     np.testing.assert_array_equal(r_acc, li.planted_len)
+
+
+@pytest.mark.parametrize("V,hidden,dtype", [(777, 96, "bf16"), (40, 64, "f16"), (1, 32, "bf16"),
+                                            (4096, 256, "bf16")])
+def test_pack_layout(gpu_lib, V, hidden, dtype):
+    """lm_head_pack against the tile layout written out with numpy: pad the rows to a
+    multiple of 32 with zeros, view W as [unit][half][row j][chunk q][group g][8] and
+    store it as [unit][q][half][g][j][8]; bit for bit."""
+    rng = np.random.default_rng([V, hidden])
+    w = rng.standard_normal((V, hidden)).astype(np.float32)
+    wd = torch.from_numpy(w).to("cuda").to(torch.bfloat16 if dtype == "bf16" else torch.float16)
+    say(f"[lm head pack] V={V} hidden={hidden} {dtype}")
+    packed = gpu_lib.lm_head_pack(wd)
+    torch.cuda.synchronize()
+    bits = wd.view(torch.int16).cpu().numpy()
+    U, Q = (V + 31) // 32, hidden // 32
+    pad = np.zeros((U * 32, hidden), dtype=np.int16)
+    pad[:V] = bits
+    want = pad.reshape(U, 2, 16, Q, 4, 8).transpose(0, 3, 1, 4, 2, 5).reshape(-1)
+    np.testing.assert_array_equal(packed.view(torch.int16).cpu().numpy(), want)
 
 
 @pytest.mark.parametrize("B,K,hidden,V,dtype", [
@@ -41,16 +69,18 @@ def test_qwen7b_lm_head_full_size(gpu_lib):
     (1, 4, 32, 1, "bf16"),           # one token, one step
     (5, 9, 1024, 40000, "f16"),
 ])
-def test_lm_head_shapes(gpu_lib, B, K, hidden, V, dtype):
+@pytest.mark.parametrize("packed", [False, True])
+def test_lm_head_shapes(gpu_lib, B, K, hidden, V, dtype, packed):
     rng = np.random.default_rng(B * 1000 + K * 10 + hidden + V)
     li = W.make_lm_head(rng, B=B, K=K, hidden=hidden, V=V, dtype=dtype)
-    say(f"[lm head] B={B} K={K} hidden={hidden} V={V} {dtype}")
-    r_acc = _run(gpu_lib, li)
+    say(f"[lm head] B={B} K={K} hidden={hidden} V={V} {dtype} packed={packed}")
+    r_acc = _run(gpu_lib, li, packed)
     if V > 1:
         np.testing.assert_array_equal(r_acc, li.planted_len)
 
 
-def test_lm_head_ties_take_the_lowest_index(gpu_lib):
+@pytest.mark.parametrize("packed", [False, True])
+def test_lm_head_ties_take_the_lowest_index(gpu_lib, packed):
     """A vocabulary row duplicated later, and one duplicated earlier: equal logits from
     identical rows, so the lower index must win on both sides."""
     rng = np.random.default_rng(77)
@@ -61,8 +91,8 @@ def test_lm_head_ties_take_the_lowest_index(gpu_lib):
     w[0] = w[t[1]]                    # earlier copy of row t1: token 0 wins
     li2 = W.LmHeadInputs(1, 6, 256, 2000, "bf16", li.hidden_states, w, li.drafts,
                          li.planted_len, li.planted_tok)
-    acc, toks, am = gpu_lib.lm_head_greedy(to_dev(li2.hidden_states, "bf16"),
-                                           to_dev(li2.weight, "bf16"), i32(li2.drafts))
+    acc, toks, am = _call(gpu_lib, to_dev(li2.hidden_states, "bf16"), to_dev(li2.weight, "bf16"),
+                          i32(li2.drafts), packed)
     torch.cuda.synchronize()
     r_acc, r_toks, r_am, _ = oracle.lm_head_greedy_ref(li2.hidden_states, w, li2.drafts, "bf16")
     np.testing.assert_array_equal(am.cpu().numpy(), r_am)
@@ -78,9 +108,13 @@ def _bound(li, rows_idx, cols):
     return li.hidden * 2.0 ** -24 * (h[rows_idx] * w).sum(axis=-1)
 
 
-@pytest.mark.parametrize("B,K,hidden,V", [(1, 16, 3584, 152064), (2, 8, 1024, 50000),
-                                          (4, 16, 256, 7000)])
-def test_lm_head_unsteered(gpu_lib, B, K, hidden, V):
+@pytest.mark.parametrize("B,K,hidden,V,packed", [(1, 16, 3584, 152064, False),
+                                                 (1, 16, 3584, 152064, True),
+                                                 (2, 8, 1024, 50000, False),
+                                                 (2, 8, 1024, 50000, True),
+                                                 (4, 16, 256, 7000, False),
+                                                 (4, 16, 256, 7000, True)])
+def test_lm_head_unsteered(gpu_lib, B, K, hidden, V, packed):
     """Natural logits: hidden states N(0, 1) against W ~ N(0, 0.02), nothing steered, so
     the top-2 gaps are whatever they are.  On every row whose float64 top-2 gap exceeds
     the sum of the two entries' fp32 accumulation bounds the argmax must match bit for
@@ -98,9 +132,9 @@ def test_lm_head_unsteered(gpu_lib, B, K, hidden, V):
         drafts[b, :L[b]] = t[b, :L[b]]
         if L[b] < K - 1:
             drafts[b, L[b]] = (t[b, L[b]] + 1) % V
-    say(f"[lm head] unsteered B={B} K={K} hidden={hidden} V={V}")
-    acc, toks, am = gpu_lib.lm_head_greedy(to_dev(li.hidden_states, "bf16"),
-                                           to_dev(li.weight, "bf16"), i32(drafts))
+    say(f"[lm head] unsteered B={B} K={K} hidden={hidden} V={V} packed={packed}")
+    acc, toks, am = _call(gpu_lib, to_dev(li.hidden_states, "bf16"), to_dev(li.weight, "bf16"),
+                          i32(drafts), packed)
     torch.cuda.synchronize()
     acc, toks, am = acc.cpu().numpy(), toks.cpu().numpy(), am.cpu().numpy()
     r_acc, r_toks, r_am, _ = oracle.lm_head_greedy_ref(li.hidden_states, li.weight, drafts,

@@ -140,12 +140,13 @@ def hbm_probe(torch, dev, single_bytes, copies, reps):
     the chip's sustained read rate; (2) one launch over `single_bytes`, rotating over
     `copies` buffers (more than twice the last-level cache), timed exactly as the
     attention pass is (back-to-back launches between HIP events on the launch stream).
-    Each figure is the best over a few workgroup sizes."""
+    Each figure is the best over a few workgroup sizes and both load kinds (ordinary and
+    non-temporal)."""
     import block_verify_sv_amd as sv
     lib = ctypes.CDLL(os.path.join(os.path.dirname(sv.LIB_PATH), "libsvprobe.so"))
     lib.sv_probe_read.restype = ctypes.c_int
     lib.sv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
-                                  ctypes.c_void_p, ctypes.c_void_p]
+                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.sv_probe_workgroups.restype = ctypes.c_uint64
     lib.sv_probe_workgroups.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
     big = 2 << 30
@@ -157,8 +158,8 @@ def hbm_probe(torch, dev, single_bytes, copies, reps):
     stream = torch.cuda.Stream(device=dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
 
-    def launch(buf, nbytes, wg):
-        st = lib.sv_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, wg,
+    def launch(buf, nbytes, wg, nt):
+        st = lib.sv_probe_read(ctypes.c_void_p(buf.data_ptr()), nbytes, wg, nt,
                                ctypes.c_void_p(sink.data_ptr()), sp)
         if st:
             raise RuntimeError(f"sv_probe_read failed ({st})")
@@ -177,23 +178,28 @@ def hbm_probe(torch, dev, single_bytes, copies, reps):
         return e0.elapsed_time(e1) * 1000.0 / n
 
     big_rows, single_rows = {}, {}
-    for wg in PROBE_WG_BYTES:
-        us = timed(lambda i: launch(big_buf, big, wg), 10)
-        big_rows[wg] = big / (us * 1e-6) / 1e9
-        us = timed(lambda i: launch(bufs[i % copies], single_bytes, wg), reps)
-        single_rows[wg] = (us, single_bytes / (us * 1e-6) / 1e9)
+    for nt in (0, 1):
+        for wg in PROBE_WG_BYTES:
+            us = timed(lambda i: launch(big_buf, big, wg, nt), 10)
+            big_rows[(wg, nt)] = big / (us * 1e-6) / 1e9
+            us = timed(lambda i: launch(bufs[i % copies], single_bytes, wg, nt), reps)
+            single_rows[(wg, nt)] = (us, single_bytes / (us * 1e-6) / 1e9)
     best_big = max(big_rows, key=big_rows.get)
     best_single = min(single_rows, key=lambda w: single_rows[w][0])
     del big_buf, bufs, sink
     torch.cuda.empty_cache()
+    kind = ("ordinary", "non-temporal")
     return {"kernel": "hbm_read_kernel (libsvprobe.so, hand-written HIP)",
-            "read_2GiB_GBps": big_rows[best_big], "read_2GiB_wg_bytes": best_big,
+            "read_2GiB_GBps": big_rows[best_big], "read_2GiB_wg_bytes": best_big[0],
+            "read_2GiB_loads": kind[best_big[1]],
             "single_launch_bytes": single_bytes,
             "single_launch_us": single_rows[best_single][0],
             "single_launch_GBps": single_rows[best_single][1],
-            "single_launch_wg_bytes": best_single,
-            "sweep_GBps": {str(w): [round(big_rows[w], 1), round(single_rows[w][1], 1)]
-                           for w in PROBE_WG_BYTES}}
+            "single_launch_wg_bytes": best_single[0],
+            "single_launch_loads": kind[best_single[1]],
+            "sweep_GBps": {f"{w}{'/nt' if nt else ''}": [round(big_rows[(w, nt)], 1),
+                                                        round(single_rows[(w, nt)][1], 1)]
+                           for (w, nt) in big_rows}}
 
 
 # ------------------------------------------------------------------ further rows

@@ -343,7 +343,6 @@ static sv_status lm_head_call(int32_t B, int32_t K, int32_t V, int32_t hidden, i
   p.weight = weight;
   p.nwg = sv::lm_head_workgroups(V);
   p.part = static_cast<unsigned long long*>(workspace);
-  p.keys = p.part + static_cast<size_t>(M) * p.nwg;
   p.M = M;
   p.V = V;
   p.Hd = hidden;
@@ -354,14 +353,11 @@ static sv_status lm_head_call(int32_t B, int32_t K, int32_t V, int32_t hidden, i
   w.accept_len = accept_len;
   w.out_tokens = out_tokens;
   w.argmax = argmax;
-  w.keys = p.keys;
   w.B = B;
   w.K = K;
   w.V = V;
-  w.chunk = V;
-  w.nchunk = 1;
   return device_status(sv::launch_lm_head(p, w, static_cast<sv_dtype>(dtype),
-                                               static_cast<hipStream_t>(stream)), what);
+                                          static_cast<hipStream_t>(stream)), what);
 }
 
 sv_status sv_lm_head_greedy(int32_t B, int32_t K, int32_t V, int32_t hidden, sv_dtype dtype,

@@ -10,6 +10,8 @@
 // `kLoads * kThreads * 16` bytes, so each stretch is a run of whole DRAM pages.  The
 // loaded words are folded into an XOR that is written only if it equals a value the
 // data never produces, which keeps every load alive without adding write traffic.
+// The loads are either ordinary or non-temporal (streaming); the faster of the two is
+// the ceiling.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -21,6 +23,7 @@ constexpr int kThreads = 256;
 constexpr int kLoads = 8;
 constexpr uint32_t kNever = 0x9E3779B9u;
 
+template <bool NT>
 __global__ void __launch_bounds__(kThreads)
 hbm_read_kernel(const u32x4* src, uint64_t n16, uint64_t per_wg, u32x4* sink) {
   const uint64_t begin = static_cast<uint64_t>(blockIdx.x) * per_wg;
@@ -33,7 +36,11 @@ hbm_read_kernel(const u32x4* src, uint64_t n16, uint64_t per_wg, u32x4* sink) {
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
       const uint64_t i = r + static_cast<uint64_t>(u) * kThreads + threadIdx.x;
-      v[u] = src[i < end ? i : end - 1];           // clamped: in bounds, counted once below
+      const u32x4* a = src + (i < end ? i : end - 1);  // clamped: in bounds, counted once below
+      if constexpr (NT)
+        v[u] = __builtin_nontemporal_load(a);
+      else
+        v[u] = *a;
     }
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
@@ -57,18 +64,23 @@ uint64_t sv_probe_workgroups(uint64_t bytes, uint64_t wg_bytes) {
 // Reads `bytes` (a multiple of 16) at `src` (16-byte aligned) once, in one launch of
 // ceil(bytes / wg_bytes) workgroups of 256 threads.  `sink` must hold
 // 16 * 256 * sv_probe_workgroups(bytes, wg_bytes) bytes; it is written only in the
-// (never occurring) case described above.  Returns 0, or -1 for invalid arguments, or
-// the HIP error code of the launch.
-int sv_probe_read(const void* src, uint64_t bytes, uint64_t wg_bytes, void* sink,
-                  void* stream) {
+// (never occurring) case described above.  nontemporal != 0 reads with non-temporal
+// loads.  Returns 0, or -1 for invalid arguments, or the HIP error code of the launch.
+int sv_probe_read(const void* src, uint64_t bytes, uint64_t wg_bytes, int nontemporal,
+                  void* sink, void* stream) {
   if (!src || !sink || bytes == 0 || (bytes & 15u) || (reinterpret_cast<uintptr_t>(src) & 15u))
     return -1;
   if (wg_bytes < 16 || (wg_bytes & 15u)) return -1;
   const uint64_t grid = sv_probe_workgroups(bytes, wg_bytes);
   if (grid > 0x7FFFFFFFull) return -1;
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src), bytes / 16,
-                     wg_bytes / 16, static_cast<u32x4*>(sink));
+  if (nontemporal)
+    hipLaunchKernelGGL(hbm_read_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       0, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                       bytes / 16, wg_bytes / 16, static_cast<u32x4*>(sink));
+  else
+    hipLaunchKernelGGL(hbm_read_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                       0, static_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                       bytes / 16, wg_bytes / 16, static_cast<u32x4*>(sink));
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? 0 : static_cast<int>(e);
 }

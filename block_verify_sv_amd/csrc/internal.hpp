@@ -47,7 +47,6 @@ struct LmHeadParams {
   const void* hidden;         // [M][Hd]
   const void* weight;         // [V][Hd], or the packed tile layout when packed != 0
   unsigned long long* part;   // [M][nwg] per-workgroup argmax keys
-  unsigned long long* keys;   // [M] row argmax keys (the walk's nchunk = 1)
   int32_t M, V, Hd;
   int32_t nwg;
   int32_t packed;

@@ -16,8 +16,8 @@
 // logit into a packed key (orderable value bits << 32 | ~index), reduces each row over
 // the wave's 32 columns with shuffles and over the four waves through LDS, and stores
 // one key per (row, workgroup).
-// Pass 2 (lm_head_reduce_kernel): one workgroup per row folds its keys into one.
-// Pass 3: the greedy walk of the chain rule over those keys.
+// Pass 2 (lm_head_finish_kernel): one workgroup per sequence folds each row's keys into
+// its greedy token and walks the chain rule over them.
 //
 // Packed layout: W is cut into tiles of 16 rows x 32 columns.  Tile (u, q, h) covers rows
 // 32u + 16h .. 32u + 16h + 15 and columns 32q .. 32q + 31; its 16-byte piece l = 16g + j
@@ -164,22 +164,45 @@ lm_head_argmax_kernel(const void* hidden, const void* weight, int32_t M, int32_t
   }
 }
 
-// One workgroup per row: the maximum of the row's per-workgroup keys.
-__global__ void __launch_bounds__(kThreads)
-lm_head_reduce_kernel(const unsigned long long* part, int32_t M, int32_t nwg,
-                      const LmHeadParams p) {
-  __shared__ uint64_t red[kThreads / kWave];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const unsigned long long* src = part + static_cast<size_t>(row) * nwg;
-  uint64_t best = 0;
-  for (int i = tid; i < nwg; i += kThreads) best = src[i] > best ? static_cast<uint64_t>(src[i]) : best;
-  best = wave_max_u64(best);
-  if ((tid & 63) == 0) red[tid >> 6] = best;
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < kThreads / kWave; ++w) best = red[w] > best ? red[w] : best;
-    p.keys[row] = best;                           // wave 0's maximum is already in best
+// One workgroup of 16 waves per sequence: wave w folds the per-workgroup keys of rows
+// w, w + 16, ... of the sequence (20 loads per lane in flight, clamped indexes; a
+// repeated key changes no maximum) into the row's greedy token, then wave 0 applies the
+// chain rule to the K tokens: drafts are accepted while they equal the previous row's
+// token, and the first row that disagrees (or the last row) gives the correction.
+constexpr int kFinishThreads = 1024;
+constexpr int kFinishLoads = 20;
+
+__global__ void __launch_bounds__(kFinishThreads)
+lm_head_finish_kernel(const unsigned long long* part, int32_t K, int32_t nwg,
+                      const GreedyParams p) {
+  __shared__ int32_t tok[64];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = wave; r < K; r += kFinishThreads / kWave) {
+    const unsigned long long* src = part + (static_cast<size_t>(b) * K + r) * nwg;
+    uint64_t best = 0;
+    for (int base = 0; base < nwg; base += kFinishLoads * kWave) {
+      uint64_t k[kFinishLoads];
+#pragma unroll
+      for (int u = 0; u < kFinishLoads; ++u) k[u] = src[min(base + u * kWave + lane, nwg - 1)];
+#pragma unroll
+      for (int u = 0; u < kFinishLoads; ++u) best = k[u] > best ? k[u] : best;
+    }
+    best = wave_max_u64(best);
+    if (lane == 0) tok[r] = static_cast<int32_t>(argmax_key_index(best));
   }
+  __syncthreads();
+  if (wave != 0) return;
+  const bool in = lane < K;
+  const int32_t t = in ? tok[lane] : -1;
+  if (in && p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
+  // draft k+1 (drafts[b][k]) is checked against row k's token, k = 0 .. K-2
+  const int32_t d = lane < K - 1 ? p.drafts[static_cast<size_t>(b) * (K - 1) + lane] : 0;
+  const uint64_t miss = __ballot(lane < K - 1 && d != t);
+  const int a = miss ? __builtin_ctzll(miss) : K - 1;   // accepted drafts
+  const int32_t corr = __shfl(t, a);
+  if (in) p.out_tokens[static_cast<size_t>(b) * K + lane] = lane < a ? d : (lane == a ? corr : -1);
+  if (lane == 0) p.accept_len[b] = a;
 }
 
 // Copies W [V][Hd] into the packed tile layout, one 16-byte piece per thread and step;
@@ -230,7 +253,7 @@ int lm_head_workgroups(int V) {
 }
 
 size_t lm_head_workspace_bytes(int M, int V) {
-  return (static_cast<size_t>(M) * lm_head_workgroups(V) + M) * sizeof(uint64_t);
+  return static_cast<size_t>(M) * lm_head_workgroups(V) * sizeof(uint64_t);
 }
 
 size_t lm_head_packed_elems(int V, int Hd) {
@@ -253,11 +276,9 @@ hipError_t launch_lm_head(const LmHeadParams& p, const GreedyParams& walk, sv_dt
       ? (dtype == SV_F16 ? launch_typed<TagF16, true>(p, stream) : launch_typed<TagBF16, true>(p, stream))
       : (dtype == SV_F16 ? launch_typed<TagF16, false>(p, stream) : launch_typed<TagBF16, false>(p, stream));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lm_head_reduce_kernel, dim3(p.M), dim3(kThreads), 0, stream,
-                     p.part, p.M, p.nwg, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_greedy_walk(walk, stream);
+  hipLaunchKernelGGL(lm_head_finish_kernel, dim3(walk.B), dim3(kFinishThreads), 0, stream,
+                     p.part, walk.K, p.nwg, walk);
+  return hipGetLastError();
 }
 
 }  // namespace sv

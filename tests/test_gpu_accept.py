@@ -87,6 +87,56 @@ def test_greedy_workspace_reuse(gpu_lib):
             assert_greedy(gpu_lib, g.logits, g.drafts, "bf16", f"reuse{i}")
 
 
+def test_greedy_workspace_garbage_and_graph_replays(gpu_lib):
+    """The workspace needs no initial contents: calls on a workspace filled with 0xFF bytes,
+    with random bytes and with zeros match the oracle.  One call captured in a HIP graph
+    and replayed five times, with new logits copied in eagerly between replays, matches
+    the oracle on every replay."""
+    import ctypes
+    B, K, V = 3, 16, 50000
+    n = ctypes.c_size_t()
+    assert gpu_lib.load().sv_accept_greedy_workspace(B, K, V, ctypes.byref(n)) == 0
+    gs = [W.make_greedy(np.random.default_rng(900 + i), B=B, K=K, V=V, dtype="bf16")
+          for i in range(6)]
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    fills = [torch.full((n.value,), 0xFF, dtype=torch.uint8),
+             torch.randint(0, 256, (n.value,), dtype=torch.uint8, generator=gen),
+             torch.zeros(n.value, dtype=torch.uint8)]
+    for i, fill in enumerate(fills):
+        say(f"[greedy] workspace fill {i}")
+        ws = fill.cuda()
+        acc, toks, am = gpu_lib.accept_greedy(to_dev(gs[i].logits, "bf16"), i32(gs[i].drafts),
+                                              workspace=ws)
+        torch.cuda.synchronize()
+        r_acc, r_toks, r_am = oracle.accept_greedy_ref(gs[i].logits, gs[i].drafts, "bf16")
+        np.testing.assert_array_equal(am.cpu().numpy(), r_am)
+        np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+        np.testing.assert_array_equal(toks.cpu().numpy(), r_toks)
+    say("[greedy] graph replays")
+    logits = to_dev(gs[0].logits, "bf16")
+    drafts = i32(gs[0].drafts)
+    ws = torch.full((n.value,), 0xA5, dtype=torch.uint8, device="cuda")
+    outs = (torch.empty(B, dtype=torch.int32, device="cuda"),
+            torch.empty(B, K, dtype=torch.int32, device="cuda"),
+            torch.empty(B, K, dtype=torch.int32, device="cuda"))
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        gpu_lib.accept_greedy(logits, drafts, out=outs, workspace=ws, stream=st)
+    for r in range(5):
+        g = gs[1 + r]
+        logits.copy_(to_dev(g.logits, "bf16"))
+        drafts.copy_(i32(g.drafts))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        r_acc, r_toks, r_am = oracle.accept_greedy_ref(g.logits, g.drafts, "bf16")
+        np.testing.assert_array_equal(outs[2].cpu().numpy(), r_am, err_msg=f"replay {r}")
+        np.testing.assert_array_equal(outs[0].cpu().numpy(), r_acc, err_msg=f"replay {r}")
+        np.testing.assert_array_equal(outs[1].cpu().numpy(), r_toks, err_msg=f"replay {r}")
+
+
 # ------------------------------------------------------------------------- sampling
 def sample_gpu(sv, s):
     acc, toks = sv.accept_sample(to_dev(s.target_logits, s.dtype), to_dev(s.draft_logits, s.dtype),

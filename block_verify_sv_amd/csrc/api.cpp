@@ -341,7 +341,7 @@ static sv_status lm_head_call(int32_t B, int32_t K, int32_t V, int32_t hidden, i
   sv::LmHeadParams p;
   p.hidden = hidden_states;
   p.weight = weight;
-  p.nwg = sv::lm_head_workgroups(V);
+  p.nwg = 0;
   p.part = static_cast<unsigned long long*>(workspace);
   p.M = M;
   p.V = V;

@@ -48,11 +48,10 @@ struct LmHeadParams {
   const void* weight;         // [V][Hd], or the packed tile layout when packed != 0
   unsigned long long* part;   // [M][nwg] per-workgroup argmax keys
   int32_t M, V, Hd;
-  int32_t nwg;
+  int32_t nwg;                // argmax workgroups (chosen at launch)
   int32_t packed;
 };
 
-int lm_head_workgroups(int V);
 size_t lm_head_workspace_bytes(int M, int V);
 size_t lm_head_packed_elems(int V, int Hd);   // ceil(V / 32) * 32 * Hd
 hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int Hd,

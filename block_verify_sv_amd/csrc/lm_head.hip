@@ -3,8 +3,10 @@
 // reduced to each row's argmax without ever storing a logit, then the chain rule (the
 // verify forward's last step before the acceptance of the VFlash-FM cycle figure).
 //
-// Pass 1 (lm_head_argmax_kernel): each workgroup owns 128 vocabulary rows, 32 per wave
-// as two 16-row MFMA blocks (16x16x32 bf16/f16, fp32 accumulate).  The contraction
+// Pass 1 (lm_head_argmax_kernel): the vocabulary's 32-row units are shared out evenly
+// over the workgroups, up to four each, one per wave as two 16-row MFMA blocks
+// (16x16x32 bf16/f16, fp32 accumulate); the grid is sized to the chip's resident
+// workgroups so that every CU streams about the same bytes.  The contraction
 // runs over Hd in 32-column chunks, one MFMA each: lane (j, g) of a wave holds columns
 // 32q + 8g .. 32q + 8g + 7 of W row v0 + 16*blk + j (and of H row j), loaded as 16 bytes
 // straight into MFMA operand registers through a register ring; no LDS staging, no
@@ -36,6 +38,8 @@ constexpr int kThreads = 256;
 constexpr int kBlocks = 2;                        // 16-row MFMA blocks per wave
 constexpr int kRowsPerWave = 16 * kBlocks;
 constexpr int kSub = 2;                           // MFMA steps per load step (when Hd allows)
+constexpr int kUnitsPerWG = kThreads / kWave;     // 32-row units per workgroup, at most
+constexpr int kMaxResidentPerCU = 8;              // workgroups of four waves per CU, at most
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -68,15 +72,21 @@ lm_head_argmax_kernel(const void* hidden, const void* weight, int32_t M, int32_t
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int v0 = blockIdx.x * (kThreads / kWave) * kRowsPerWave + wave * kRowsPerWave;
+  // 32-row units shared out evenly: workgroup w takes units [w*U/nwg, (w+1)*U/nwg) (at
+  // most four, one per wave); a wave without a unit loads nothing and keeps no key
+  const int units = (V + kRowsPerWave - 1) / kRowsPerWave;
+  const int ub = static_cast<int>(static_cast<int64_t>(blockIdx.x) * units / p.nwg);
+  const int ue = static_cast<int>(static_cast<int64_t>(blockIdx.x + 1) * units / p.nwg);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);   // uniform: kept in scalar registers
+  const bool live = ub + wv < ue;
+  const int v0 = min(ub + wv, units - 1) * kRowsPerWave;
   const uint16_t* W = static_cast<const uint16_t*>(weight);
   const uint16_t* H = static_cast<const uint16_t*>(hidden);
   // rows past V or M are clamped in bounds; their keys are never kept
   const uint16_t* wrow[kBlocks];
   const u32x4* wunit = nullptr;
   if constexpr (PACKED) {
-    const int unit = min(v0, V - 1) / kRowsPerWave;
-    wunit = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(unit) * kRowsPerWave * Hd) + lane;
+    wunit = reinterpret_cast<const u32x4*>(W + static_cast<size_t>(v0) * Hd) + lane;
   } else {
 #pragma unroll
     for (int nb = 0; nb < kBlocks; ++nb)
@@ -117,6 +127,7 @@ lm_head_argmax_kernel(const void* hidden, const void* weight, int32_t M, int32_t
   // counts of every path into the loop head, and a reordered prologue or an exit from
   // the middle of a group would make it drain the ring once per group.
   St ring[RING];
+  if (live) {
 #pragma unroll
   for (int u = 0; u < RING - 1; ++u) {
     load(ring[u], u);
@@ -138,6 +149,7 @@ lm_head_argmax_kernel(const void* hidden, const void* weight, int32_t M, int32_t
       }
     }
   }
+  }
 
   // epilogue: lane (j, g) holds logit (row 16mt + 4g + r, column v0 + 16nb + j)
 #pragma unroll
@@ -148,7 +160,7 @@ lm_head_argmax_kernel(const void* hidden, const void* weight, int32_t M, int32_t
 #pragma unroll
       for (int nb = 0; nb < kBlocks; ++nb) {
         const int v = v0 + 16 * nb + l16;
-        const uint64_t key = v < V ? argmax_key(acc[mt][nb][r], static_cast<uint32_t>(v)) : 0;
+        const uint64_t key = live && v < V ? argmax_key(acc[mt][nb][r], static_cast<uint32_t>(v)) : 0;
         best = key > best ? key : best;
       }
       best = group_max_u64<4>(best);               // over the 16 columns of the lane group
@@ -227,33 +239,53 @@ lm_head_pack_kernel(const u32x4* weight, u32x4* packed, int32_t V, int32_t Hd, i
 // Up to 16 rows with a 64-column-multiple width: two chunks per load step (128 contiguous
 // bytes of a row, or 4 KB of the packed stream), 3-step ring (four waves per SIMD
 // unpacked, five packed); otherwise single MFMA steps through a 6-step ring.
-template <class Tag, bool PACKED>
-hipError_t launch_typed(const LmHeadParams& p, hipStream_t stream) {
-  const dim3 grid(p.nwg), block(kThreads);
-  if (p.M <= 16 && p.Hd % (32 * kSub) == 0)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, kSub, 3, PACKED>), grid, block, 0, stream,
-                       p.hidden, p.weight, p.M, p.V, p.Hd, p);
-  else if (p.M <= 16)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 1, 1, 6, PACKED>), grid, block, 0, stream,
-                       p.hidden, p.weight, p.M, p.V, p.Hd, p);
-  else if (p.M <= 32)
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 2, 1, 6, PACKED>), grid, block, 0, stream,
-                       p.hidden, p.weight, p.M, p.V, p.Hd, p);
-  else
-    hipLaunchKernelGGL((lm_head_argmax_kernel<Tag, 4, 1, 6, PACKED>), grid, block, 0, stream,
-                       p.hidden, p.weight, p.M, p.V, p.Hd, p);
+// Workgroups for the vocabulary's U units of 32 rows, given how many the chip keeps
+// resident (a multiple of the CU count).  Units are shared out evenly over the grid, four
+// per workgroup at most.  When the grid fits in one resident round it is rounded up to a
+// whole number of workgroups per CU, so that every CU streams about U / 256 units
+// (measured: 152,064 rows 167.9 -> 164.9 us, 100,000 rows 128.0 -> 118.5 us); a larger
+// grid keeps four units per workgroup (whole resident rounds of fewer units measured
+// slower).
+int argmax_workgroups(int V, int resident) {
+  const int units = (V + kRowsPerWave - 1) / kRowsPerWave;
+  const int need = (units + kUnitsPerWG - 1) / kUnitsPerWG;
+  if (need <= resident) return std::min(units, (need + kNumCUs - 1) / kNumCUs * kNumCUs);
+  return need;
+}
+
+template <auto Kernel>
+hipError_t launch_argmax(LmHeadParams& p, hipStream_t stream) {
+  static int resident = 0;   // workgroups resident on the chip: occupancy query, once per kernel
+  if (resident == 0) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, kThreads, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    resident = std::min(per_cu, kMaxResidentPerCU) * kNumCUs;
+  }
+  p.nwg = argmax_workgroups(p.V, resident);
+  hipLaunchKernelGGL(Kernel, dim3(p.nwg), dim3(kThreads), 0, stream, p.hidden, p.weight, p.M,
+                     p.V, p.Hd, p);
   return hipGetLastError();
+}
+
+template <class Tag, bool PACKED>
+hipError_t launch_typed(LmHeadParams& p, hipStream_t stream) {
+  if (p.M <= 16 && p.Hd % (32 * kSub) == 0)
+    return launch_argmax<lm_head_argmax_kernel<Tag, 1, kSub, 3, PACKED>>(p, stream);
+  if (p.M <= 16) return launch_argmax<lm_head_argmax_kernel<Tag, 1, 1, 6, PACKED>>(p, stream);
+  if (p.M <= 32) return launch_argmax<lm_head_argmax_kernel<Tag, 2, 1, 6, PACKED>>(p, stream);
+  return launch_argmax<lm_head_argmax_kernel<Tag, 4, 1, 6, PACKED>>(p, stream);
 }
 
 }  // namespace
 
-int lm_head_workgroups(int V) {
-  const int per = (kThreads / kWave) * kRowsPerWave;
-  return (V + per - 1) / per;
-}
-
 size_t lm_head_workspace_bytes(int M, int V) {
-  return static_cast<size_t>(M) * lm_head_workgroups(V) * sizeof(uint64_t);
+  // one key per (row, workgroup), for the largest grid argmax_workgroups can choose
+  const int units = (V + kRowsPerWave - 1) / kRowsPerWave;
+  const int most = std::max((units + kUnitsPerWG - 1) / kUnitsPerWG,
+                            std::min(units, kMaxResidentPerCU * kNumCUs));
+  return static_cast<size_t>(M) * most * sizeof(uint64_t);
 }
 
 size_t lm_head_packed_elems(int V, int Hd) {
@@ -270,8 +302,9 @@ hipError_t launch_lm_head_pack(const void* weight, void* packed, int V, int Hd,
   return hipGetLastError();
 }
 
-hipError_t launch_lm_head(const LmHeadParams& p, const GreedyParams& walk, sv_dtype dtype,
+hipError_t launch_lm_head(const LmHeadParams& params, const GreedyParams& walk, sv_dtype dtype,
                           hipStream_t stream) {
+  LmHeadParams p = params;                        // nwg is set by the argmax launch
   hipError_t e = p.packed
       ? (dtype == SV_F16 ? launch_typed<TagF16, true>(p, stream) : launch_typed<TagBF16, true>(p, stream))
       : (dtype == SV_F16 ? launch_typed<TagF16, false>(p, stream) : launch_typed<TagBF16, false>(p, stream));

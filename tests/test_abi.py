@@ -201,7 +201,9 @@ def test_tree_validation(lib):
 def test_lm_head_validation(lib):
     n = ctypes.c_size_t()
     assert lib.sv_lm_head_greedy_workspace(1, 16, 152064, 3584, ctypes.byref(n)) == OK
-    assert n.value == 16 * 1188 * 8            # one key per (row, 128-row workgroup)
+    # one key per (row, argmax workgroup), sized for the largest grid: 2,048 workgroups
+    # (eight per CU) over the 4,752 units of 32 rows
+    assert n.value == 16 * 2048 * 8
     for B, K, V, Hd in [(5, 16, 10, 64), (1, 16, 10, 48), (1, 16, 10, 0), (1, 0, 10, 64),
                         (1, 16, 0, 64)]:
         assert lib.sv_lm_head_greedy_workspace(B, K, V, Hd, ctypes.byref(n)) == INVALID

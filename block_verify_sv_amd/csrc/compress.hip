@@ -8,10 +8,12 @@
 // and turns the scores into fp16 weights exp(s - max) and their fp32 sum (of the
 // rounded weights).
 // Pass 3 (out_kernel): grid (D/128 tile, b).  The workgroup streams F_b in 32-row tiles
-// through a register ring (several tiles in flight, each with its weight operands read
-// from the cache-resident workspace) into LDS as loaded; the contraction runs over the
-// feature rows, so each MFMA operand (8 consecutive rows of one column) comes from two
-// LDS transpose reads.  out = W . F_b / rowsum accumulates on MFMA.
+// (with the 256-column tile, non-temporal loads: this is the features' last use in the
+// call, while pass 1 reads them with ordinary loads so that this pass finds them in the
+// Infinity Cache) through a register ring (several tiles in flight, each with its weight
+// operands read from the cache-resident workspace) into LDS as loaded; the contraction
+// runs over the feature rows, so each MFMA operand (8 consecutive rows of one column)
+// comes from two LDS transpose reads.  out = W . F_b / rowsum accumulates on MFMA.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -228,7 +230,11 @@ out_kernel(const void* feats, const uint16_t* weights, const float* rowsum, cons
     for (int u = 0; u < CPT; ++u) {
       const int ch = tid + kThreads * u;
       const int r = min(nt + ch / CPR, N - 1);
-      f.v[u] = *reinterpret_cast<const u32x4*>(fb + static_cast<size_t>(r) * D + dbase + (ch % CPR) * 8);
+      const u32x4* src = reinterpret_cast<const u32x4*>(fb + static_cast<size_t>(r) * D + dbase + (ch % CPR) * 8);
+      if constexpr (DT == 256)
+        f.v[u] = __builtin_nontemporal_load(src);   // long streams: measured 82.0 -> 80.7 us
+      else
+        f.v[u] = *src;                             // (36, 324): ordinary loads measured faster
     }
 #pragma unroll
     for (int ks = 0; ks < kNT / 16; ++ks) f.a[ks] = *reinterpret_cast<const u32x4*>(wsrc + nt + ks * 16);

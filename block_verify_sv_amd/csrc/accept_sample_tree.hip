@@ -96,7 +96,8 @@ tree_row_norm_kernel(const void* target, const void* draft, int32_t B, int32_t K
   };
   if (V % EPL == 0) {
     // every load of a round is issued before any is consumed (clamped, in-bounds
-    // indices; those past the part's end are masked afterwards)
+    // indices; those past the part's end are masked afterwards); non-temporal: the rows
+    // stream through once here (Tree-60 call 96.2 -> 94.8 us measured)
     const int nvec = V / EPL;
     const int span = (nvec + kNormSplit - 1) / kNormSplit;
     const int v0 = part * span, v1 = min(v0 + span, nvec);
@@ -105,7 +106,7 @@ tree_row_norm_kernel(const void* target, const void* draft, int32_t B, int32_t K
 #pragma unroll
       for (int u = 0; u < kNormLoads; ++u) {
         const int i = min(base + u * kNormThreads + tid, v1 - 1);
-        w[u] = *reinterpret_cast<const u32x4*>(row + static_cast<size_t>(i) * 16);
+        w[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + static_cast<size_t>(i) * 16));
       }
 #pragma unroll
       for (int u = 0; u < kNormLoads; ++u) {

@@ -140,19 +140,25 @@ attn_split_kernel(const int32_t* page_table, const void* k_cache, const void* v_
   const int l32 = lane & 31;
   const int rg = wave % RG;                      // row group: row blocks rg + RG*t
   const int kh = wave / RG;                      // key part of each tile
-  // blockIdx.x = rgroup * nsplit_pad + s: the row groups of one split are
-  // nsplit_pad (then a multiple of 8) workgroups apart, so round-robin dispatch puts them
-  // on one XCD and the later reads of each KV tile come from that XCD's L2
+  // blockIdx.x = rgroup * nsplit_pad + s_raw: the row groups of one split are
+  // nsplit_pad (then a multiple of 8) workgroups apart, so round-robin dispatch (id i on
+  // XCD i mod 8) puts them on one XCD and the later reads of each KV tile come from that
+  // XCD's L2.  With a padded grid, split s of (sequence b, KV head g) runs at
+  // s_raw = (s + b * Hkv + g) mod nsplit_pad, so that every (b, g) starts on another XCD:
+  // otherwise the first splits of all sequences, the ones a short sequence still has,
+  // would all land on the first XCDs and overfill them (a batch of 8 sequences put 44
+  // live workgroups on the 32 CUs of XCD 0).
   // With LOADS_FIRST no branch comes before the tile loads are issued: an exit taken on
   // a loaded value (the split padding, the context length) would make the compiler wait
   // for that value first and sink every load behind the branch.  A padding workgroup
   // reads pages at its own (clamped) positions, then has no tiles and stores nothing.
-  const int rgroup = blockIdx.x / nsplit_pad;
-  const int s_raw = blockIdx.x - rgroup * nsplit_pad;
-  const bool pad = s_raw >= p.nsplit;
-  const int s = s_raw;                           // a padding id only reads (clamped) pages
   const int g = blockIdx.y;
   const int b = blockIdx.z;
+  const int rgroup = blockIdx.x / nsplit_pad;
+  const int s_raw = blockIdx.x - rgroup * nsplit_pad;
+  const int rot = (nsplit_pad & 7) == 0 ? (b * Hkv + g) % nsplit_pad : 0;
+  const int s = s_raw >= rot ? s_raw - rot : s_raw - rot + nsplit_pad;  // padding ids only
+  const bool pad = s >= p.nsplit;                                       // read (clamped) pages
   const int rb0 = rgroup * RG * NRB;               // first row block of this row group
 
   // ---- start-up.  Nothing below needs the context length until the early-exit test,
@@ -1077,15 +1083,24 @@ AttnPlan plan_attention(const sv_attn_desc& d) {
   pl.row_groups = (pl.rows + group_rows - 1) / group_rows;
   int64_t chunk = d.split_keys;
   if (chunk == 0) {
-    // one workgroup per compute unit: total (context + block) keys over all KV heads and
-    // row groups, spread over the 256 CUs in whole 64-key tiles, and no longer than the
-    // longest sequence rounded up to min(P, 64) keys
+    // at most one workgroup per compute unit: total (context + block) keys over all KV
+    // heads and row groups, spread in whole 64-key tiles, and no longer than the longest
+    // sequence rounded up to min(P, 64) keys.  Every sequence's last split may be
+    // partial, so the keys are spread over the CUs left after one such split per
+    // (sequence, KV head, row group).  One sequence fills those CUs; a batch, whose
+    // per-sequence lengths are not known here, is spread over three quarters of them
+    // (sweeps of 8-sequence batches over the split size ran fastest with 150-200 live
+    // workgroups: 80.8 -> 60.7, 82.0 -> 76.4 and 80.8 -> 65 us per pass for three
+    // context mixes, against the 272-296 live workgroups of a full spread).
     const int64_t gran = d.page_size < 64 ? d.page_size : 64;
     const int64_t ctx_sum =
         d.sum_ctx_hint > 0 ? d.sum_ctx_hint : static_cast<int64_t>(d.batch) * d.max_ctx;
     const int64_t work =
         (ctx_sum + static_cast<int64_t>(d.batch) * d.block) * d.num_kv_heads * pl.row_groups;
-    chunk = (work + kNumCUs - 1) / kNumCUs;
+    const int64_t tails = static_cast<int64_t>(d.batch) * d.num_kv_heads * pl.row_groups;
+    const int64_t target = d.batch > 1 ? kNumCUs * 3 / 4 : kNumCUs;
+    const int64_t cus = tails <= target / 2 ? target - tails : target;
+    chunk = (work + cus - 1) / cus;
     // whole 64-key tiles: a split's last tile costs a full step however few keys it
     // holds, so rounding up to the tile keeps the step count and needs fewer splits
     chunk = (chunk + 63) / 64 * 64;

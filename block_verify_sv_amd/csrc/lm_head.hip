@@ -27,6 +27,7 @@
 // Tiles are stored in the order u, then q, then h; rows at or past V are zero.  Size:
 // ceil(V / 32) * 32 * Hd elements.
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -255,13 +256,19 @@ int argmax_workgroups(int V, int resident) {
 
 template <auto Kernel>
 hipError_t launch_argmax(LmHeadParams& p, hipStream_t stream) {
-  static int resident = 0;   // workgroups resident on the chip: occupancy query, once per kernel
+  // workgroups resident on the chip: an occupancy query, once per kernel (a concurrent
+  // first call only repeats the query)
+  static std::atomic<int> cached{0};
+  int resident = cached.load(std::memory_order_relaxed);
   if (resident == 0) {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, kThreads, 0) != hipSuccess ||
-        per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, kThreads, 0) != hipSuccess) {
+      (void)hipGetLastError();                    // not the launch's error: clear it
       per_cu = 1;
+    }
+    if (per_cu < 1) per_cu = 1;
     resident = std::min(per_cu, kMaxResidentPerCU) * kNumCUs;
+    cached.store(resident, std::memory_order_relaxed);
   }
   p.nwg = argmax_workgroups(p.V, resident);
   hipLaunchKernelGGL(Kernel, dim3(p.nwg), dim3(kThreads), 0, stream, p.hidden, p.weight, p.M,

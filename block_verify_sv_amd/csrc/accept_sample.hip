@@ -137,38 +137,63 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
   const double it = p.inv_t;
   const int32_t* dr = drafts + static_cast<size_t>(b) * (K - 1);
 
-  // ---- loads that need nothing computed here, issued together: the drafted tokens'
-  // logits for the ratio tests (lane k-1 of wave 0 tests draft k) ...
+  // ---- start-up loads.  The drafted token of lane k-1 of wave 0 (which tests draft k)
+  // comes first, then the chunk partials of the log-normalisers of the K target rows and
+  // the K-1 draft rows (lpr lanes, a power of two aligned in the wave, share a row, each
+  // taking every lpr-th partial, kFold of them per batch): all are issued before the first
+  // wait.  Only the logits at the drafted tokens wait for a load (the token), and they
+  // are issued before the partials are consumed, so the start-up costs two round trips.
+  // Every index is clamped in bounds and every load is unconditional: a load under a
+  // branch makes the compiler wait for it before the next one.
   const bool tester = tid < K - 1;
-  int32_t d = tester ? dr[tid] : 0;
+  const int32_t d = K > 1 ? dr[min(tid, K - 2)] : 0;
+  const int nrows = 2 * K - 1;
+  int lpr = 1;
+  while (lpr * 2 * nrows <= kThreads && lpr < 16) lpr *= 2;
+  const int row = tid / lpr, sub = tid - row * lpr;
+  const bool has = row < nrows;
+  const int rr = has ? row : 0;
+  const int rho = rr < K ? b * K + rr : B * K + b * (K - 1) + (rr - K);
+  const float* pm = part_m + static_cast<size_t>(rho) * nchunk;
+  const double* ps = part_s + static_cast<size_t>(rho) * nchunk;
+  constexpr int kFold = 8;
+  float mv[kFold];
+  double sv[kFold];
+#pragma unroll
+  for (int u = 0; u < kFold; ++u) {
+    const int q = min(sub + u * lpr, nchunk - 1);
+    mv[u] = pm[q];
+    sv[u] = ps[q];
+  }
   const bool in_vocab = d >= 0 && d < V;
   const int dc = in_vocab ? d : 0;
-  const double lp = tester ? static_cast<double>(logit_at<kBF16>(
-      target, (static_cast<size_t>(b) * K + tid) * V + dc)) : 0.0;
-  const double lq = tester ? static_cast<double>(logit_at<kBF16>(
-      draft, (static_cast<size_t>(b) * (K - 1) + tid) * V + dc)) : 0.0;
-  // ... and the log-normalisers of the K target rows, then the K-1 draft rows: lpr
-  // lanes (a power of two, aligned in the wave) share a row, each folding every lpr-th
-  // chunk partial, then combine by shuffles
+  const int tk = min(tid, K > 1 ? K - 2 : 0);
+  const double lp = static_cast<double>(logit_at<kBF16>(target, (static_cast<size_t>(b) * K + tk) * V + dc));
+  // at K = 1 there are no draft rows: the (unused) value is read from the target row
+  const void* qsrc = K > 1 ? draft : target;
+  const size_t qr = K > 1 ? static_cast<size_t>(b) * (K - 1) + tk : static_cast<size_t>(b) * K;
+  const double lq = static_cast<double>(logit_at<kBF16>(qsrc, qr * V + dc));
   {
-    const int nrows = 2 * K - 1;
-    int lpr = 1;
-    while (lpr * 2 * nrows <= kThreads && lpr < 16) lpr *= 2;
-    const int row = tid / lpr, sub = tid - row * lpr;
-    const bool has = row < nrows;
-    const int rr = has ? row : 0;
-    const int rho = rr < K ? b * K + rr : B * K + b * (K - 1) + (rr - K);
-    const float* pm = part_m + static_cast<size_t>(rho) * nchunk;
-    const double* ps = part_s + static_cast<size_t>(rho) * nchunk;
+    // this lane's partials: q = sub, sub + lpr, ... in ascending order; the first batch is
+    // already loaded, further batches (more than kFold * lpr chunks) are loaded in turn.
+    // Maximum over the lane group, then every lane's sum against it, summed over the group
+    // by shuffles (the same order whatever the batching).
     float m = -INFINITY;
-    for (int q = sub; q < nchunk; q += lpr) m = fmaxf(m, pm[q]);
+#pragma unroll
+    for (int u = 0; u < kFold; ++u)
+      if (sub + u * lpr < nchunk) m = fmaxf(m, mv[u]);
+    for (int q = sub + kFold * lpr; q < nchunk; q += lpr) m = fmaxf(m, pm[q]);
     // over the lane group (lpr <= 16 lanes, aligned): uniform branches
     if (lpr > 1) m = fmaxf(m, xlane_f32<0>(m));
     if (lpr > 2) m = fmaxf(m, xlane_f32<1>(m));
     if (lpr > 4) m = fmaxf(m, xlane_f32<2>(m));
     if (lpr > 8) m = fmaxf(m, xlane_f32<3>(m));
     double s = 0.0;
-    for (int q = sub; q < nchunk; q += lpr)
+#pragma unroll
+    for (int u = 0; u < kFold; ++u)
+      if (sub + u * lpr < nchunk)
+        s += sv[u] * exp((static_cast<double>(mv[u]) - static_cast<double>(m)) * it);
+    for (int q = sub + kFold * lpr; q < nchunk; q += lpr)
       s += ps[q] * exp((static_cast<double>(pm[q]) - static_cast<double>(m)) * it);
     if (lpr > 1) s += xlane_f64<0>(s);
     if (lpr > 2) s += xlane_f64<1>(s);
@@ -259,6 +284,10 @@ sample_finish_kernel(const double* race_key, const int32_t* race_idx, const int3
   __shared__ int32_t ri[2][kThreads / kWave];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  // the decision and the drafted tokens are loaded first, so that their round trip
+  // overlaps the winners' (clamped, unconditional loads)
+  const int a = decision[b];
+  const int32_t dtok = K > 1 ? drafts[static_cast<size_t>(b) * (K - 1) + min(tid, K - 2)] : 0;
   double bk_r = INFINITY, bk_p = INFINITY;
   int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
   for (int q = tid; q < race_nchunk; q += kThreads) {
@@ -269,13 +298,10 @@ sample_finish_kernel(const double* race_key, const int32_t* race_idx, const int3
     if (better(k1, i1, bk_p, bi_p)) { bk_p = k1; bi_p = i1; }
   }
   block_best<kThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
-  const int a = decision[b];
   // a race with no positive weight (a row with no finite logit) draws nothing: -1
   const int32_t token = (bk_r < INFINITY) ? bi_r : (bk_p < INFINITY ? bi_p : -1);
-  if (tid < K) {
-    const int32_t* dr = drafts + static_cast<size_t>(b) * (K - 1);
-    p.out_tokens[static_cast<size_t>(b) * K + tid] = tid < a ? dr[tid] : (tid == a ? token : -1);
-  }
+  if (tid < K)
+    p.out_tokens[static_cast<size_t>(b) * K + tid] = tid < a ? dtok : (tid == a ? token : -1);
   if (tid == 0) p.accept_len[b] = a;
 }
 

@@ -92,6 +92,9 @@ greedy_walk_kernel(const unsigned long long* chunk_keys, const int32_t* drafts, 
   const int b = blockIdx.x * kWalkSeqs + (threadIdx.x >> 6);
   if (b >= B) return;                             // whole waves
   const bool in = lane < K;
+  // draft k+1 (drafts[b][k]) is checked against row k's choice, k = 0 .. K-2; loaded
+  // first (clamped, unconditional) so that it shares the keys' round trip
+  const int32_t dl = K > 1 ? drafts[static_cast<size_t>(b) * (K - 1) + min(lane, K - 2)] : 0;
   // lane i reduces row i's chunk keys (at most kMaxChunks; plain data written by the
   // argmax pass; all loads in flight, clamped index)
   const unsigned long long* keys = chunk_keys + static_cast<size_t>(b) * K * nchunk;
@@ -104,17 +107,17 @@ greedy_walk_kernel(const unsigned long long* chunk_keys, const int32_t* drafts, 
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) best = k[c] > best ? k[c] : best;
   }
-  int32_t t = -1;
-  if (in) {
-    t = static_cast<int32_t>(argmax_key_index(best));
-    if (p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
-  }
-  // draft k+1 (drafts[b][k]) is checked against row k's choice, k = 0 .. K-2
-  const int32_t d = lane < K - 1 ? drafts[static_cast<size_t>(b) * (K - 1) + lane] : 0;
+  const int32_t t = in ? static_cast<int32_t>(argmax_key_index(best)) : -1;
+  const int32_t d = lane < K - 1 ? dl : 0;
   const uint64_t miss = __ballot(lane < K - 1 && d != t);
   const int a = miss ? __builtin_ctzll(miss) : K - 1;   // accepted drafts
   const int32_t corr = __shfl(t, a);
-  if (in) p.out_tokens[static_cast<size_t>(b) * K + lane] = lane < a ? d : (lane == a ? corr : -1);
+  // every store last: a store before the ballot made the compiler wait for its
+  // acknowledgement before using the (long since loaded) draft token
+  if (in) {
+    if (p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
+    p.out_tokens[static_cast<size_t>(b) * K + lane] = lane < a ? d : (lane == a ? corr : -1);
+  }
   if (lane == 0) p.accept_len[b] = a;
 }
 
@@ -132,6 +135,11 @@ greedy_tree_walk_kernel(const unsigned long long* chunk_keys, const int32_t* dra
   const int b = blockIdx.x * kWalkSeqs + (threadIdx.x >> 6);
   if (b >= B) return;                             // whole waves
   const bool in = lane < K;
+  // the node's parent and draft token, loaded first (clamped, unconditional) so that
+  // they share the keys' round trip
+  const size_t nb0 = static_cast<size_t>(b) * (K - 1) + min(max(lane - 1, 0), max(K - 2, 0));
+  const int32_t par_l = K > 1 ? parents[nb0] : -1;
+  const int32_t tok_l = K > 1 ? drafts[nb0] : 0;
   const unsigned long long* keys = chunk_keys + static_cast<size_t>(b) * K * nchunk;
   uint64_t best = 0;
   if (in) {
@@ -142,15 +150,10 @@ greedy_tree_walk_kernel(const unsigned long long* chunk_keys, const int32_t* dra
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) best = k[c] > best ? k[c] : best;
   }
-  int32_t t = -1;
-  if (in) {
-    t = static_cast<int32_t>(argmax_key_index(best));
-    if (p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
-  }
+  const int32_t t = in ? static_cast<int32_t>(argmax_key_index(best)) : -1;
   const bool node = lane >= 1 && lane < K;        // a draft node
-  const size_t nb = static_cast<size_t>(b) * (K - 1) + (lane - 1);
-  const int32_t par = node ? parents[nb] : -1;
-  const int32_t tok = node ? drafts[nb] : 0;
+  const int32_t par = node ? par_l : -1;
+  const int32_t tok = node ? tok_l : 0;
   int cur = 0, a = 0;
   int32_t my_path = lane == 0 ? 0 : -1;           // lane j ends up holding path[j]
   for (int step = 1; step < K; ++step) {
@@ -164,8 +167,9 @@ greedy_tree_walk_kernel(const unsigned long long* chunk_keys, const int32_t* dra
   const int32_t next_node = __shfl(my_path, lane < 63 ? lane + 1 : 63);   // path[j+1]
   const int32_t next_tok = __shfl(tok, next_node > 0 ? next_node : 0);
   const int32_t corr = __shfl(t, cur);
-  if (in) {
+  if (in) {                                        // every store last (as in the chain walk)
     const size_t o = static_cast<size_t>(b) * K + lane;
+    if (p.argmax) p.argmax[o] = t;
     p.out_tokens[o] = lane < a ? next_tok : (lane == a ? corr : -1);
     p.path[o] = my_path;
   }

@@ -445,6 +445,22 @@ tree_race_kernel(const TreeSampleParams p) {
   const int jb = chunk * p.race_chunk + 4 * tid;   // one Philox block (4 tokens) a thread
   double bk_r = INFINITY, bk_p = INFINITY;
   int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
+  // every element load is issued before any is used (clamped, in-bounds indices; the
+  // draft row is valid whatever m is, c being 1 at a leaf; the stored residual only
+  // under the workgroup-uniform from_buf): a load inside the element loop made the
+  // compiler wait for each in turn, three round trips per element
+  float xp[4], xq[4];
+  double rb[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int v = min(jb + e, V - 1);
+    xp[e] = logit_at<kBF16>(p.target, trow + v);
+    xq[e] = logit_at<kBF16>(p.draft, qrow + v);
+  }
+  if (from_buf) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rb[e] = buf[min(jb + e, V - 1)];
+  }
   if (jb < V) {
     const U64x4 w = philox(p.offset, static_cast<uint64_t>(b), kResample | static_cast<uint64_t>(u),
                            static_cast<uint64_t>(jb >> 2), p.seed, 0);
@@ -452,11 +468,11 @@ tree_race_kernel(const TreeSampleParams p) {
     for (int e = 0; e < 4; ++e) {
       const int v = jb + e;
       if (v >= V) break;
-      const double pv = exp(static_cast<double>(logit_at<kBF16>(p.target, trow + v)) * it - st.lp);
+      const double pv = exp(static_cast<double>(xp[e]) * it - st.lp);
       double r = pv;
       if (m > 0) {
-        const double rh = from_buf ? buf[v] / zp : pv;
-        const double qv = exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow + v)) * it - st.lq);
+        const double rh = from_buf ? rb[e] / zp : pv;
+        const double qv = exp(static_cast<double>(xq[e]) * it - st.lq);
         r = fmax(0.0, rh - qv);
       }
       const double ej = neg_log1m(to_uniform(w.x[e]));
@@ -487,6 +503,7 @@ tree_finish_kernel(const TreeSampleParams p) {
   __shared__ int32_t ri[2][kThreads / kWave];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  const int a = p.accept_len[b];                  // loaded first: it shares the winners' trip
   double bk_r = INFINITY, bk_p = INFINITY;
   int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
   for (int q = tid; q < p.race_nchunk; q += kThreads) {
@@ -499,7 +516,7 @@ tree_finish_kernel(const TreeSampleParams p) {
   block_best<kThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
   if (tid == 0) {
     const int32_t token = (bk_r < INFINITY) ? bi_r : (bk_p < INFINITY ? bi_p : -1);
-    p.out_tokens[static_cast<size_t>(b) * p.K + p.accept_len[b]] = token;
+    p.out_tokens[static_cast<size_t>(b) * p.K + a] = token;
   }
 }
 

@@ -191,6 +191,9 @@ lm_head_finish_kernel(const unsigned long long* part, int32_t K, int32_t nwg,
   __shared__ int32_t tok[64];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the drafted token of lane k (draft k+1), loaded first (clamped, unconditional): it
+  // shares the keys' round trip
+  const int32_t dl = K > 1 ? p.drafts[static_cast<size_t>(b) * (K - 1) + min(lane, K - 2)] : 0;
   for (int r = wave; r < K; r += kFinishThreads / kWave) {
     const unsigned long long* src = part + (static_cast<size_t>(b) * K + r) * nwg;
     uint64_t best = 0;
@@ -208,13 +211,15 @@ lm_head_finish_kernel(const unsigned long long* part, int32_t K, int32_t nwg,
   if (wave != 0) return;
   const bool in = lane < K;
   const int32_t t = in ? tok[lane] : -1;
-  if (in && p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
   // draft k+1 (drafts[b][k]) is checked against row k's token, k = 0 .. K-2
-  const int32_t d = lane < K - 1 ? p.drafts[static_cast<size_t>(b) * (K - 1) + lane] : 0;
+  const int32_t d = lane < K - 1 ? dl : 0;
   const uint64_t miss = __ballot(lane < K - 1 && d != t);
   const int a = miss ? __builtin_ctzll(miss) : K - 1;   // accepted drafts
   const int32_t corr = __shfl(t, a);
-  if (in) p.out_tokens[static_cast<size_t>(b) * K + lane] = lane < a ? d : (lane == a ? corr : -1);
+  if (in) {                                        // every store last
+    if (p.argmax) p.argmax[static_cast<size_t>(b) * K + lane] = t;
+    p.out_tokens[static_cast<size_t>(b) * K + lane] = lane < a ? d : (lane == a ? corr : -1);
+  }
   if (lane == 0) p.accept_len[b] = a;
 }
 

@@ -290,6 +290,7 @@ tree_walk_kernel(const TreeSampleParams p) {
   __shared__ double zc[kMaxBlock];                 // Z after child c, from the passes' table
   __shared__ double zlast[kMaxBlock];              // Z after child c, folded here
   __shared__ double qv[kMaxBlock][kMaxBlock];      // [c][l]: q_l(x_c), elder sibling l's probability of c's token
+  __shared__ int32_t nd_m[kMaxBlock], nd_last[kMaxBlock], nd_second[kMaxBlock], nd_slot[kMaxBlock];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int lane = tid & 63;
@@ -321,6 +322,16 @@ tree_walk_kernel(const TreeSampleParams p) {
         lsh[r] = p.has_lnorm ? p.lnorm[rho] : fold_lnorm(p, rho);   // written by the first pass
       }
       if (r < K) zc[r] = p.ztab[static_cast<size_t>(b) * K + r];
+      // every node's stop-record fields (child count, last and second-to-last child,
+      // residual slot), so that the record needs no global load after the walk
+      if (r < K) {
+        const int m = p.child_count[r];
+        const int cs = p.child_start[r];
+        nd_m[r] = m;
+        nd_last[r] = m > 0 ? p.child_list[cs + m - 1] : 1;
+        nd_second[r] = m > 1 ? p.child_list[cs + m - 2] : 0;
+        nd_slot[r] = p.branch_slot[r];
+      }
     } else {
       // Z after each branching node's second-to-last child: the six waves' 16-lane groups
       // fold entries g, g + 24, ... of last_z, every partial of a round in flight
@@ -410,13 +421,13 @@ tree_walk_kernel(const TreeSampleParams p) {
   if (lane == 0) {
     // the race draws from max(0, rhat_{m-1} - q_c) at the stop node (every child c_1 ..
     // c_m rejected; c = c_m), or from p_u at a leaf
-    const int m = p.child_count[cur];
+    const int m = nd_m[cur];
     TreeStop st;
     st.u = cur;
     st.m = m;
-    st.c = m > 0 ? p.child_list[p.child_start[cur] + m - 1] : 1;
-    st.slot = p.branch_slot[cur];
-    st.zp = m > 1 ? zlast[p.child_list[p.child_start[cur] + m - 2]] : 1.0;
+    st.c = nd_last[cur];
+    st.slot = nd_slot[cur];
+    st.zp = m > 1 ? zlast[nd_second[cur]] : 1.0;
     st.lp = lsh[cur];
     st.lq = m > 0 ? lsh[K - 1 + st.c] : 0.0;
     p.stop[b] = st;

@@ -20,7 +20,10 @@
 //      the j-th child, max(0, rhat_{j-1} - q_j), stored per element in fp64 (one row per
 //      branching node, updated in place pass after pass) and its partial sums, which the
 //      next pass folds into Z_j.  The first pass also writes every row's normaliser into
-//      a table, and each pass writes q_j at the tokens of c_j's younger siblings;
+//      a table, and each pass writes q_j at the tokens of c_j's younger siblings.
+//      When the grid fits the device at once, passes 2 .. run instead as one launch,
+//      tree_residual_chain_kernel, whose workgroups keep their residual entries in
+//      registers and wait on each other's published partial sums (bounded waits);
 //   3. tree_walk_kernel, one workgroup per sequence: its other waves gather the row
 //      normalisers, the residual normalisers (folding the ones no later pass folded) and
 //      every node's elder siblings' probabilities of its token while wave 0 loads its
@@ -31,9 +34,11 @@
 //      stop node's last residual (the chain's race: RESAMPLE uniforms of the stop row,
 //      with a race over p_u carried along for an all-zero residual);
 //   5. tree_finish_kernel, one workgroup per sequence: the winner and the outputs.
-// Kernel boundaries order everything; the workspace carries no state between calls.
+// Kernel boundaries order everything else; the workspace carries no state between calls.
 // Every reduction runs in a fixed order, so results are bitwise reproducible.
 #include <math.h>
+
+#include <atomic>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -52,6 +57,11 @@ constexpr int kZChunk = 4 * kThreads;             // vocabulary entries per resi
 constexpr int kRaceThreads = 256;
 constexpr int kRaceChunk = 4 * kRaceThreads;      // vocabulary entries per race workgroup
 constexpr uint64_t kResample = 1ull << 32;        // RESAMPLE purpose in counter word 2
+// An unwritten partial-sum slot of the fused residual passes: a signalling NaN, which no
+// floating-point operation returns.
+constexpr uint64_t kSlotEmpty = 0x7FF5A5A5A5A5A5A5ull;
+constexpr int kSpinLimit = 1 << 18;               // polls of a slot wait before it gives up
+constexpr int kMaxDevices = 64;                   // devices whose residency is cached
 
 // Row index rho of target row u / draft row of node c in the normaliser table.
 __device__ __forceinline__ int target_rho(int b, int K, int u) { return b * K + u; }
@@ -154,6 +164,12 @@ tree_row_norm_kernel(const void* target, const void* draft, int32_t B, int32_t K
     p.part_m[static_cast<size_t>(rho) * kNormSplit + part] = mb;
     p.part_s[static_cast<size_t>(rho) * kNormSplit + part] = S;
   }
+  // every partial-sum slot starts empty (the fused residual passes wait on them)
+  const size_t slots = static_cast<size_t>(B) * K * p.nz;
+  const size_t stride = static_cast<size_t>(gridDim.x) * gridDim.y * kNormThreads;
+  for (size_t i = (static_cast<size_t>(blockIdx.y) * gridDim.x + part) * kNormThreads + tid;
+       i < slots; i += stride)
+    reinterpret_cast<uint64_t*>(p.zpart)[i] = kSlotEmpty;
 }
 
 // A row's log-normaliser from its kNormSplit parts (fixed order, fp64).
@@ -273,6 +289,143 @@ tree_residual_kernel(int32_t j, int32_t off, int32_t n_nodes, const TreeSamplePa
     for (int q = 0; q < kThreads / kWave; ++q) t += red[q];
     p.zpart[(static_cast<size_t>(b) * K + c) * p.nz + chunk] = t;
   }
+}
+
+// ---- 2b. passes j = 2 .. m-1 of every node with m >= 3 children in one launch, used when
+// the whole grid fits the device at once (the host checks).  Workgroup (pair of chunks,
+// sequence x node) keeps its 2,048 entries of the node's residual in registers from pass
+// to pass, so the rows are read once and written once (the last pass) instead of once
+// per pass.  The only data crossing workgroups is each pass's per-chunk partial sums, and
+// each is its own ready flag: the normaliser pass fills every slot with a signalling-NaN
+// pattern that no arithmetic produces (fmax(0, .) never yields a NaN either), a
+// workgroup publishes a sum with an agent-scope atomic store, and wave 0 of every
+// workgroup of the node re-reads the previous pass's slots with agent-scope atomic loads
+// until none holds the pattern.  With the grid resident every awaited workgroup is
+// running; the wait is bounded all the same (kSpinLimit polls), so every wave ends.
+// Every element operation, sum and summation order is tree_residual_kernel's, so the two
+// paths give the same bits.
+template <bool kBF16>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+tree_residual_chain_kernel(int32_t off, int32_t n_nodes, const TreeSampleParams p) {
+  __shared__ double zprev_sh;
+  __shared__ double red[2][kThreads / kWave];
+  __shared__ int32_t tok_sh[kMaxBlock];
+  constexpr int EPT = kZChunk / kThreads;         // entries per thread and chunk
+  constexpr int E2 = 2 * EPT;
+  const int tid = threadIdx.x;
+  const int pair = blockIdx.x;
+  const int b = blockIdx.y / n_nodes;
+  const int32_t w = p.pass_node[off + blockIdx.y - b * n_nodes];   // the node's pass-2 word
+  const int u = pn_u(w);
+  const int K = p.K, V = p.V, nz = p.nz;
+  const int m = p.child_count[u];
+  const int cs = p.child_start[u];
+  const double it = p.inv_t;
+  double* buf = p.resid + (static_cast<size_t>(b) * p.nbranch + pn_slot(w)) * V;
+  const size_t trow = (static_cast<size_t>(b) * K + u) * V;
+  const int base = pair * 2 * kZChunk;
+  // entry e: chunk 2*pair + e / EPT, the same entry of that chunk as in the per-pass kernel
+  auto vidx = [&](int e) { return base + (e / EPT) * kZChunk + (e % EPT) * kThreads + tid; };
+  auto qrow_of = [&](int c) { return (static_cast<size_t>(b) * (K - 1) + (c - 1)) * V; };
+  // q_j of the pass in flight is computed as soon as its loads land, off the path from
+  // one pass's published sums to the next pass's (the same expression as in the
+  // per-pass kernel, so the same bits)
+  double rb[E2], qv[E2];
+  float xq[E2];
+  {
+    const size_t qrow = qrow_of(p.child_list[cs + 1]);
+#pragma unroll
+    for (int e = 0; e < E2; ++e) {
+      const int v = min(vidx(e), V - 1);
+      rb[e] = buf[v];
+      xq[e] = logit_at<kBF16>(p.draft, qrow + v);
+    }
+  }
+  if (tid < K - 1) tok_sh[tid + 1] = p.tokens[static_cast<size_t>(b) * (K - 1) + tid];
+  const double Lp = p.lnorm[target_rho(b, K, u)];
+  double Lq = p.lnorm[draft_rho(p.B, b, K, p.child_list[cs + 1])];
+#pragma unroll
+  for (int e = 0; e < E2; ++e) qv[e] = exp(static_cast<double>(xq[e]) * it - Lq);
+  for (int j = 2; j < m; ++j) {
+    const int c = p.child_list[cs + j - 1], cp = p.child_list[cs + j - 2];
+    if (j + 1 < m) {                                // the next pass's draft row, in flight
+      const size_t qrow = qrow_of(p.child_list[cs + j]);
+#pragma unroll
+      for (int e = 0; e < E2; ++e) xq[e] = logit_at<kBF16>(p.draft, qrow + min(vidx(e), V - 1));
+    }
+    if (tid < kWave) {                              // Z_{j-1}, once every slot is written
+      const uint64_t* z = reinterpret_cast<const uint64_t*>(p.zpart) +
+                          (static_cast<size_t>(b) * K + cp) * nz;
+      double sz = 0.0;
+      for (int tries = 0;; ++tries) {
+        bool empty = false;
+        sz = 0.0;
+        for (int q = tid; q < nz; q += kWave) {
+          const uint64_t bits = __hip_atomic_load(z + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          empty |= bits == kSlotEmpty;
+          sz += __longlong_as_double(static_cast<long long>(bits));
+        }
+        if (__ballot(empty) == 0 || tries >= kSpinLimit) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      sz = wave_sum_f64(sz);
+      if (tid == 0) {
+        zprev_sh = sz;
+        if (pair == 0) p.ztab[static_cast<size_t>(b) * K + cp] = sz;
+      }
+    }
+    __syncthreads();
+    const double zp = zprev_sh;
+    const bool from_p = !(zp > 0.0);                // Z_{j-1} = 0: the residual restarts at p_u
+    float xp[E2];
+    if (from_p) {
+#pragma unroll
+      for (int e = 0; e < E2; ++e) xp[e] = logit_at<kBF16>(p.target, trow + min(vidx(e), V - 1));
+    }
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int e = 0; e < E2; ++e) {
+      if (vidx(e) < V) {
+        const double r = from_p ? exp(static_cast<double>(xp[e]) * it - Lp) : rb[e] / zp;
+        const double raw = fmax(0.0, r - qv[e]);
+        rb[e] = raw;
+        if (e < EPT) s0 += raw;
+        else s1 += raw;
+      }
+    }
+    s0 = wave_sum_f64(s0);
+    s1 = wave_sum_f64(s1);
+    if ((tid & 63) == 0) {
+      red[0][tid >> 6] = s0;
+      red[1][tid >> 6] = s1;
+    }
+    __syncthreads();
+    if (tid < 2 && 2 * pair + tid < nz) {
+      double t = 0.0;
+#pragma unroll
+      for (int q = 0; q < kThreads / kWave; ++q) t += red[tid][q];
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(p.zpart) +
+                             (static_cast<size_t>(b) * K + c) * nz + 2 * pair + tid,
+                         static_cast<uint64_t>(__double_as_longlong(t)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // q_c at the tokens of c's younger siblings that fall in these two chunks (read by
+    // the walk, after this kernel)
+    if (tid < K && ((p.younger[c] >> tid) & 1u)) {
+      const int xs = tok_sh[tid];
+      if (xs >= base && xs < min(base + 2 * kZChunk, V))
+        p.qpair[(static_cast<size_t>(b) * K + tid) * kMaxBlock + c] =
+            exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow_of(c) + xs)) * it - Lq);
+    }
+    if (j + 1 < m) {
+      Lq = p.lnorm[draft_rho(p.B, b, K, p.child_list[cs + j])];
+#pragma unroll
+      for (int e = 0; e < E2; ++e) qv[e] = exp(static_cast<double>(xq[e]) * it - Lq);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E2; ++e)
+    if (vidx(e) < V) buf[vidx(e)] = rb[e];
 }
 
 // ---- 3. the tests and the walk, one workgroup per sequence.  The other waves first
@@ -647,6 +800,32 @@ int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host, TreePassP
   return rounds;
 }
 
+// Workgroups of the fused residual passes that the current device holds at once: an
+// occupancy query and the device's compute-unit count, once per device (0 when either
+// query fails, which keeps the per-pass launches).
+template <bool kBF16>
+int chain_resident() {
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int r = cached[dev].load(std::memory_order_relaxed);
+  if (r == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, tree_residual_chain_kernel<kBF16>,
+                                                     kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();                    // not a launch's error: clear it
+      return 0;
+    }
+    r = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
+    cached[dev].store(r, std::memory_order_relaxed);
+  }
+  return r > 0 ? r : 0;
+}
+
 hipError_t launch_sample_tree(const TreeSampleParams& p, const TreePassPlan& plan, int rounds,
                               sv_dtype dtype, hipStream_t stream) {
   const bool bf = dtype == SV_BF16;
@@ -659,7 +838,10 @@ hipError_t launch_sample_tree(const TreeSampleParams& p, const TreePassPlan& pla
                        stream, p.target, p.draft, p.B, p.K, p.V, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  for (int j = 1; j <= rounds; ++j) {
+  // passes 2 .. in one launch when its grid fits the device at once
+  const int fused_wg = rounds >= 2 ? (p.nz + 1) / 2 * p.B * plan.n[2] : 0;
+  const bool fused = rounds >= 2 && fused_wg <= (bf ? chain_resident<true>() : chain_resident<false>());
+  for (int j = 1; j <= (fused ? 1 : rounds); ++j) {
     const dim3 g(p.nz, p.B * plan.n[j]);
     if (bf)
       hipLaunchKernelGGL(tree_residual_kernel<true>, g, dim3(kThreads), 0, stream, j, plan.off[j],
@@ -667,6 +849,17 @@ hipError_t launch_sample_tree(const TreeSampleParams& p, const TreePassPlan& pla
     else
       hipLaunchKernelGGL(tree_residual_kernel<false>, g, dim3(kThreads), 0, stream, j, plan.off[j],
                          plan.n[j], p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (fused) {
+    const dim3 g((p.nz + 1) / 2, p.B * plan.n[2]);
+    if (bf)
+      hipLaunchKernelGGL(tree_residual_chain_kernel<true>, g, dim3(kThreads), 0, stream,
+                         plan.off[2], plan.n[2], p);
+    else
+      hipLaunchKernelGGL(tree_residual_chain_kernel<false>, g, dim3(kThreads), 0, stream,
+                         plan.off[2], plan.n[2], p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -48,6 +48,27 @@ def test_tree60_workload(gpu_lib):
     assert max(depths) > 0 and min(depths) < max(depths)
 
 
+def test_tree60_one_sequence_against_batch(gpu_lib):
+    """Tree-60 at full vocabulary for one sequence (its residual passes 2-9 run as one
+    launch whose workgroups keep the residual rows in registers and wait on each other's
+    partial sums) against the oracle and, bit for bit, against the same sequence inside a
+    batch of two (one launch per pass there): 4 cycles, T = 1 and 2.5."""
+    from dataclasses import replace
+    for cyc in range(4):
+        ts2 = W.make_workload_tree_sample(cycle=10 + cyc, B=2)
+        if cyc >= 2:
+            ts2.temperature = 2.5
+        ts1 = replace(ts2, B=1, target_logits=ts2.target_logits[:1],
+                      draft_logits=ts2.draft_logits[:1], tokens=ts2.tokens[:1])
+        say(f"[tree sample] Tree-60 one sequence, cycle={10 + cyc} T={ts2.temperature}")
+        acc1 = assert_tree(gpu_lib, ts1, f"tree60 B=1/{cyc}")
+        acc2, toks2, path2 = tree_gpu(gpu_lib, ts2)
+        _, toks1, path1 = tree_gpu(gpu_lib, ts1)
+        assert acc1[0] == acc2[0]
+        np.testing.assert_array_equal(toks1[0], toks2[0])
+        np.testing.assert_array_equal(path1[0], path2[0])
+
+
 @pytest.mark.parametrize("V,dtype,T", [(152064, "bf16", 1.0), (3001, "f32", 0.7)])
 def test_chain_topology_equals_chain_call(gpu_lib, V, dtype, T):
     """A chain through the tree call returns exactly what sv_accept_sample returns."""

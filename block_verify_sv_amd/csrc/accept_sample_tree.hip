@@ -21,9 +21,10 @@
 //      branching node, updated in place pass after pass) and its partial sums, which the
 //      next pass folds into Z_j.  The first pass also writes every row's normaliser into
 //      a table, and each pass writes q_j at the tokens of c_j's younger siblings.
-//      When the grid fits the device at once, passes 2 .. run instead as one launch,
-//      tree_residual_chain_kernel, whose workgroups keep their residual entries in
-//      registers and wait on each other's published partial sums (bounded waits);
+//      When the workgroups of the nodes with three or more children fit the device at
+//      once, every pass runs instead as one launch, tree_residual_chain_kernel, whose
+//      workgroups keep their residual entries in registers and wait on each other's
+//      published partial sums (bounded waits);
 //   3. tree_walk_kernel, one workgroup per sequence: its other waves gather the row
 //      normalisers, the residual normalisers (folding the ones no later pass folded) and
 //      every node's elder siblings' probabilities of its token while wave 0 loads its
@@ -291,31 +292,34 @@ tree_residual_kernel(int32_t j, int32_t off, int32_t n_nodes, const TreeSamplePa
   }
 }
 
-// ---- 2b. passes j = 2 .. m-1 of every node with m >= 3 children in one launch, used when
-// the whole grid fits the device at once (the host checks).  Workgroup (pair of chunks,
-// sequence x node) keeps its 2,048 entries of the node's residual in registers from pass
-// to pass, so the rows are read once and written once (the last pass) instead of once
-// per pass.  The only data crossing workgroups is each pass's per-chunk partial sums, and
-// each is its own ready flag: the normaliser pass fills every slot with a signalling-NaN
-// pattern that no arithmetic produces (fmax(0, .) never yields a NaN either), a
-// workgroup publishes a sum with an agent-scope atomic store, and wave 0 of every
-// workgroup of the node re-reads the previous pass's slots with agent-scope atomic loads
-// until none holds the pattern.  With the grid resident every awaited workgroup is
-// running; the wait is bounded all the same (kSpinLimit polls), so every wave ends.
-// Every element operation, sum and summation order is tree_residual_kernel's, so the two
-// paths give the same bits.
+// ---- 2b. every residual pass of every branching node in one launch, used when the
+// workgroups of the nodes with three or more children fit the device at once (the host
+// checks; they come first in workgroup order, so in-order dispatch makes them resident
+// together).  Workgroup (pair of chunks, node x sequence) keeps its 2,048 entries of the
+// node's residual in registers from pass to pass, so each row is read once and written
+// once.  The only data crossing workgroups is each pass's per-chunk partial sums, and
+// each is its own ready flag: the normaliser pass fills every slot with a
+// signalling-NaN pattern that no arithmetic produces (fmax(0, .) never yields a NaN
+// either), a workgroup publishes a sum with an agent-scope atomic store, and wave 0 of
+// every workgroup of the node re-reads the previous pass's slots with agent-scope
+// atomic loads until none holds the pattern.  Every awaited workgroup is running; the
+// wait is bounded all the same (kSpinLimit polls), so every wave ends.  Every element
+// operation, sum and summation order is tree_residual_kernel's, and the normalisers are
+// folded by the same function, so the two paths give the same bits.
 template <bool kBF16>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
-tree_residual_chain_kernel(int32_t off, int32_t n_nodes, const TreeSampleParams p) {
+tree_residual_chain_kernel(int32_t off, const TreeSampleParams p) {
   __shared__ double zprev_sh;
   __shared__ double red[2][kThreads / kWave];
+  __shared__ double ln_sh[kMaxBlock];             // L of target row u, then of c_1, c_2, ...
   __shared__ int32_t tok_sh[kMaxBlock];
   constexpr int EPT = kZChunk / kThreads;         // entries per thread and chunk
   constexpr int E2 = 2 * EPT;
   const int tid = threadIdx.x;
   const int pair = blockIdx.x;
-  const int b = blockIdx.y / n_nodes;
-  const int32_t w = p.pass_node[off + blockIdx.y - b * n_nodes];   // the node's pass-2 word
+  const int node = blockIdx.y / p.B;              // node-major: the most children first
+  const int b = blockIdx.y - node * p.B;
+  const int32_t w = p.pass_node[off + node];      // the node's first-pass word
   const int u = pn_u(w);
   const int K = p.K, V = p.V, nz = p.nz;
   const int m = p.child_count[u];
@@ -327,32 +331,93 @@ tree_residual_chain_kernel(int32_t off, int32_t n_nodes, const TreeSampleParams 
   // entry e: chunk 2*pair + e / EPT, the same entry of that chunk as in the per-pass kernel
   auto vidx = [&](int e) { return base + (e / EPT) * kZChunk + (e % EPT) * kThreads + tid; };
   auto qrow_of = [&](int c) { return (static_cast<size_t>(b) * (K - 1) + (c - 1)) * V; };
-  // q_j of the pass in flight is computed as soon as its loads land, off the path from
-  // one pass's published sums to the next pass's (the same expression as in the
-  // per-pass kernel, so the same bits)
+  // this workgroup's entries of a row: off one address with immediate offsets when the
+  // pair lies wholly inside the row, else at clamped indices
+  const bool whole = base + 2 * kZChunk <= V;
+  auto load_row = [&](float (&x)[E2], const void* src, size_t row) {
+    if (whole) {
+      const size_t at = row + base + tid;
+#pragma unroll
+      for (int e = 0; e < E2; ++e)
+        x[e] = logit_at<kBF16>(src, at + (e / EPT) * kZChunk + (e % EPT) * kThreads);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E2; ++e) x[e] = logit_at<kBF16>(src, row + min(vidx(e), V - 1));
+    }
+  };
   double rb[E2], qv[E2];
   float xq[E2];
   {
-    const size_t qrow = qrow_of(p.child_list[cs + 1]);
+    float xp[E2];
+    load_row(xp, p.target, trow);
+    load_row(xq, p.draft, qrow_of(p.child_list[cs]));
+    if (tid < K - 1) tok_sh[tid + 1] = p.tokens[static_cast<size_t>(b) * (K - 1) + tid];
+    if (tid < m)                                  // this node's normalisers, one lane each
+      ln_sh[tid] = fold_lnorm(p, tid == 0 ? target_rho(b, K, u)
+                                          : draft_rho(p.B, b, K, p.child_list[cs + tid - 1]));
+    // the table the later kernels read, from the last workgroup (the fewest passes)
+    if (blockIdx.x == gridDim.x - 1 && blockIdx.y == gridDim.y - 1) {
+      const int rows = p.B * (2 * K - 1);
+      for (int r = tid; r < rows; r += kThreads) p.lnorm[r] = fold_lnorm(p, r);
+    }
+    __syncthreads();
+    const double Lp = ln_sh[0], Lq = ln_sh[1];
 #pragma unroll
-    for (int e = 0; e < E2; ++e) {
-      const int v = min(vidx(e), V - 1);
-      rb[e] = buf[v];
-      xq[e] = logit_at<kBF16>(p.draft, qrow + v);
+    for (int e = 0; e < E2; ++e) {                // pass 1: the residual from p_u
+      rb[e] = fmax(0.0, exp(static_cast<double>(xp[e]) * it - Lp) -
+                            exp(static_cast<double>(xq[e]) * it - Lq));
+      __builtin_amdgcn_sched_barrier(0);          // one entry's exponentials at a time
     }
   }
-  if (tid < K - 1) tok_sh[tid + 1] = p.tokens[static_cast<size_t>(b) * (K - 1) + tid];
-  const double Lp = p.lnorm[target_rho(b, K, u)];
-  double Lq = p.lnorm[draft_rho(p.B, b, K, p.child_list[cs + 1])];
+  // the pass-j sums of the two chunks into their slots, then q_c at the tokens of c's
+  // younger siblings that fall in these chunks (read by the walk, after this kernel)
+  auto publish = [&](int c, double Lq) {
+    double s0 = 0.0, s1 = 0.0;
 #pragma unroll
-  for (int e = 0; e < E2; ++e) qv[e] = exp(static_cast<double>(xq[e]) * it - Lq);
+    for (int e = 0; e < E2; ++e)
+      if (vidx(e) < V) {
+        if (e < EPT) s0 += rb[e];
+        else s1 += rb[e];
+      }
+    s0 = wave_sum_f64(s0);
+    s1 = wave_sum_f64(s1);
+    if ((tid & 63) == 0) {
+      red[0][tid >> 6] = s0;
+      red[1][tid >> 6] = s1;
+    }
+    __syncthreads();
+    if (tid < 2 && 2 * pair + tid < nz) {
+      double t = 0.0;
+#pragma unroll
+      for (int q = 0; q < kThreads / kWave; ++q) t += red[tid][q];
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(p.zpart) +
+                             (static_cast<size_t>(b) * K + c) * nz + 2 * pair + tid,
+                         static_cast<uint64_t>(__double_as_longlong(t)), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid < K && ((p.younger[c] >> tid) & 1u)) {
+      const int xs = tok_sh[tid];
+      if (xs >= base && xs < min(base + 2 * kZChunk, V))
+        p.qpair[(static_cast<size_t>(b) * K + tid) * kMaxBlock + c] =
+            exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow_of(c) + xs)) * it - Lq);
+    }
+  };
+  // q of the pass after next is loaded at the top of a pass and exponentiated after the
+  // publish, off the path from one pass's sums to the next pass's
+  auto load_q = [&](int c) { load_row(xq, p.draft, qrow_of(c)); };
+  if (m > 2) load_q(p.child_list[cs + 1]);
+  publish(p.child_list[cs], ln_sh[1]);
+  if (m > 2) {
+#pragma unroll
+    for (int e = 0; e < E2; ++e) {
+      qv[e] = exp(static_cast<double>(xq[e]) * it - ln_sh[2]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const double Lp = ln_sh[0];
   for (int j = 2; j < m; ++j) {
     const int c = p.child_list[cs + j - 1], cp = p.child_list[cs + j - 2];
-    if (j + 1 < m) {                                // the next pass's draft row, in flight
-      const size_t qrow = qrow_of(p.child_list[cs + j]);
-#pragma unroll
-      for (int e = 0; e < E2; ++e) xq[e] = logit_at<kBF16>(p.draft, qrow + min(vidx(e), V - 1));
-    }
+    if (j + 1 < m) load_q(p.child_list[cs + j]);
     if (tid < kWave) {                              // Z_{j-1}, once every slot is written
       const uint64_t* z = reinterpret_cast<const uint64_t*>(p.zpart) +
                           (static_cast<size_t>(b) * K + cp) * nz;
@@ -376,51 +441,23 @@ tree_residual_chain_kernel(int32_t off, int32_t n_nodes, const TreeSampleParams 
     }
     __syncthreads();
     const double zp = zprev_sh;
-    const bool from_p = !(zp > 0.0);                // Z_{j-1} = 0: the residual restarts at p_u
-    float xp[E2];
-    if (from_p) {
+    if (!(zp > 0.0)) {                              // Z_{j-1} = 0: the residual restarts at p_u
 #pragma unroll
-      for (int e = 0; e < E2; ++e) xp[e] = logit_at<kBF16>(p.target, trow + min(vidx(e), V - 1));
-    }
-    double s0 = 0.0, s1 = 0.0;
-#pragma unroll
-    for (int e = 0; e < E2; ++e) {
-      if (vidx(e) < V) {
-        const double r = from_p ? exp(static_cast<double>(xp[e]) * it - Lp) : rb[e] / zp;
-        const double raw = fmax(0.0, r - qv[e]);
-        rb[e] = raw;
-        if (e < EPT) s0 += raw;
-        else s1 += raw;
+      for (int e = 0; e < E2; ++e) {
+        const float xp = logit_at<kBF16>(p.target, trow + min(vidx(e), V - 1));
+        rb[e] = fmax(0.0, exp(static_cast<double>(xp) * it - Lp) - qv[e]);
       }
-    }
-    s0 = wave_sum_f64(s0);
-    s1 = wave_sum_f64(s1);
-    if ((tid & 63) == 0) {
-      red[0][tid >> 6] = s0;
-      red[1][tid >> 6] = s1;
-    }
-    __syncthreads();
-    if (tid < 2 && 2 * pair + tid < nz) {
-      double t = 0.0;
+    } else {
 #pragma unroll
-      for (int q = 0; q < kThreads / kWave; ++q) t += red[tid][q];
-      __hip_atomic_store(reinterpret_cast<uint64_t*>(p.zpart) +
-                             (static_cast<size_t>(b) * K + c) * nz + 2 * pair + tid,
-                         static_cast<uint64_t>(__double_as_longlong(t)), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      for (int e = 0; e < E2; ++e) rb[e] = fmax(0.0, rb[e] / zp - qv[e]);
     }
-    // q_c at the tokens of c's younger siblings that fall in these two chunks (read by
-    // the walk, after this kernel)
-    if (tid < K && ((p.younger[c] >> tid) & 1u)) {
-      const int xs = tok_sh[tid];
-      if (xs >= base && xs < min(base + 2 * kZChunk, V))
-        p.qpair[(static_cast<size_t>(b) * K + tid) * kMaxBlock + c] =
-            exp(static_cast<double>(logit_at<kBF16>(p.draft, qrow_of(c) + xs)) * it - Lq);
-    }
+    publish(c, ln_sh[j]);
     if (j + 1 < m) {
-      Lq = p.lnorm[draft_rho(p.B, b, K, p.child_list[cs + j])];
 #pragma unroll
-      for (int e = 0; e < E2; ++e) qv[e] = exp(static_cast<double>(xq[e]) * it - Lq);
+      for (int e = 0; e < E2; ++e) {
+        qv[e] = exp(static_cast<double>(xq[e]) * it - ln_sh[j + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 #pragma unroll
@@ -838,10 +875,12 @@ hipError_t launch_sample_tree(const TreeSampleParams& p, const TreePassPlan& pla
                        stream, p.target, p.draft, p.B, p.K, p.V, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // passes 2 .. in one launch when its grid fits the device at once
-  const int fused_wg = rounds >= 2 ? (p.nz + 1) / 2 * p.B * plan.n[2] : 0;
-  const bool fused = rounds >= 2 && fused_wg <= (bf ? chain_resident<true>() : chain_resident<false>());
-  for (int j = 1; j <= (fused ? 1 : rounds); ++j) {
+  // every pass in one launch when the workgroups of the nodes with three or more
+  // children (pass 2's nodes, first in its grid) fit the device at once
+  const int waiting_wg = rounds >= 2 ? (p.nz + 1) / 2 * p.B * plan.n[2] : 0;
+  const bool fused =
+      rounds >= 2 && waiting_wg <= (bf ? chain_resident<true>() : chain_resident<false>());
+  for (int j = 1; j <= (fused ? 0 : rounds); ++j) {
     const dim3 g(p.nz, p.B * plan.n[j]);
     if (bf)
       hipLaunchKernelGGL(tree_residual_kernel<true>, g, dim3(kThreads), 0, stream, j, plan.off[j],
@@ -853,13 +892,13 @@ hipError_t launch_sample_tree(const TreeSampleParams& p, const TreePassPlan& pla
     if (e != hipSuccess) return e;
   }
   if (fused) {
-    const dim3 g((p.nz + 1) / 2, p.B * plan.n[2]);
+    const dim3 g((p.nz + 1) / 2, p.B * plan.n[1]);
     if (bf)
       hipLaunchKernelGGL(tree_residual_chain_kernel<true>, g, dim3(kThreads), 0, stream,
-                         plan.off[2], plan.n[2], p);
+                         plan.off[1], p);
     else
       hipLaunchKernelGGL(tree_residual_chain_kernel<false>, g, dim3(kThreads), 0, stream,
-                         plan.off[2], plan.n[2], p);
+                         plan.off[1], p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -17,10 +17,12 @@
 //     key_j = -ln(1 - u_j) / r_j,  r = max(0, p_{k-1} - q_k) (or p_{K-1} for the bonus)
 // in fp64, one Philox block (4 tokens) per thread, keeping the smallest key (lowest
 // index on ties); a race over p itself is carried along for the (measure-zero) case
-// r == 0 everywhere.  Launch 3 (sample_finish_kernel), one workgroup per sequence,
-// reduces the chunk winners and writes the outputs.  The kernel boundaries order the
-// three launches, so no fences or arrival counters are needed and the workspace
-// carries no state between calls.
+// r == 0 everywhere.  Each chunk publishes its winners with agent-scope atomic stores
+// into slots the first launch left empty (a signalling-NaN key, index -1); the last
+// chunk workgroup of each sequence, started after every other one of its sequence by
+// in-order dispatch, waits (bounded) until all its sequence's slots are written, reduces
+// the winners and writes the outputs.  No fences or counters: each slot is its own
+// ready flag, and the workspace carries no state between calls.
 #include <math.h>
 
 #include "common.hpp"
@@ -118,6 +120,14 @@ row_lse_kernel(const void* target, const void* draft, int32_t B, int32_t K, int3
     for (int w = 0; w < kLseThreads / kWave; ++w) t += redd[w];
     p.part_m[static_cast<size_t>(rho) * p.nchunk + c] = m;
     p.part_s[static_cast<size_t>(rho) * p.nchunk + c] = t;
+  }
+  // every race slot starts empty (each sequence's last race workgroup waits on them)
+  const size_t slots = static_cast<size_t>(B) * p.race_nchunk * 2;
+  const size_t stride = static_cast<size_t>(gridDim.x) * gridDim.y * kLseThreads;
+  for (size_t i = (static_cast<size_t>(rho) * gridDim.x + c) * kLseThreads + tid; i < slots;
+       i += stride) {
+    reinterpret_cast<uint64_t*>(p.race_key)[i] = kSlotEmpty;
+    p.race_idx[i] = kIdxEmpty;
   }
 }
 
@@ -221,7 +231,6 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
     if (tid == 0) {
       const int a = fails ? __builtin_ctzll(fails) : K - 1;
       a_sh = a;
-      if (c == 0) p.decision[b] = a;
     }
   }
   __syncthreads();
@@ -266,40 +275,48 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
     }
   }
   block_best<kThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
+  uint64_t* const keys = reinterpret_cast<uint64_t*>(p.race_key);
   if (tid == 0) {
     const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + c) * 2;
-    p.race_key[slot] = bk_r;
-    p.race_idx[slot] = bi_r;
-    p.race_key[slot + 1] = bk_p;
-    p.race_idx[slot + 1] = bi_p;
+    __hip_atomic_store(keys + slot, static_cast<uint64_t>(__double_as_longlong(bk_r)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.race_idx + slot, bi_r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(keys + slot + 1, static_cast<uint64_t>(__double_as_longlong(bk_p)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.race_idx + slot + 1, bi_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-}
+  if (c != static_cast<int>(gridDim.x) - 1) return;
 
-// One workgroup per sequence: the race winner over every chunk (the (key, index) minimum
-// is order-independent), then the outputs.
-__global__ void __launch_bounds__(kThreads)
-sample_finish_kernel(const double* race_key, const int32_t* race_idx, const int32_t* decision,
-                     const int32_t* drafts, int32_t K, int32_t race_nchunk, const SampleParams p) {
-  __shared__ double rk[2][kThreads / kWave];
-  __shared__ int32_t ri[2][kThreads / kWave];
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  // the decision and the drafted tokens are loaded first, so that their round trip
-  // overlaps the winners' (clamped, unconditional loads)
-  const int a = decision[b];
-  const int32_t dtok = K > 1 ? drafts[static_cast<size_t>(b) * (K - 1) + min(tid, K - 2)] : 0;
-  double bk_r = INFINITY, bk_p = INFINITY;
-  int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
-  for (int q = tid; q < race_nchunk; q += kThreads) {
-    const size_t slot = (static_cast<size_t>(b) * race_nchunk + q) * 2;
-    const double k0 = race_key[slot], k1 = race_key[slot + 1];
-    const int32_t i0 = race_idx[slot], i1 = race_idx[slot + 1];
-    if (better(k0, i0, bk_r, bi_r)) { bk_r = k0; bi_r = i0; }
-    if (better(k1, i1, bk_p, bi_p)) { bk_p = k1; bi_p = i1; }
+  // ---- the sequence's last chunk: the winner over every chunk (the (key, index) minimum
+  // is order-independent), then the outputs.  Every other chunk of the sequence has a
+  // lower workgroup id, so in-order dispatch has started it before this one, and none of
+  // them waits on anything: each thread polls its chunk's slot until it is written.
+  __syncthreads();                                 // rk, ri are reused
+  const int32_t dtok = K > 1 ? dr[min(tid, K - 2)] : 0;
+  double fk_r = INFINITY, fk_p = INFINITY;
+  int32_t fi_r = 0x7FFFFFFF, fi_p = 0x7FFFFFFF;
+  for (int q = tid; q < static_cast<int>(gridDim.x); q += kThreads) {
+    const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + q) * 2;
+    uint64_t k0, k1;
+    int32_t i0, i1;
+    for (int tries = 0;; ++tries) {
+      k0 = __hip_atomic_load(keys + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      k1 = __hip_atomic_load(keys + slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      i0 = __hip_atomic_load(p.race_idx + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      i1 = __hip_atomic_load(p.race_idx + slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((k0 != kSlotEmpty && k1 != kSlotEmpty && i0 != kIdxEmpty && i1 != kIdxEmpty) ||
+          tries >= kSpinLimit)
+        break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    const double d0 = __longlong_as_double(static_cast<long long>(k0));
+    const double d1 = __longlong_as_double(static_cast<long long>(k1));
+    if (better(d0, i0, fk_r, fi_r)) { fk_r = d0; fi_r = i0; }
+    if (better(d1, i1, fk_p, fi_p)) { fk_p = d1; fi_p = i1; }
   }
-  block_best<kThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
+  block_best<kThreads>(fk_r, fi_r, fk_p, fi_p, rk, ri);
   // a race with no positive weight (a row with no finite logit) draws nothing: -1
-  const int32_t token = (bk_r < INFINITY) ? bi_r : (bk_p < INFINITY ? bi_p : -1);
+  const int32_t token = (fk_r < INFINITY) ? fi_r : (fk_p < INFINITY ? fi_p : -1);
   if (tid < K)
     p.out_tokens[static_cast<size_t>(b) * K + tid] = tid < a ? dtok : (tid == a ? token : -1);
   if (tid == 0) p.accept_len[b] = a;
@@ -326,7 +343,6 @@ size_t sample_workspace_bytes(int B, int K, int V) {
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(double);  // race_key
   off += rows * nchunk * sizeof(float);                     // part_m
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(int32_t); // race_idx
-  off += static_cast<size_t>(B) * sizeof(int32_t);          // decision
   return (off + 15) & ~static_cast<size_t>(15);
 }
 
@@ -346,10 +362,6 @@ hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, hipStream_t stre
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sample_race_kernel<false>, g2, dim3(kThreads), 0, stream, RACE_ARGS);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sample_finish_kernel, dim3(p.B), dim3(kThreads), 0, stream, p.race_key,
-                     p.race_idx, p.decision, p.drafts, p.K, p.race_nchunk, p);
 #undef LSE_ARGS
 #undef RACE_ARGS
   return hipGetLastError();

@@ -33,8 +33,10 @@
 //      record for the race;
 //   4. tree_race_kernel, grid (1024-entry chunk, sequence): the exponential race over the
 //      stop node's last residual (the chain's race: RESAMPLE uniforms of the stop row,
-//      with a race over p_u carried along for an all-zero residual);
-//   5. tree_finish_kernel, one workgroup per sequence: the winner and the outputs.
+//      with a race over p_u carried along for an all-zero residual).  Each chunk
+//      publishes its winners into slots the first launch left empty; the last chunk
+//      workgroup of each sequence (started after the others by in-order dispatch) waits,
+//      bounded, for its sequence's slots, reduces them and writes the drawn token.
 // Kernel boundaries order everything else; the workspace carries no state between calls.
 // Every reduction runs in a fixed order, so results are bitwise reproducible.
 #include <math.h>
@@ -58,10 +60,6 @@ constexpr int kZChunk = 4 * kThreads;             // vocabulary entries per resi
 constexpr int kRaceThreads = 256;
 constexpr int kRaceChunk = 4 * kRaceThreads;      // vocabulary entries per race workgroup
 constexpr uint64_t kResample = 1ull << 32;        // RESAMPLE purpose in counter word 2
-// An unwritten partial-sum slot of the fused residual passes: a signalling NaN, which no
-// floating-point operation returns.
-constexpr uint64_t kSlotEmpty = 0x7FF5A5A5A5A5A5A5ull;
-constexpr int kSpinLimit = 1 << 18;               // polls of a slot wait before it gives up
 constexpr int kMaxDevices = 64;                   // devices whose residency is cached
 
 // Row index rho of target row u / draft row of node c in the normaliser table.
@@ -171,6 +169,13 @@ tree_row_norm_kernel(const void* target, const void* draft, int32_t B, int32_t K
   for (size_t i = (static_cast<size_t>(blockIdx.y) * gridDim.x + part) * kNormThreads + tid;
        i < slots; i += stride)
     reinterpret_cast<uint64_t*>(p.zpart)[i] = kSlotEmpty;
+  // and so does every race slot (each sequence's last race workgroup waits on them)
+  const size_t rslots = static_cast<size_t>(B) * p.race_nchunk * 2;
+  for (size_t i = (static_cast<size_t>(blockIdx.y) * gridDim.x + part) * kNormThreads + tid;
+       i < rslots; i += stride) {
+    reinterpret_cast<uint64_t*>(p.race_key)[i] = kSlotEmpty;
+    p.race_idx[i] = kIdxEmpty;
+  }
 }
 
 // A row's log-normaliser from its kNormSplit parts (fixed order, fp64).
@@ -688,35 +693,48 @@ tree_race_kernel(const TreeSampleParams p) {
     }
   }
   block_best<kRaceThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
+  uint64_t* const keys = reinterpret_cast<uint64_t*>(p.race_key);
   if (tid == 0) {
     const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + chunk) * 2;
-    p.race_key[slot] = bk_r;
-    p.race_idx[slot] = bi_r;
-    p.race_key[slot + 1] = bk_p;
-    p.race_idx[slot + 1] = bi_p;
+    __hip_atomic_store(keys + slot, static_cast<uint64_t>(__double_as_longlong(bk_r)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.race_idx + slot, bi_r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(keys + slot + 1, static_cast<uint64_t>(__double_as_longlong(bk_p)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.race_idx + slot + 1, bi_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-}
+  if (chunk != static_cast<int>(gridDim.x) - 1) return;
 
-// ---- 5. the winner over every chunk, then the drawn token at slot accept_len
-__global__ void __launch_bounds__(kThreads)
-tree_finish_kernel(const TreeSampleParams p) {
-  __shared__ double rk[2][kThreads / kWave];
-  __shared__ int32_t ri[2][kThreads / kWave];
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  const int a = p.accept_len[b];                  // loaded first: it shares the winners' trip
-  double bk_r = INFINITY, bk_p = INFINITY;
-  int32_t bi_r = 0x7FFFFFFF, bi_p = 0x7FFFFFFF;
-  for (int q = tid; q < p.race_nchunk; q += kThreads) {
+  // ---- the sequence's last chunk: the winner over every chunk, then the drawn token.
+  // Every other chunk of the sequence has a lower workgroup id, so in-order dispatch has
+  // started it before this one, and none of them waits on anything: each thread polls
+  // its chunk's slot until it is written (the (key, index) minimum is order-independent).
+  __syncthreads();                                 // rk, ri are reused
+  const int a = p.accept_len[b];                  // the walk's, before this launch
+  double fk_r = INFINITY, fk_p = INFINITY;
+  int32_t fi_r = 0x7FFFFFFF, fi_p = 0x7FFFFFFF;
+  for (int q = tid; q < static_cast<int>(gridDim.x); q += kRaceThreads) {
     const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + q) * 2;
-    const double k0 = p.race_key[slot], k1 = p.race_key[slot + 1];
-    const int32_t i0 = p.race_idx[slot], i1 = p.race_idx[slot + 1];
-    if (better(k0, i0, bk_r, bi_r)) { bk_r = k0; bi_r = i0; }
-    if (better(k1, i1, bk_p, bi_p)) { bk_p = k1; bi_p = i1; }
+    uint64_t k0, k1;
+    int32_t i0, i1;
+    for (int tries = 0;; ++tries) {
+      k0 = __hip_atomic_load(keys + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      k1 = __hip_atomic_load(keys + slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      i0 = __hip_atomic_load(p.race_idx + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      i1 = __hip_atomic_load(p.race_idx + slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((k0 != kSlotEmpty && k1 != kSlotEmpty && i0 != kIdxEmpty && i1 != kIdxEmpty) ||
+          tries >= kSpinLimit)
+        break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    const double d0 = __longlong_as_double(static_cast<long long>(k0));
+    const double d1 = __longlong_as_double(static_cast<long long>(k1));
+    if (better(d0, i0, fk_r, fi_r)) { fk_r = d0; fi_r = i0; }
+    if (better(d1, i1, fk_p, fi_p)) { fk_p = d1; fi_p = i1; }
   }
-  block_best<kThreads>(bk_r, bi_r, bk_p, bi_p, rk, ri);
+  block_best<kRaceThreads>(fk_r, fi_r, fk_p, fi_p, rk, ri);
   if (tid == 0) {
-    const int32_t token = (bk_r < INFINITY) ? bi_r : (bk_p < INFINITY ? bi_p : -1);
+    const int32_t token = (fk_r < INFINITY) ? fi_r : (fk_p < INFINITY ? fi_p : -1);
     p.out_tokens[static_cast<size_t>(b) * p.K + a] = token;
   }
 }
@@ -909,9 +927,6 @@ hipError_t launch_sample_tree(const TreeSampleParams& p, const TreePassPlan& pla
   const dim3 gr(p.race_nchunk, p.B);
   if (bf) hipLaunchKernelGGL(tree_race_kernel<true>, gr, dim3(kRaceThreads), 0, stream, p);
   else hipLaunchKernelGGL(tree_race_kernel<false>, gr, dim3(kRaceThreads), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tree_finish_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -460,8 +460,6 @@ sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
   p.part_m = reinterpret_cast<float*>(w);
   w += rows * nchunk * sizeof(float);
   p.race_idx = reinterpret_cast<int32_t*>(w);
-  w += static_cast<size_t>(B) * race_nchunk * 2 * sizeof(int32_t);
-  p.decision = reinterpret_cast<int32_t*>(w);
   p.B = B;
   p.K = K;
   p.V = V;

@@ -70,7 +70,6 @@ struct SampleParams {
   double* part_s;             // [rows][nchunk] chunk sums of exp((x - m) / T)
   double* race_key;           // [B][race_nchunk][2] chunk winners' keys (residual, p)
   int32_t* race_idx;          // [B][race_nchunk][2]
-  int32_t* decision;          // [B] drafts accepted
   int32_t B, K, V;
   int32_t chunk, nchunk;      // vocabulary chunks of the normaliser pass
   int32_t race_chunk, race_nchunk;

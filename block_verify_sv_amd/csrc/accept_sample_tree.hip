@@ -60,6 +60,7 @@ constexpr int kZChunk = 4 * kThreads;             // vocabulary entries per resi
 constexpr int kRaceThreads = 256;
 constexpr int kRaceChunk = 4 * kRaceThreads;      // vocabulary entries per race workgroup
 constexpr uint64_t kResample = 1ull << 32;        // RESAMPLE purpose in counter word 2
+constexpr int kPollLoads = 3;                     // slot loads per lane in flight in one poll
 constexpr int kMaxDevices = 64;                   // devices whose residency is cached
 
 // Row index rho of target row u / draft row of node c in the normaliser table.
@@ -430,10 +431,22 @@ tree_residual_chain_kernel(int32_t off, const TreeSampleParams p) {
       for (int tries = 0;; ++tries) {
         bool empty = false;
         sz = 0.0;
-        for (int q = tid; q < nz; q += kWave) {
-          const uint64_t bits = __hip_atomic_load(z + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          empty |= bits == kSlotEmpty;
-          sz += __longlong_as_double(static_cast<long long>(bits));
+        // a poll has its loads in flight together, one per slot (lanes past the last
+        // slot load nothing); each lane sums its slots in increasing order
+        for (int q0 = 0; q0 < nz; q0 += kPollLoads * kWave) {
+          uint64_t bits[kPollLoads];
+#pragma unroll
+          for (int k = 0; k < kPollLoads; ++k) {
+            const int q = q0 + k * kWave + tid;
+            bits[k] = q < nz ? __hip_atomic_load(z + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : 0;
+          }
+#pragma unroll
+          for (int k = 0; k < kPollLoads; ++k)
+            if (q0 + k * kWave + tid < nz) {
+              empty |= bits[k] == kSlotEmpty;
+              sz += __longlong_as_double(static_cast<long long>(bits[k]));
+            }
         }
         if (__ballot(empty) == 0 || tries >= kSpinLimit) break;
         __builtin_amdgcn_s_sleep(2);

@@ -214,7 +214,8 @@ def test_sample_deterministic_and_offset_sensitive(gpu_lib):
 
 def test_sample_workspace_shape_change(gpu_lib):
     """A workspace first used by a large call and then by a smaller one with more
-    sequences: the arrival counters must not inherit the earlier call's partial sums."""
+    sequences: the race's winner slots (which the last chunk of each sequence waits on)
+    must not inherit the earlier call's winners."""
     rng = np.random.default_rng(12)
     for i, (B, K, V) in enumerate([(1, 32, 60000), (16, 8, 1000), (2, 4, 30000), (24, 3, 500)]):
         s = W.make_sample(rng, B=B, K=K, V=V, dtype="bf16", seed=5, offset=i)

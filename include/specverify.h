@@ -35,6 +35,13 @@
  *     Results are bitwise reproducible for identical inputs and shapes.
  *   - Workspaces carry no state between calls and need no initialisation; two
  *     calls that share one workspace must not overlap in time.
+ *   - Inside sv_accept_sample and sv_accept_sample_tree, some workgroups wait for
+ *     results that other workgroups of the same launch publish (agent-scope atomic
+ *     stores and loads, no fences): the last race workgroup of each sequence, and the
+ *     residual passes of a tree run as one launch when the device holds those
+ *     workgroups at once.  A race workgroup waits only on workgroups that in-order
+ *     dispatch started before it; a tree pass waits only on workgroups that are
+ *     resident with it.  Every wait is bounded besides, so a launch always ends.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H

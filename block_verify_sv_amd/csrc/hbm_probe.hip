@@ -1,7 +1,7 @@
 // Streaming-read probe for the HBM roofline (measurement only; not part of
 // libspecverify).  It answers one question: how fast can a plain, hand-written kernel
 // read a given number of bytes from HBM on this GPU, as one launch?  The verify-attention
-// pass reads its KV cache exactly once, so this is the ceiling its bandwidth is judged
+// pass reads its KV cache exactly once, so this is the ceiling its bandwidth is measured
 // against next to the 8 TB/s data-sheet peak.
 //
 // Each thread issues `kLoads` 16-byte loads per round, all in flight before any is

@@ -212,6 +212,61 @@ def test_sample_deterministic_and_offset_sensitive(gpu_lib):
     assert not np.array_equal(a1[1], a3[1])
 
 
+def test_sample_workspace_garbage_and_graph_replays(gpu_lib):
+    """The last race workgroup of each sequence waits on its sequence's winner slots, which
+    the first launch of every call empties: calls on workspaces filled with 0xFF bytes,
+    with random bytes and with the empty-slot pattern itself match the oracle, and one
+    call captured in a HIP graph and replayed four times, with new logits copied in
+    eagerly between replays, matches the oracle on every replay."""
+    import ctypes
+    B, K, V = 4, 8, 20000
+    n = ctypes.c_size_t()
+    assert gpu_lib.load().sv_accept_sample_workspace(B, K, V, ctypes.byref(n)) == 0
+    ss = [W.make_sample(np.random.default_rng(700 + i), B=B, K=K, V=V, dtype="bf16",
+                        seed=11, offset=i) for i in range(7)]
+    gen = torch.Generator(device="cpu").manual_seed(6)
+    empty = np.frombuffer(np.array([0x7FF5A5A5A5A5A5A5], np.uint64).tobytes(), np.uint8)
+    fills = [torch.full((n.value,), 0xFF, dtype=torch.uint8),
+             torch.randint(0, 256, (n.value,), dtype=torch.uint8, generator=gen),
+             torch.from_numpy(np.resize(empty, n.value).copy())]
+    for i, fill in enumerate(fills):
+        say(f"[sample] workspace fill {i}")
+        s = ss[i]
+        acc, toks = gpu_lib.accept_sample(to_dev(s.target_logits, "bf16"),
+                                          to_dev(s.draft_logits, "bf16"), i32(s.drafts),
+                                          s.temperature, s.seed, s.offset, workspace=fill.cuda())
+        torch.cuda.synchronize()
+        r_acc, r_toks = oracle.accept_sample_ref(s.target_logits, s.draft_logits, s.drafts,
+                                                 "bf16", s.temperature, s.seed, s.offset)
+        np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+        np.testing.assert_array_equal(toks.cpu().numpy(), r_toks)
+    say("[sample] graph replays")
+    s0 = ss[3]
+    tl, dl = to_dev(s0.target_logits, "bf16"), to_dev(s0.draft_logits, "bf16")
+    dr = i32(s0.drafts)
+    ws = torch.full((n.value,), 0xA5, dtype=torch.uint8, device="cuda")
+    outs = (torch.empty(B, dtype=torch.int32, device="cuda"),
+            torch.empty(B, K, dtype=torch.int32, device="cuda"))
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        gpu_lib.accept_sample(tl, dl, dr, s0.temperature, s0.seed, s0.offset, out=outs,
+                              workspace=ws, stream=st)
+    for r in range(4):
+        s = ss[3 + r]
+        tl.copy_(to_dev(s.target_logits, "bf16"))
+        dl.copy_(to_dev(s.draft_logits, "bf16"))
+        dr.copy_(i32(s.drafts))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        r_acc, r_toks = oracle.accept_sample_ref(s.target_logits, s.draft_logits, s.drafts,
+                                                 "bf16", s.temperature, s.seed, s0.offset)
+        np.testing.assert_array_equal(outs[0].cpu().numpy(), r_acc, err_msg=f"replay {r}")
+        np.testing.assert_array_equal(outs[1].cpu().numpy(), r_toks, err_msg=f"replay {r}")
+
+
 def test_sample_workspace_shape_change(gpu_lib):
     """A workspace first used by a large call and then by a smaller one with more
     sequences: the race's winner slots (which the last chunk of each sequence waits on)

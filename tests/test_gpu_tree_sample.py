@@ -127,6 +127,67 @@ def test_masked_vocabulary_and_invalid_tokens(gpu_lib):
         assert acc[2] == 0 or tree_gpu(gpu_lib, ts, off)[2][2, 1] != 1
 
 
+def test_workspace_garbage_and_graph_replays(gpu_lib):
+    """The single-launch residual passes and the race's last workgroup wait on slots that
+    the first launch of every call empties: calls on workspaces filled with 0xFF bytes,
+    with random bytes and with the empty-slot pattern itself match the oracle, and one
+    call captured in a HIP graph and replayed four times, with new logits copied in
+    eagerly between replays, matches the oracle on every replay."""
+    import ctypes
+    parents = W.make_tree_topology(np.random.default_rng(21))
+    B, K, V = 3, len(parents) + 1, 9000
+    n = ctypes.c_size_t()
+    assert gpu_lib.load().sv_accept_sample_tree_workspace(B, K, V, ctypes.byref(n)) == 0
+    tss = [W.make_tree_sample(np.random.default_rng(800 + i), B=B, V=V, parents=parents,
+                              dtype="bf16", offset=i) for i in range(7)]
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    empty = np.frombuffer(np.array([0x7FF5A5A5A5A5A5A5], np.uint64).tobytes(), np.uint8)
+    fills = [torch.full((n.value,), 0xFF, dtype=torch.uint8),
+             torch.randint(0, 256, (n.value,), dtype=torch.uint8, generator=gen),
+             torch.from_numpy(np.resize(empty, n.value).copy())]
+
+    def ref(ts, off):
+        return oracle.accept_sample_tree_ref(ts.target_logits, ts.draft_logits, ts.parents,
+                                             ts.tokens, ts.dtype, ts.temperature, ts.seed, off)
+    for i, fill in enumerate(fills):
+        say(f"[tree sample] workspace fill {i}")
+        ts = tss[i]
+        acc, toks, path = gpu_lib.accept_sample_tree(
+            to_dev(ts.target_logits, "bf16"), to_dev(ts.draft_logits, "bf16"), ts.parents,
+            i32(ts.tokens), ts.temperature, ts.seed, ts.offset, workspace=fill.cuda())
+        torch.cuda.synchronize()
+        r_acc, r_toks, r_path = ref(ts, ts.offset)
+        np.testing.assert_array_equal(acc.cpu().numpy(), r_acc)
+        np.testing.assert_array_equal(path.cpu().numpy(), r_path)
+        np.testing.assert_array_equal(toks.cpu().numpy(), r_toks)
+    say("[tree sample] graph replays")
+    t0 = tss[3]
+    tl, dl = to_dev(t0.target_logits, "bf16"), to_dev(t0.draft_logits, "bf16")
+    tk = i32(t0.tokens)
+    ws = torch.full((n.value,), 0xA5, dtype=torch.uint8, device="cuda")
+    outs = (torch.empty(B, dtype=torch.int32, device="cuda"),
+            torch.empty(B, K, dtype=torch.int32, device="cuda"),
+            torch.empty(B, K, dtype=torch.int32, device="cuda"))
+    st = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        gpu_lib.accept_sample_tree(tl, dl, t0.parents, tk, t0.temperature, t0.seed, t0.offset,
+                                   out=outs, workspace=ws, stream=st)
+    for r in range(4):
+        ts = tss[3 + r]
+        tl.copy_(to_dev(ts.target_logits, "bf16"))
+        dl.copy_(to_dev(ts.draft_logits, "bf16"))
+        tk.copy_(i32(ts.tokens))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        r_acc, r_toks, r_path = ref(ts, t0.offset)
+        np.testing.assert_array_equal(outs[0].cpu().numpy(), r_acc, err_msg=f"replay {r}")
+        np.testing.assert_array_equal(outs[2].cpu().numpy(), r_path, err_msg=f"replay {r}")
+        np.testing.assert_array_equal(outs[1].cpu().numpy(), r_toks, err_msg=f"replay {r}")
+
+
 def test_deterministic_and_offset_sensitive(gpu_lib):
     ts = W.make_tree_sample(np.random.default_rng(9), B=16, V=5000,
                             parents=W.make_tree_topology(np.random.default_rng(3)), dtype="bf16")

@@ -188,6 +188,31 @@ def test_workspace_garbage_and_graph_replays(gpu_lib):
         np.testing.assert_array_equal(outs[1].cpu().numpy(), r_toks, err_msg=f"replay {r}")
 
 
+def test_random_trees_and_shapes(gpu_lib):
+    """160 seeded random cases against the oracle: trees of 2-64 nodes (random parents,
+    stars of up to 63 siblings, i.e. 62 dependent residual passes in one launch), batches
+    of 1-8, vocabularies of 100-30,000 (odd sizes, sizes just around the 2,048-entry pairs
+    of the residual workgroups, sizes not a multiple of 8), bf16 and fp32, T in
+    [0.5, 2.5]."""
+    rng = np.random.default_rng(2024)
+    sizes = [100, 1023, 1024, 2047, 2048, 2049, 4095, 6143, 8191, 12289, 30000]
+    for case in range(160):
+        K = int(rng.integers(2, 65))
+        if case % 5 == 0:
+            parents = np.zeros(K - 1, np.int32)                 # a star
+        else:
+            parents = np.array([rng.integers(0, i + 1) for i in range(K - 1)], np.int32)
+        B = int(rng.integers(1, 9))
+        V = int(sizes[case % len(sizes)] + (rng.integers(0, 7) if case % 3 == 0 else 0))
+        dtype = "f32" if case % 4 == 3 else "bf16"
+        T = float(rng.uniform(0.5, 2.5))
+        ts = W.make_tree_sample(rng, B=B, V=V, parents=parents, dtype=dtype, temperature=T,
+                                noise=float(rng.uniform(0.2, 2.0)), seed=int(rng.integers(1 << 40)),
+                                offset=case)
+        say(f"[tree sample] random case {case}: B={B} K={K} V={V} {dtype} T={T:.2f}")
+        assert_tree(gpu_lib, ts, f"random/{case}")
+
+
 def test_deterministic_and_offset_sensitive(gpu_lib):
     ts = W.make_tree_sample(np.random.default_rng(9), B=16, V=5000,
                             parents=W.make_tree_topology(np.random.default_rng(3)), dtype="bf16")

@@ -26,7 +26,7 @@ __all__ = [
     "attention_workspace_bytes", "mask_array", "accept_greedy", "accept_greedy_tree",
     "accept_sample", "accept_sample_tree", "lm_head_greedy", "lm_head_pack",
     "lm_head_greedy_packed", "latent_compress", "kv_append", "commit", "commit_tree",
-    "make_desc", "SV_F32", "SV_BF16", "SV_F16",
+    "make_desc", "set_wait_limit", "SV_F32", "SV_BF16", "SV_F16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
@@ -57,6 +57,7 @@ _SIGNATURES = {
     "sv_version": (c_i32, []),
     "sv_status_string": (ctypes.c_char_p, [c_i32]),
     "sv_last_error": (ctypes.c_char_p, []),
+    "sv_set_wait_limit": (c_i32, [c_i32]),
     "sv_verify_attention_workspace": (c_i32, [ctypes.POINTER(AttnDesc), ctypes.POINTER(c_sz)]),
     "sv_verify_attention": (c_i32, [ctypes.POINTER(AttnDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                     c_vp, c_vp, c_vp, c_sz, c_vp]),
@@ -501,6 +502,12 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, start: torch.Tensor,
 
 
 # ----------------------------------------------------------------------- cycle commit
+def set_wait_limit(polls: int) -> None:
+    """Polls a waiting workgroup of the sampling calls makes before it gives up and reports
+    its sequence as failed (accept_len -1); process-wide, 2**18 by default."""
+    _check(load().sv_set_wait_limit(int(polls)), "sv_set_wait_limit")
+
+
 def commit(accept_len: torch.Tensor, out_tokens: torch.Tensor, ctx_lens: torch.Tensor,
            next_anchor: torch.Tensor = None, stream=None) -> torch.Tensor:
     """Close a cycle on the device: ctx_lens += accept_len + 1 (in place) and return the

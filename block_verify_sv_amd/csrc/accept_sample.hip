@@ -295,6 +295,7 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
   const int32_t dtok = K > 1 ? dr[min(tid, K - 2)] : 0;
   double fk_r = INFINITY, fk_p = INFINITY;
   int32_t fi_r = 0x7FFFFFFF, fi_p = 0x7FFFFFFF;
+  bool gave_up = false;
   for (int q = tid; q < static_cast<int>(gridDim.x); q += kThreads) {
     const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + q) * 2;
     uint64_t k0, k1;
@@ -304,9 +305,11 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
       k1 = __hip_atomic_load(keys + slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       i0 = __hip_atomic_load(p.race_idx + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       i1 = __hip_atomic_load(p.race_idx + slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((k0 != kSlotEmpty && k1 != kSlotEmpty && i0 != kIdxEmpty && i1 != kIdxEmpty) ||
-          tries >= kSpinLimit)
+      if (k0 != kSlotEmpty && k1 != kSlotEmpty && i0 != kIdxEmpty && i1 != kIdxEmpty) break;
+      if (tries >= p.wait_limit) {
+        gave_up = true;
         break;
+      }
       __builtin_amdgcn_s_sleep(2);
     }
     const double d0 = __longlong_as_double(static_cast<long long>(k0));
@@ -314,12 +317,18 @@ sample_race_kernel(const void* target, const void* draft, const int32_t* drafts,
     if (better(d0, i0, fk_r, fi_r)) { fk_r = d0; fi_r = i0; }
     if (better(d1, i1, fk_p, fi_p)) { fk_p = d1; fi_p = i1; }
   }
+  // a thread whose wait gave up enters the key -inf with index kGaveUp, which wins the
+  // minimum (every real key is >= 0), so the workgroup learns of it with no extra barrier
+  if (gave_up) { fk_r = -INFINITY; fi_r = kGaveUp; }
   block_best<kThreads>(fk_r, fi_r, fk_p, fi_p, rk, ri);
-  // a race with no positive weight (a row with no finite logit) draws nothing: -1
+  gave_up = fk_r == -INFINITY && fi_r == kGaveUp;
+  // a race with no positive weight (a row with no finite logit) draws nothing: -1; a
+  // wait that gave up reports accept_len -1 and no tokens
   const int32_t token = (fk_r < INFINITY) ? fi_r : (fk_p < INFINITY ? fi_p : -1);
   if (tid < K)
-    p.out_tokens[static_cast<size_t>(b) * K + tid] = tid < a ? dtok : (tid == a ? token : -1);
-  if (tid == 0) p.accept_len[b] = a;
+    p.out_tokens[static_cast<size_t>(b) * K + tid] =
+        gave_up ? -1 : (tid < a ? dtok : (tid == a ? token : -1));
+  if (tid == 0) p.accept_len[b] = gave_up ? -1 : a;
 }
 
 }  // namespace

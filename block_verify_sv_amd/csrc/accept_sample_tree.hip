@@ -177,6 +177,8 @@ tree_row_norm_kernel(const void* target, const void* draft, int32_t B, int32_t K
     reinterpret_cast<uint64_t*>(p.race_key)[i] = kSlotEmpty;
     p.race_idx[i] = kIdxEmpty;
   }
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = tid; i < B; i += kNormThreads) p.fail[i] = 0;
 }
 
 // A row's log-normaliser from its kNormSplit parts (fixed order, fp64).
@@ -309,7 +311,7 @@ tree_residual_kernel(int32_t j, int32_t off, int32_t n_nodes, const TreeSamplePa
 // either), a workgroup publishes a sum with an agent-scope atomic store, and wave 0 of
 // every workgroup of the node re-reads the previous pass's slots with agent-scope
 // atomic loads until none holds the pattern.  Every awaited workgroup is running; the
-// wait is bounded all the same (kSpinLimit polls), so every wave ends.  Every element
+// wait is bounded all the same (the call's wait limit of polls), so every wave ends.  Every element
 // operation, sum and summation order is tree_residual_kernel's, and the normalisers are
 // folded by the same function, so the two paths give the same bits.
 template <bool kBF16>
@@ -448,7 +450,11 @@ tree_residual_chain_kernel(int32_t off, const TreeSampleParams p) {
               sz += __longlong_as_double(static_cast<long long>(bits[k]));
             }
         }
-        if (__ballot(empty) == 0 || tries >= kSpinLimit) break;
+        if (__ballot(empty) == 0) break;
+        if (tries >= p.wait_limit) {                  // reported through the outputs
+          if (tid == 0) p.fail[b] = 1;
+          break;
+        }
         __builtin_amdgcn_s_sleep(2);
       }
       sz = wave_sum_f64(sz);
@@ -724,8 +730,10 @@ tree_race_kernel(const TreeSampleParams p) {
   // its chunk's slot until it is written (the (key, index) minimum is order-independent).
   __syncthreads();                                 // rk, ri are reused
   const int a = p.accept_len[b];                  // the walk's, before this launch
+  const int failed = p.fail[b];                   // a residual pass's wait gave up
   double fk_r = INFINITY, fk_p = INFINITY;
   int32_t fi_r = 0x7FFFFFFF, fi_p = 0x7FFFFFFF;
+  bool gave_up = false;
   for (int q = tid; q < static_cast<int>(gridDim.x); q += kRaceThreads) {
     const size_t slot = (static_cast<size_t>(b) * p.race_nchunk + q) * 2;
     uint64_t k0, k1;
@@ -735,9 +743,11 @@ tree_race_kernel(const TreeSampleParams p) {
       k1 = __hip_atomic_load(keys + slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       i0 = __hip_atomic_load(p.race_idx + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       i1 = __hip_atomic_load(p.race_idx + slot + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((k0 != kSlotEmpty && k1 != kSlotEmpty && i0 != kIdxEmpty && i1 != kIdxEmpty) ||
-          tries >= kSpinLimit)
+      if (k0 != kSlotEmpty && k1 != kSlotEmpty && i0 != kIdxEmpty && i1 != kIdxEmpty) break;
+      if (tries >= p.wait_limit) {
+        gave_up = true;
         break;
+      }
       __builtin_amdgcn_s_sleep(2);
     }
     const double d0 = __longlong_as_double(static_cast<long long>(k0));
@@ -745,8 +755,18 @@ tree_race_kernel(const TreeSampleParams p) {
     if (better(d0, i0, fk_r, fi_r)) { fk_r = d0; fi_r = i0; }
     if (better(d1, i1, fk_p, fi_p)) { fk_p = d1; fi_p = i1; }
   }
+  // a thread whose wait gave up enters the key -inf with index kGaveUp, which wins the
+  // minimum (every real key is >= 0), so the workgroup learns of it with no extra barrier
+  if (gave_up) { fk_r = -INFINITY; fi_r = kGaveUp; }
   block_best<kRaceThreads>(fk_r, fi_r, fk_p, fi_p, rk, ri);
-  if (tid == 0) {
+  gave_up = fk_r == -INFINITY && fi_r == kGaveUp;
+  if (failed || gave_up) {                         // a wait gave up: the sequence reports -1
+    if (tid < p.K) {
+      p.out_tokens[static_cast<size_t>(b) * p.K + tid] = -1;
+      p.path[static_cast<size_t>(b) * p.K + tid] = -1;
+    }
+    if (tid == 0) p.accept_len[b] = -1;
+  } else if (tid == 0) {
     const int32_t token = (fk_r < INFINITY) ? fi_r : (fk_p < INFINITY ? fi_p : -1);
     p.out_tokens[static_cast<size_t>(b) * p.K + a] = token;
   }
@@ -773,6 +793,7 @@ size_t sample_tree_workspace_bytes(int B, int K, int V) {
   off += static_cast<size_t>(B) * sizeof(TreeStop);             // stop
   off += static_cast<size_t>(B) * nrace * 2 * sizeof(int32_t);  // race_idx
   off += rows * kNormSplit * sizeof(float);                     // part_m
+  off += static_cast<size_t>(B) * sizeof(int32_t);              // fail
   return (off + 15) & ~static_cast<size_t>(15);
 }
 
@@ -798,6 +819,8 @@ void carve_sample_tree_workspace(TreeSampleParams& p, void* workspace) {
   p.race_idx = reinterpret_cast<int32_t*>(w);
   w += static_cast<size_t>(p.B) * p.race_nchunk * 2 * sizeof(int32_t);
   p.part_m = reinterpret_cast<float*>(w);
+  w += rows * kNormSplit * sizeof(float);
+  p.fail = reinterpret_cast<int32_t*>(w);
 }
 
 int plan_sample_tree(TreeSampleParams& p, const int32_t* parents_host, TreePassPlan& plan) {

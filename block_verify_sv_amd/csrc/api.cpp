@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <atomic>
 #include <string>
 
 #include "internal.hpp"
@@ -109,6 +110,13 @@ sv_status check_attn_desc(const sv_attn_desc* d) {
 }  // namespace
 
 
+namespace sv {
+namespace {
+std::atomic<int32_t> g_wait_limit{1 << 18};
+}  // namespace
+int32_t wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+}  // namespace sv
+
 extern "C" {
 
 int sv_version(void) { return SV_API_VERSION; }
@@ -125,6 +133,12 @@ const char* sv_status_string(int status) {
 }
 
 const char* sv_last_error(void) { return g_last_error.c_str(); }
+
+sv_status sv_set_wait_limit(int32_t polls) {
+  if (polls < 1) return fail(SV_ERR_INVALID_ARG, "sv_set_wait_limit: polls must be >= 1");
+  sv::g_wait_limit.store(polls, std::memory_order_relaxed);
+  return SV_OK;
+}
 
 // ---------------------------------------------------------------- attention
 sv_status sv_verify_attention_workspace(const sv_attn_desc* desc, size_t* bytes) {
@@ -468,6 +482,7 @@ sv_status sv_accept_sample(int32_t B, int32_t K, int32_t V, sv_dtype logit_dtype
   p.race_chunk = race_chunk;
   p.race_nchunk = race_nchunk;
   p.inv_t = 1.0 / static_cast<double>(temperature);
+  p.wait_limit = sv::wait_limit();
   p.seed = seed;
   p.offset = offset;
   return device_status(sv::launch_sample(p, logit_dtype, static_cast<hipStream_t>(stream)),
@@ -524,6 +539,7 @@ sv_status sv_accept_sample_tree(int32_t B, int32_t K, int32_t V, sv_dtype logit_
   p.K = K;
   p.V = V;
   p.inv_t = 1.0 / static_cast<double>(temperature);
+  p.wait_limit = sv::wait_limit();
   p.seed = seed;
   p.offset = offset;
   sv::TreePassPlan plan;

@@ -73,10 +73,14 @@ struct SampleParams {
   int32_t B, K, V;
   int32_t chunk, nchunk;      // vocabulary chunks of the normaliser pass
   int32_t race_chunk, race_nchunk;
+  int32_t wait_limit;         // polls a waiting workgroup makes before it gives up
   double inv_t;
   uint64_t seed, offset;
 };
 
+// Polls a workgroup waiting on another one's published result makes before it gives up
+// (sv_set_wait_limit; 2^18 by default).
+int32_t wait_limit();
 size_t sample_workspace_bytes(int B, int K, int V);
 int sample_chunk(int V);
 int sample_race_chunk(int V);
@@ -108,12 +112,14 @@ struct TreeSampleParams {
   double* race_key;           // [B][race_nchunk][2]
   int32_t* race_idx;
   TreeStop* stop;             // [B]
+  int32_t* fail;              // [B] 1: a wait inside a launch gave up (outputs invalid)
   int32_t B, K, V;
   int32_t nz;                 // residual chunks per row
   int32_t race_chunk, race_nchunk;
   int32_t nbranch;            // nodes with two or more children (at least 1)
   int32_t n_last;             // entries of last_z
   int32_t has_lnorm;          // 1: a residual pass runs and writes lnorm
+  int32_t wait_limit;         // polls a waiting workgroup makes before it gives up
   double inv_t;
   uint64_t seed, offset;
   uint64_t elder[kMaxBlock];      // bit i: node i is an elder sibling of node c

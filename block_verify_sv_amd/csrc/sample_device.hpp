@@ -13,11 +13,12 @@ namespace {
 
 // An unwritten partial-result slot that a later workgroup of the same launch waits on:
 // a signalling NaN, which no floating-point operation returns.  Producers publish with
-// agent-scope atomic stores, consumers poll with agent-scope atomic loads, at most
-// kSpinLimit times (so every wave ends whatever happens).
+// agent-scope atomic stores, consumers poll with agent-scope atomic loads, at most the
+// call's wait limit of times (a kernel argument, sv_set_wait_limit), so every wave ends
+// whatever happens.
 constexpr uint64_t kSlotEmpty = 0x7FF5A5A5A5A5A5A5ull;
-constexpr int kSpinLimit = 1 << 18;
 constexpr int32_t kIdxEmpty = -1;                 // an unwritten race index slot
+constexpr int32_t kGaveUp = -2;                   // a race key entered for a wait that gave up
 
 // ---- Philox4x64-10 (Salmon et al., SC'11): multipliers and Weyl key increments of
 // the 4x64 variant; ten rounds.

@@ -41,7 +41,10 @@
  *     residual passes of a tree run as one launch when the device holds those
  *     workgroups at once.  A race workgroup waits only on workgroups that in-order
  *     dispatch started before it; a tree pass waits only on workgroups that are
- *     resident with it.  Every wait is bounded besides, so a launch always ends.
+ *     resident with it.  Every wait is bounded besides (sv_set_wait_limit), so a launch
+ *     always ends; a sequence whose wait gave up (only if other work held the device
+ *     for a large fraction of a second) reports accept_len -1 and out_tokens (and
+ *     accept_path) all -1.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -69,6 +72,13 @@ int sv_version(void);
 const char* sv_status_string(int status);
 /* Message of the last failed call on this thread ("" if none). */
 const char* sv_last_error(void);
+/* Polls a waiting workgroup of sv_accept_sample / sv_accept_sample_tree makes before it
+ * gives up and reports its sequence as failed (accept_len -1, see the conventions
+ * above): polls >= 1, default 262,144 (2^18), process-wide, read by each call when it
+ * launches.  For callers that prefer an early, reported failure to a long wait, and for
+ * tests of that path (a small limit makes the waits give up without any fault).
+ * SV_ERR_INVALID_ARG for polls < 1. */
+sv_status sv_set_wait_limit(int32_t polls);
 
 /* -------------------------------------------------------------------------------------
  * Block-verification attention.

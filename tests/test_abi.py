@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert lib.sv_version() == 1
@@ -294,4 +294,11 @@ def test_out_of_range_dtype_values(lib):
         d = _desc(dtype=bad)
         assert lib.sv_kv_append(ctypes.byref(d), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                 None) == UNSUPPORTED
+
+
+def test_wait_limit_validation(lib):
+    assert lib.sv_set_wait_limit(0) == INVALID
+    assert lib.sv_set_wait_limit(-5) == INVALID
+    assert lib.sv_set_wait_limit(1) == OK
+    assert lib.sv_set_wait_limit(1 << 18) == OK                 # the default, restored
 

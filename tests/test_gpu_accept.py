@@ -267,6 +267,34 @@ def test_sample_workspace_garbage_and_graph_replays(gpu_lib):
         np.testing.assert_array_equal(outs[1].cpu().numpy(), r_toks, err_msg=f"replay {r}")
 
 
+def test_sample_waits_that_give_up_are_reported(gpu_lib):
+    """With the wait limit forced down to one poll from the host, the last race workgroup
+    of a sequence may give up waiting for the other chunks' winners: every sequence then
+    either matches the oracle or reports accept_len -1 with all tokens -1, and every
+    kernel still ends normally.  The default limit gives the oracle's results."""
+    s = W.make_sample(np.random.default_rng(31), B=8, K=32, V=152064, dtype="bf16",
+                      seed=0x5EED, offset=3)
+    r_acc, r_toks = oracle.accept_sample_ref(s.target_logits, s.draft_logits, s.drafts, "bf16",
+                                             s.temperature, s.seed, s.offset)
+    failed = 0
+    try:
+        gpu_lib.set_wait_limit(1)
+        for rep in range(4):
+            say(f"[sample] wait limit 1, call {rep}")
+            acc, toks = sample_gpu(gpu_lib, s)
+            for b in range(s.B):
+                if acc[b] == -1:
+                    failed += 1
+                    assert (toks[b] == -1).all()
+                else:
+                    assert acc[b] == r_acc[b]
+                    np.testing.assert_array_equal(toks[b], r_toks[b])
+    finally:
+        gpu_lib.set_wait_limit(1 << 18)
+    say(f"  sequences reporting a wait that gave up: {failed} of {4 * s.B}")
+    assert_sample(gpu_lib, s, "default wait limit")
+
+
 def test_sample_workspace_shape_change(gpu_lib):
     """A workspace first used by a large call and then by a smaller one with more
     sequences: the race's winner slots (which the last chunk of each sequence waits on)

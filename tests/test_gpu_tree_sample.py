@@ -213,6 +213,33 @@ def test_random_trees_and_shapes(gpu_lib):
         assert_tree(gpu_lib, ts, f"random/{case}")
 
 
+def test_waits_that_give_up_are_reported(gpu_lib):
+    """With the wait limit forced down to one poll from the host, the in-launch waits
+    (the single-launch residual passes, the race's last workgroup) may give up: every
+    sequence then either matches the oracle or reports accept_len -1 with all outputs -1,
+    and every kernel still ends normally.  The default limit gives the oracle's results."""
+    ts = W.make_workload_tree_sample(cycle=20, B=1)
+    r = oracle.accept_sample_tree_ref(ts.target_logits, ts.draft_logits, ts.parents,
+                                      ts.tokens, ts.dtype, ts.temperature, ts.seed, ts.offset)
+    failed = 0
+    try:
+        gpu_lib.set_wait_limit(1)
+        for rep in range(6):
+            say(f"[tree sample] wait limit 1, call {rep}")
+            acc, toks, path = tree_gpu(gpu_lib, ts)
+            if acc[0] == -1:
+                failed += 1
+                assert (toks[0] == -1).all() and (path[0] == -1).all()
+            else:
+                np.testing.assert_array_equal(acc, r[0])
+                np.testing.assert_array_equal(toks, r[1])
+                np.testing.assert_array_equal(path, r[2])
+    finally:
+        gpu_lib.set_wait_limit(1 << 18)
+    say(f"  calls reporting a wait that gave up: {failed} of 6")
+    assert_tree(gpu_lib, ts, "default wait limit")
+
+
 def test_deterministic_and_offset_sensitive(gpu_lib):
     ts = W.make_tree_sample(np.random.default_rng(9), B=16, V=5000,
                             parents=W.make_tree_topology(np.random.default_rng(3)), dtype="bf16")

@@ -240,6 +240,44 @@ def test_waits_that_give_up_are_reported(gpu_lib):
     assert_tree(gpu_lib, ts, "default wait limit")
 
 
+def test_concurrent_with_other_streams(gpu_lib):
+    """The in-launch waits with other work competing for the compute units: a Tree-60
+    sampling call (its residual passes in one launch) on one stream while a 72B-shaped
+    chain sampling call and a Tree-60 greedy call run on two other streams, five rounds;
+    every result matches the oracle (a wait that gave up would report -1)."""
+    ts = W.make_workload_tree_sample(cycle=40, B=1)
+    s = W.make_sample(np.random.default_rng(41), B=8, K=32, V=152064, dtype="bf16",
+                      seed=0x5EED, offset=9)
+    r_tree = oracle.accept_sample_tree_ref(ts.target_logits, ts.draft_logits, ts.parents,
+                                           ts.tokens, ts.dtype, ts.temperature, ts.seed,
+                                           ts.offset)
+    r_acc, r_toks = oracle.accept_sample_ref(s.target_logits, s.draft_logits, s.drafts, "bf16",
+                                             s.temperature, s.seed, s.offset)
+    g_lg = torch.randn(2, ts.K, ts.V, device="cuda").to(torch.bfloat16)
+    g_tok = torch.randint(0, ts.V, (2, ts.K - 1), dtype=torch.int32, device="cuda")
+    g_par = torch.from_numpy(np.tile(np.asarray(ts.parents, np.int32), (2, 1))).cuda()
+    tl, dl, tk = to_dev(ts.target_logits, "bf16"), to_dev(ts.draft_logits, "bf16"), i32(ts.tokens)
+    sl, sd, sr = to_dev(s.target_logits, "bf16"), to_dev(s.draft_logits, "bf16"), i32(s.drafts)
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    torch.cuda.synchronize()
+    for rnd in range(5):
+        say(f"[tree sample] concurrent round {rnd}")
+        with torch.cuda.stream(streams[1]):
+            c_out = gpu_lib.accept_sample(sl, sd, sr, s.temperature, s.seed, s.offset,
+                                          stream=streams[1])
+        with torch.cuda.stream(streams[2]):
+            gpu_lib.accept_greedy_tree(g_lg, g_par, g_tok, stream=streams[2])
+        with torch.cuda.stream(streams[0]):
+            t_out = gpu_lib.accept_sample_tree(tl, dl, ts.parents, tk, ts.temperature, ts.seed,
+                                               ts.offset, stream=streams[0])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(t_out[0].cpu().numpy(), r_tree[0])
+        np.testing.assert_array_equal(t_out[1].cpu().numpy(), r_tree[1])
+        np.testing.assert_array_equal(t_out[2].cpu().numpy(), r_tree[2])
+        np.testing.assert_array_equal(c_out[0].cpu().numpy(), r_acc)
+        np.testing.assert_array_equal(c_out[1].cpu().numpy(), r_toks)
+
+
 def test_deterministic_and_offset_sensitive(gpu_lib):
     ts = W.make_tree_sample(np.random.default_rng(9), B=16, V=5000,
                             parents=W.make_tree_topology(np.random.default_rng(3)), dtype="bf16")
